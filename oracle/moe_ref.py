@@ -1,0 +1,377 @@
+"""fp64 CPU oracle for the sparse MoE FFN layer forward.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only the tests, the smoke check and the CPU-baseline
+leg of the benchmark use it.  It is deliberately plain and slow: NumPy in
+float64, explicit rank counting and running counters instead of sorts, one
+expert at a time.  It shares no code, table or helper with the HIP library.
+
+What is computed, and the passage each step follows (page titles as printed
+in the sources):
+
+  [RM]  "MoE architecture in practice" (deepseekmodel.com blog), section
+        "routing math: softmax, top-k and the small must-do steps" -- the
+        TopKRouter: bias-free gate, additive jitter, softmax, top-k,
+        renormalisation, capacity from the expected load, earliest-arrival
+        keep rule.
+  [LB]  same article, section "load-balancing loss" -- the f_i * P_i
+        statistic and the BiasBalancedRouter (bias used for the choice
+        only; sign update of the bias).
+  [SE]  same article, section "shared expert" -- one always-on expert whose
+        output is added.
+  [EP]  same article, section "expert parallelism and all-to-all" -- flatten
+        to [T*k] token-major, stable group-by-expert.
+  [G]   llm-compass "MoE" page, section "sparse gating and top-k routing",
+        gate equation g = softmax(TopK(x W_g, k)) and y = sum_i g_i E_i(x).
+  [AF]  llm-compass "MoE" page, section "load balancing: from aux loss to
+        aux-loss-free": T = TopK({s_i + b_i}), g_i proportional to s_i.
+  [AUX] llm-compass "MoE" page, same section: L_aux = alpha*N*sum f_i P_i.
+  [CAP] llm-compass "MoE" page, section "capacity factor and expert
+        parallelism": capacity = capacity_factor * tokens / N, overflow
+        dropped.
+  [SG]  "MoE common taste of open models", section 7: sigmoid gating, an
+        independent score per expert, then top-k and normalisation.
+  [NL]  "MoE industrial evolution" (alishangtian.com), section 4
+        (DeepSeek route): node-limited routing, each token's experts lie in
+        at most M groups.
+
+Readings taken where the pages are silent or garbled are listed in the
+repository's design notes; the ones that change arithmetic are restated at
+the function that applies them.  Parity of the group score (sum of the best
+k/topk_groups keys of a group) is unpinned by the pages: it is pinned only by
+brute-force enumeration in the tests.
+"""
+from __future__ import annotations
+
+import math
+from typing import Callable, Dict, Optional, Sequence, Tuple, Union
+
+import numpy as np
+
+f32 = np.float32
+
+# ---------------------------------------------------------------------------
+# router: affinity, scores
+# ---------------------------------------------------------------------------
+
+
+def router_logits(x: np.ndarray, w_router: np.ndarray,
+                  logit_add: Optional[np.ndarray] = None) -> np.ndarray:
+    """l = x W_g^T (+ additive logit term), fp64.
+
+    [RM]: the gate is a linear layer with no bias; training-time jitter is
+    added to the logits (read as l + noise, the noise drawn outside and passed
+    in).  [G]: affinity x W_g.  x [T, d], w_router [N, d] -> [T, N].
+    """
+    l = np.asarray(x, np.float64) @ np.asarray(w_router, np.float64).T
+    if logit_add is not None:
+        l = l + np.asarray(logit_add, np.float64)
+    return l
+
+
+def scores_from_logits(l: np.ndarray, score_fn: str) -> np.ndarray:
+    """softmax over the N experts of each token ([RM], [G]) or an
+    independent logistic score per expert ([SG]).  fp64."""
+    l = np.asarray(l, np.float64)
+    if score_fn == "softmax":
+        z = l - l.max(axis=1, keepdims=True)
+        e = np.exp(z)
+        return e / e.sum(axis=1, keepdims=True)
+    if score_fn == "sigmoid":
+        return 1.0 / (1.0 + np.exp(-l))
+    raise ValueError(score_fn)
+
+
+# ---------------------------------------------------------------------------
+# selection
+# ---------------------------------------------------------------------------
+
+
+def selection_keys(s32: np.ndarray, bias: Optional[np.ndarray]) -> np.ndarray:
+    """key_i = fl32(s_i + b_i): one IEEE fp32 addition ([AF]; [LB]
+    BiasBalancedRouter adds the bias to the scores and selects on the sum).
+    Weights never see the bias.  -0 is canonicalised to +0."""
+    s32 = np.asarray(s32, f32)
+    if bias is None:
+        key = s32.copy()
+    else:
+        key = (s32 + np.asarray(bias, f32)[None, :]).astype(f32)
+    key[key == 0] = f32(0.0)
+    return key
+
+
+def _beats(a_val, a_nan, b_val, b_nan):
+    """a > b in the total order used for selection: numbers above NaN, NaN
+    equal to NaN, otherwise the usual order."""
+    return (~a_nan & b_nan) | (~a_nan & ~b_nan & (a_val > b_val))
+
+
+def _ranks(keys: np.ndarray, cand: Optional[np.ndarray] = None,
+           chunk: int = 64) -> np.ndarray:
+    """rank_i = #{j candidate : key_j beats key_i, or key_j == key_i and j < i}
+    for every candidate i of every row; non-candidates get a rank >= N."""
+    T, N = keys.shape
+    if cand is None:
+        cand = np.ones((T, N), dtype=bool)
+    out = np.empty((T, N), dtype=np.int64)
+    idx = np.arange(N)
+    lower = idx[None, :] < idx[:, None]  # [i, j] : j < i
+    for t0 in range(0, T, chunk):
+        k = keys[t0:t0 + chunk]
+        c = cand[t0:t0 + chunk]
+        nan = np.isnan(k)
+        v = np.where(nan, 0.0, k).astype(np.float64)
+        # [t, i, j]
+        gt = _beats(v[:, None, :], nan[:, None, :], v[:, :, None], nan[:, :, None])
+        eq = (nan[:, None, :] & nan[:, :, None]) | (
+            ~nan[:, None, :] & ~nan[:, :, None] & (v[:, None, :] == v[:, :, None]))
+        before = (gt | (eq & lower[None])) & c[:, None, :]
+        r = before.sum(axis=2)
+        out[t0:t0 + chunk] = np.where(c, r, N + r)
+    return out
+
+
+def group_candidates(keys: np.ndarray, n_groups: int, topk_groups: int,
+                     per_group: int) -> np.ndarray:
+    """Group-limited routing ([NL]): experts are split into n_groups
+    contiguous groups; a group's score is fl32 sum of its best `per_group`
+    keys (reading: per_group = k / topk_groups, summed in descending order);
+    the topk_groups best groups (ties to the lower group index) stay
+    candidates, all other experts are excluded.  Returns bool [T, N]."""
+    T, N = keys.shape
+    gs = N // n_groups
+    gkeys = keys.reshape(T, n_groups, gs)
+    gscore = np.empty((T, n_groups), dtype=f32)
+    for g in range(n_groups):
+        kg = gkeys[:, g, :]
+        r = _ranks(kg)
+        acc = np.zeros(T, dtype=f32)
+        for m in range(per_group):
+            pick = kg[np.arange(T), np.argmax(r == m, axis=1)]
+            acc = (acc + pick).astype(f32)
+        gscore[:, g] = acc
+    grank = _ranks(gscore)
+    chosen = grank < topk_groups  # [T, G]
+    return np.repeat(chosen, gs, axis=1)
+
+
+def topk_select(keys: np.ndarray, k: int, cand: Optional[np.ndarray] = None
+                ) -> np.ndarray:
+    """Token-choice top-k ([RM] probs.topk; [G] TopK): expert i is chosen iff
+    its rank < k, and sits at column rank_i, i.e. columns in descending key
+    order with ties to the lower expert index.  -> int64 [T, k]."""
+    T, N = keys.shape
+    r = _ranks(keys, cand)
+    out = np.full((T, k), -1, dtype=np.int64)
+    tt, ii = np.nonzero(r < k)
+    out[tt, r[tt, ii]] = ii
+    assert (out >= 0).all()
+    return out
+
+
+def gate_weights(s32: np.ndarray, topk_idx: np.ndarray,
+                 renormalize: bool) -> np.ndarray:
+    """g_tj = s_e / sum_{chosen} s (renormalised, [RM]; [G]; [AF] weights use
+    the raw score) or g_tj = s_e.  fp64 from the fp32 scores."""
+    s = np.asarray(s32, np.float64)
+    g = np.take_along_axis(s, topk_idx, axis=1)
+    if renormalize:
+        g = g / g.sum(axis=1, keepdims=True)
+    return g
+
+
+# ---------------------------------------------------------------------------
+# capacity and dispatch
+# ---------------------------------------------------------------------------
+
+
+def capacity(capacity_factor: float, T: int, N: int, k: int,
+             rule: str = "tokens") -> Optional[int]:
+    """Per-expert capacity, or None for dropless (capacity_factor <= 0).
+    rule "tokens":      floor(cf * T / N)                       [CAP]
+    rule "assignments": max(int(cf * k * T / N), k)             [RM]
+    cf is taken as the fp32 value the caller passes."""
+    cf = float(f32(capacity_factor))
+    if cf <= 0:
+        return None
+    if rule == "tokens":
+        return int(math.floor(cf * T / N))
+    if rule == "assignments":
+        return max(int(k * T / float(N) * cf), k)
+    raise ValueError(rule)
+
+
+def dispatch(topk_idx: np.ndarray, N: int, C: Optional[int]) -> Dict[str, np.ndarray]:
+    """Flatten the [T, k] choices token-major into assignment ids a = t*k + j
+    ([EP] reshape(-1)), number each expert's assignments in that order (the
+    arrival position), keep an assignment iff its position < C ([RM]: the
+    earliest arrivals keep the slot, no randomness; [CAP]: overflow dropped),
+    and lay the kept ones out expert by expert, ascending a inside a segment
+    ([EP] stable group-by-expert).
+
+    Returns counts [N] (pre-drop), kept [N], offsets [N+1], pos [T*k],
+    slot [T*k] (-1 = dropped), perm [R] (assignment id per slot), n_dropped.
+    """
+    flat = topk_idx.reshape(-1)
+    A = flat.size
+    pos = np.empty(A, dtype=np.int64)
+    counts = np.zeros(N, dtype=np.int64)
+    for e in range(N):
+        where = np.nonzero(flat == e)[0]  # ascending assignment ids
+        pos[where] = np.arange(where.size)
+        counts[e] = where.size
+    kept = counts.copy() if C is None else np.minimum(counts, C)
+    offsets = np.zeros(N + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(kept)
+    keep = np.ones(A, dtype=bool) if C is None else pos < C
+    slot = np.where(keep, offsets[flat] + pos, -1)
+    R = int(offsets[-1])
+    perm = np.full(R, -1, dtype=np.int64)
+    perm[slot[keep]] = np.nonzero(keep)[0]
+    n_dropped = int(A - R)
+    return dict(counts=counts, kept=kept, offsets=offsets, pos=pos, slot=slot,
+                perm=perm, n_dropped=n_dropped, keep=keep)
+
+
+# ---------------------------------------------------------------------------
+# experts and combine
+# ---------------------------------------------------------------------------
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    return z / (1.0 + np.exp(-z))
+
+
+def swiglu_ffn(x_rows: np.ndarray, w1: np.ndarray, w2: np.ndarray) -> np.ndarray:
+    """E(x) = W2 (silu(W_gate x) * (W_up x)); w1 = [W_gate; W_up] of shape
+    [2*d_ff, d] (nn.Linear layout), w2 [d, d_ff].  fp64."""
+    x = np.asarray(x_rows, np.float64)
+    w1 = np.asarray(w1, np.float64)
+    w2 = np.asarray(w2, np.float64)
+    f = w1.shape[0] // 2
+    a = x @ w1[:f].T
+    u = x @ w1[f:].T
+    return (silu(a) * u) @ w2.T
+
+
+WeightSource = Union[Tuple[np.ndarray, np.ndarray],
+                     Callable[[int], Tuple[np.ndarray, np.ndarray]]]
+
+
+def _expert_weights(w1, w2, e):
+    if callable(w1):
+        return w1(e)
+    return w1[e], w2[e]
+
+
+def moe_layer(x: np.ndarray, w_router: np.ndarray, w1, w2, *, top_k: int,
+              score_fn: str = "softmax", renormalize: bool = True,
+              n_groups: int = 1, topk_groups: int = 1,
+              capacity_factor: float = 0.0, capacity_rule: str = "tokens",
+              bias: Optional[np.ndarray] = None,
+              logit_add: Optional[np.ndarray] = None,
+              w1_shared: Optional[np.ndarray] = None,
+              w2_shared: Optional[np.ndarray] = None,
+              scores_fp32: Optional[np.ndarray] = None,
+              tokens: Optional[Sequence[int]] = None,
+              compute_outputs: bool = True) -> Dict[str, np.ndarray]:
+    """One MoE FFN layer forward ([G] y = sum_i g_i E_i(x), [SE] plus the
+    shared expert).
+
+    x [T, d]; w_router [N, d]; w1 [N, 2*d_ff, d] and w2 [N, d, d_ff], or w1 a
+    callable e -> (w1_e, w2_e) (w2 ignored) so that weights can be streamed one
+    expert at a time.  ``scores_fp32`` replaces the fp32 scores that routing
+    starts from (the scores are otherwise fl32 of the fp64 scores).
+    ``tokens`` restricts the expert/combine stage to those token rows (routing
+    and dispatch always cover all T tokens: capacity drops depend on every
+    earlier token).  Dropped assignments contribute 0 ([RM] capacity section:
+    the FFN branch output of a dropped token is zero).
+    """
+    x = np.asarray(x)
+    T = x.shape[0]
+    N = w_router.shape[0]
+    out: Dict[str, np.ndarray] = {}
+    if scores_fp32 is None:
+        if tokens is not None:
+            raise ValueError("routing needs the scores of every token")
+        l = router_logits(x, w_router, logit_add)
+        s = scores_from_logits(l, score_fn)
+        out["logits"] = l
+        out["scores"] = s
+        s32 = s.astype(f32)
+    else:
+        s32 = np.asarray(scores_fp32, f32)
+    keys = selection_keys(s32, bias)
+    cand = None
+    if n_groups > 1:
+        if top_k % topk_groups:
+            raise ValueError("top_k must be a multiple of topk_groups")
+        cand = group_candidates(keys, n_groups, topk_groups, top_k // topk_groups)
+    idx = topk_select(keys, top_k, cand)
+    g = gate_weights(s32, idx, renormalize)
+    C = capacity(capacity_factor, T, N, top_k, capacity_rule)
+    dsp = dispatch(idx, N, C)
+    out.update(topk_idx=idx, topk_w=g, capacity=C, **dsp)
+    if not compute_outputs:
+        return out
+
+    rows = np.arange(T) if tokens is None else np.asarray(tokens, np.int64)
+    sel = np.zeros(T, dtype=bool)
+    sel[rows] = True
+    d = x.shape[1]
+    y = np.zeros((T, d), dtype=np.float64)
+    keep = dsp["keep"].reshape(T, top_k)
+    for e in range(N):
+        a = np.nonzero((idx.reshape(-1) == e) & dsp["keep"]
+                       & np.repeat(sel, top_k))[0]
+        if a.size == 0:
+            continue
+        t = a // top_k
+        j = a % top_k
+        w1e, w2e = _expert_weights(w1, w2, e)
+        o = swiglu_ffn(x[t], w1e, w2e)
+        # accumulate in ascending-j order per token: add the j-th term of each
+        # token one j at a time
+        for jj in range(top_k):
+            m = j == jj
+            y[t[m]] += g[t[m], jj][:, None] * o[m]
+    if w1_shared is not None:
+        y[rows] += swiglu_ffn(x[rows], w1_shared, w2_shared)
+    out["y"] = y[rows]
+    out["rows"] = rows
+    out["keep2d"] = keep
+    return out
+
+
+# ---------------------------------------------------------------------------
+# balancing step
+# ---------------------------------------------------------------------------
+
+
+def aux_statistic(scores: np.ndarray, counts: np.ndarray) -> float:
+    """N * sum_i f_i P_i with P_i the mean score of expert i over the T tokens
+    and f_i = count_i / T the share of tokens that chose i (pre-drop) ([AUX];
+    [LB] load_balance_loss without its extra P^2 term).  Equals 1 for a
+    perfectly uniform top-1 routing."""
+    s = np.asarray(scores, np.float64)
+    T, N = s.shape
+    P = s.mean(axis=0)
+    f = np.asarray(counts, np.float64) / T
+    return float(N * np.sum(f * P))
+
+
+def bias_update(bias: np.ndarray, counts: np.ndarray, T: int, k: int,
+                step: float = 1e-3, clamp: float = 0.0) -> np.ndarray:
+    """b_i <- fl32(b_i - fl32(step * sign(load_i - mean load))) with load_i the
+    pre-drop count and mean load T*k/N; the sign is taken exactly in integers
+    as sign(N*count_i - T*k) ([LB] update_bias: overloaded experts are pushed
+    down, underloaded up, by a fixed step; [AF]).  Optional clamp to
+    [-clamp, clamp] (clamp <= 0: off)."""
+    b = np.asarray(bias, f32)
+    N = b.size
+    c = np.asarray(counts, np.int64)
+    sg = np.sign(N * c - T * k).astype(f32)
+    nb = (b - (f32(step) * sg).astype(f32)).astype(f32)
+    if clamp > 0:
+        nb = np.clip(nb, f32(-clamp), f32(clamp)).astype(f32)
+    return nb

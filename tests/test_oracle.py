@@ -1,0 +1,412 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: a worked
+example printed on the pages, a closed form, an invariant, brute-force
+enumeration on tiny inputs, or a textbook routine (scipy / explicit loops).
+CPU only.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+
+from oracle import moe_ref as R
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+f32 = np.float32
+
+
+def rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- router ---
+
+def test_router_logits_explicit_loops():
+    r = rng(1)
+    x = r.standard_normal((3, 5))
+    w = r.standard_normal((4, 5))
+    add = r.standard_normal((3, 4))
+    l = R.router_logits(x, w, add)
+    for t in range(3):
+        for i in range(4):
+            acc = 0.0
+            for c in range(5):
+                acc += x[t, c] * w[i, c]
+            assert abs(l[t, i] - (acc + add[t, i])) < 1e-12
+
+
+def test_scores_match_scipy():
+    r = rng(2)
+    l = r.standard_normal((7, 11)) * 3
+    np.testing.assert_allclose(R.scores_from_logits(l, "softmax"),
+                               scipy.special.softmax(l, axis=1), rtol=1e-13)
+    np.testing.assert_allclose(R.scores_from_logits(l, "sigmoid"),
+                               scipy.special.expit(l), rtol=1e-13)
+    assert np.allclose(R.scores_from_logits(l, "softmax").sum(1), 1.0)
+
+
+# ------------------------------------------------------------- selection ---
+
+def _brute_topk_set(key, k, cand=None):
+    """The unique k-subset S whose every member beats every non-member
+    (higher key, or equal key and lower index), by enumeration."""
+    N = len(key)
+    idx = [i for i in range(N) if cand is None or cand[i]]
+
+    def beats(i, j):
+        return key[i] > key[j] or (key[i] == key[j] and i < j)
+
+    found = [S for S in itertools.combinations(idx, k)
+             if all(beats(i, j) for i in S for j in idx if j not in S)]
+    assert len(found) == 1
+    # order inside: descending key, ties to lower index (library sort)
+    return sorted(found[0], key=lambda i: (-key[i], i))
+
+
+def test_topk_bruteforce_all_pairs():
+    r = rng(3)
+    # every one of the C(8,2)=28 pairs must come out as the choice of some row
+    seen = set()
+    for a, b in itertools.combinations(range(8), 2):
+        key = r.uniform(0, 0.5, 8).astype(f32)
+        key[a], key[b] = f32(0.9), f32(0.7 + 0.1 * r.random())
+        got = R.topk_select(key[None, :], 2)[0].tolist()
+        assert got == _brute_topk_set(key, 2)
+        seen.add(tuple(sorted(got)))
+    assert len(seen) == 28
+
+
+def test_topk_bruteforce_random_and_ties():
+    r = rng(4)
+    for trial in range(300):
+        N = int(r.integers(2, 9))
+        k = int(r.integers(1, N + 1))
+        # values from a tiny set to force ties
+        key = r.choice(np.array([0.0, 0.25, 0.5], f32), N)
+        got = R.topk_select(key[None, :], k)[0].tolist()
+        assert got == _brute_topk_set(key, k), (key, k)
+
+
+def test_all_equal_row_picks_lowest_indices():
+    key = np.full((2, 16), 0.125, f32)
+    assert R.topk_select(key, 5).tolist() == [[0, 1, 2, 3, 4]] * 2
+
+
+def test_nan_sorts_below_everything_and_negzero_equals_zero():
+    key = np.array([[np.nan, -np.inf, -0.0, 0.0, np.nan]], f32)
+    key = R.selection_keys(key, None)
+    assert R.topk_select(key, 5)[0].tolist() == [2, 3, 1, 0, 4]
+
+
+def test_group_limited_bruteforce_70_subsets():
+    """N=16 experts in 8 groups of 2, keep 4 groups, k=8 (per_group 2 = all
+    of a group): the chosen groups must be the unique 4-subset of groups whose
+    every member beats every non-member on the group score, among all
+    C(8,4)=70 subsets; each subset is reached by some row."""
+    r = rng(5)
+    seen = set()
+    for G in itertools.combinations(range(8), 4):
+        key = r.uniform(0, 0.3, 16).astype(f32)
+        for g in G:
+            key[2 * g: 2 * g + 2] += f32(0.5)
+        key = key.astype(f32)
+        cand = R.group_candidates(key[None], 8, 4, 2)[0]
+        gsc = [float(f32(np.sort(key[2 * g:2 * g + 2])[::-1][0]
+                         + np.sort(key[2 * g:2 * g + 2])[::-1][1])) for g in range(8)]
+        subsets = [S for S in itertools.combinations(range(8), 4)
+                   if all(gsc[a] > gsc[b] or (gsc[a] == gsc[b] and a < b)
+                          for a in S for b in range(8) if b not in S)]
+        assert len(subsets) == 1
+        chosen = tuple(g for g in range(8) if cand[2 * g])
+        assert chosen == subsets[0] == G
+        idx = R.topk_select(key[None], 8, cand[None])[0].tolist()
+        assert idx == _brute_topk_set(key, 8, cand)
+        seen.add(chosen)
+    assert len(seen) == 70
+
+
+def test_group_score_uses_best_two_not_best_one():
+    # group 0: (0.9, 0.0)  -> 0.9 ; group 1: (0.5, 0.5) -> 1.0 ; keep one group
+    key = np.array([[0.9, 0.0, 0.5, 0.5]], f32)
+    cand = R.group_candidates(key, 2, 1, 2)
+    assert cand[0].tolist() == [False, False, True, True]
+    assert R.topk_select(key, 2, cand)[0].tolist() == [2, 3]
+
+
+def test_group_ties_go_to_lower_group():
+    key = np.array([[0.5, 0.25, 0.25, 0.5, 0.75, 0.0]], f32)  # 3 groups of 2
+    cand = R.group_candidates(key, 3, 1, 2)  # sums 0.75 0.75 0.75
+    assert cand[0].tolist() == [True, True, False, False, False, False]
+
+
+# ----------------------------------------------------------------- gates ---
+
+def test_worked_example_renormalisation():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "renorm_worked_example.txt"))
+            if l.strip() and not l.startswith("#")]
+    for p1, p2, g1, g2 in rows:
+        s = np.array([[float(p1), 0.01, float(p2), 0.02]], f32)
+        idx = R.topk_select(R.selection_keys(s, None), 2)
+        assert idx[0].tolist() == [0, 2]
+        g = R.gate_weights(s, idx, True)[0]
+        assert abs(g[0] - float(g1)) < 1e-7 and abs(g[1] - float(g2)) < 1e-7
+
+
+def test_gates_sum_to_one():
+    r = rng(6)
+    s = scipy.special.softmax(r.standard_normal((50, 32)) * 2, axis=1).astype(f32)
+    idx = R.topk_select(R.selection_keys(s, None), 6)
+    g = R.gate_weights(s, idx, True)
+    assert np.abs(g.sum(1) - 1).max() <= 4 * 6 * 2.0 ** -24
+
+
+def test_softmax_of_topk_logits_equals_renormalised_topk_softmax():
+    """llm-compass gate g = softmax(TopK(l)) (non-chosen logits -> -inf) vs
+    the article's softmax -> topk -> renormalise."""
+    r = rng(7)
+    l = r.standard_normal((40, 12)) * 2
+    s = R.scores_from_logits(l, "softmax")
+    idx = R.topk_select(R.selection_keys(s.astype(f32), None), 3)
+    g = R.gate_weights(s, idx, True)
+    for t in range(40):
+        top = np.argsort(-l[t], kind="stable")[:3]
+        masked = np.full(12, -np.inf)
+        masked[top] = l[t, top]
+        ref = scipy.special.softmax(masked)
+        assert sorted(top.tolist()) == sorted(idx[t].tolist())
+        np.testing.assert_allclose(g[t], ref[idx[t]], rtol=1e-12)
+
+
+def test_bias_changes_choice_not_weights():
+    r = rng(8)
+    s = scipy.special.expit(r.standard_normal((30, 16))).astype(f32)
+    b = np.zeros(16, f32)
+    b[5] = 10.0
+    idx = R.topk_select(R.selection_keys(s, b), 4)
+    assert (idx[:, 0] == 5).all()  # +10 forces expert 5 into every token
+    g = R.gate_weights(s, idx, True)
+    ref = np.take_along_axis(s.astype(np.float64), idx, 1)
+    np.testing.assert_allclose(g, ref / ref.sum(1, keepdims=True), rtol=0, atol=0)
+    # two biases giving the same choice give identical weights
+    idx2 = R.topk_select(R.selection_keys(s, b * 2), 4)
+    assert (idx2 == idx).all()
+    assert (R.gate_weights(s, idx2, True) == g).all()
+
+
+def test_selection_key_is_one_fp32_add():
+    s = np.array([[1.0, 2.0 ** -24]], f32)
+    b = np.array([2.0 ** -24, 1.0], f32)
+    k = R.selection_keys(s, b)
+    # 1 + 2^-24 rounds to 1 in fp32 (ties-to-even), same for the other
+    assert k[0, 0] == f32(1.0) and k[0, 1] == f32(1.0)
+    assert R.topk_select(k, 1)[0, 0] == 0
+
+
+# -------------------------------------------------------------- capacity ---
+
+def test_capacity_closed_forms():
+    assert R.capacity(1.25, 64, 8, 2, "tokens") == 10
+    assert R.capacity(1.25, 64, 8, 2, "assignments") == 20
+    assert R.capacity(1.0, 16384, 64, 1, "tokens") == 256
+    assert R.capacity(1.0, 16384, 64, 1, "assignments") == 256
+    assert R.capacity(0.01, 10, 8, 2, "assignments") == 2  # floor of k
+    assert R.capacity(0.0, 64, 8, 2) is None
+    assert R.capacity(-1.0, 64, 8, 2) is None
+    assert R.capacity(0.5, 7, 4, 1) == 0  # floor(0.875)
+
+
+def _brute_pos(flat):
+    pos = []
+    for a in range(len(flat)):
+        c = 0
+        for b in range(a):
+            if flat[b] == flat[a]:
+                c += 1
+        pos.append(c)
+    return np.array(pos)
+
+
+def test_dispatch_bruteforce_positions_tiny():
+    r = rng(9)
+    T, N, k = 64, 8, 2
+    s = scipy.special.softmax(r.standard_normal((T, N)), axis=1).astype(f32)
+    idx = R.topk_select(R.selection_keys(s, None), k)
+    C = R.capacity(1.25, T, N, k)
+    d = R.dispatch(idx, N, C)
+    flat = idx.reshape(-1)
+    pos = _brute_pos(flat.tolist())
+    assert (d["pos"] == pos).all()
+    assert (d["keep"] == (pos < C)).all()
+    cnt = np.bincount(flat, minlength=N)
+    assert (d["counts"] == cnt).all()
+    assert d["n_dropped"] == int(np.maximum(cnt - C, 0).sum())
+    _check_perm(d, flat, N)
+
+
+def _check_perm(d, flat, N):
+    R_ = int(d["offsets"][-1])
+    perm = d["perm"]
+    assert sorted(perm.tolist()) == sorted(np.nonzero(d["slot"] >= 0)[0].tolist())
+    assert len(set(perm.tolist())) == R_
+    for e in range(N):
+        seg = perm[d["offsets"][e]:d["offsets"][e + 1]]
+        assert (flat[seg] == e).all()
+        assert (np.diff(seg) > 0).all()
+    kept = np.nonzero(d["slot"] >= 0)[0]
+    assert (perm[d["slot"][kept]] == kept).all()
+
+
+def test_identical_tokens_drop_closed_form():
+    T, N, k = 40, 8, 2
+    C = R.capacity(1.25, T, N, k)  # floor(6.25) = 6
+    s = np.tile(np.array([0.3, 0.1, 0.2, 0.05, 0.15, 0.1, 0.05, 0.05], f32), (T, 1))
+    idx = R.topk_select(R.selection_keys(s, None), k)
+    d = R.dispatch(idx, N, C)
+    assert d["n_dropped"] == k * max(0, T - C)
+    keep = d["keep"].reshape(T, k)
+    assert keep[:C].all() and not keep[C:].any()
+
+
+def test_dropless_keeps_everything():
+    r = rng(10)
+    idx = R.topk_select(R.selection_keys(r.random((100, 16)).astype(f32), None), 4)
+    d = R.dispatch(idx, 16, None)
+    assert d["n_dropped"] == 0 and d["offsets"][-1] == 400
+    _check_perm(d, idx.reshape(-1), 16)
+
+
+def test_capacity_zero_drops_all():
+    idx = np.array([[0, 1], [1, 0]])
+    d = R.dispatch(idx, 2, 0)
+    assert d["n_dropped"] == 4 and (d["slot"] == -1).all() and d["perm"].size == 0
+
+
+# --------------------------------------------------------------- experts ---
+
+def _dense_swiglu_loops(x, w1, w2):
+    T, d = x.shape
+    f = w1.shape[0] // 2
+    y = np.zeros((T, w2.shape[0]))
+    for t in range(T):
+        h = []
+        for j in range(f):
+            a = sum(x[t, c] * w1[j, c] for c in range(d))
+            u = sum(x[t, c] * w1[f + j, c] for c in range(d))
+            h.append(a / (1.0 + math.exp(-a)) * u)
+        for o in range(w2.shape[0]):
+            y[t, o] = sum(h[j] * w2[o, j] for j in range(f))
+    return y
+
+
+def _small_layer(seed, T=6, d=8, N=4, f=5):
+    r = rng(seed)
+    x = r.standard_normal((T, d))
+    wr = r.standard_normal((N, d)) / math.sqrt(d)
+    w1 = r.standard_normal((N, 2 * f, d)) / math.sqrt(d)
+    w2 = r.standard_normal((N, d, f)) / math.sqrt(f)
+    return x, wr, w1, w2
+
+
+def test_identical_experts_collapse_to_dense():
+    x, wr, w1, w2 = _small_layer(11)
+    w1[:] = w1[0]
+    w2[:] = w2[0]
+    out = R.moe_layer(x, wr, w1, w2, top_k=2, renormalize=True)
+    np.testing.assert_allclose(out["y"], _dense_swiglu_loops(x, w1[0], w2[0]),
+                               rtol=1e-10, atol=1e-12)
+    # with a shared expert: + its own dense FFN
+    r = rng(12)
+    ws1 = r.standard_normal((6, 8)) / math.sqrt(8)
+    ws2 = r.standard_normal((8, 3)) / math.sqrt(3)
+    out2 = R.moe_layer(x, wr, w1, w2, top_k=2, renormalize=True,
+                       w1_shared=ws1, w2_shared=ws2)
+    np.testing.assert_allclose(out2["y"], _dense_swiglu_loops(x, w1[0], w2[0])
+                               + _dense_swiglu_loops(x, ws1, ws2), rtol=1e-10,
+                               atol=1e-12)
+
+
+def test_single_expert_top1_is_dense():
+    x, wr, w1, w2 = _small_layer(13, N=1)
+    out = R.moe_layer(x, wr, w1, w2, top_k=1, renormalize=True)
+    assert (out["topk_w"] == 1).all()
+    np.testing.assert_allclose(out["y"], _dense_swiglu_loops(x, w1[0], w2[0]),
+                               rtol=1e-10, atol=1e-12)
+
+
+def test_drops_scale_by_kept_gate_mass():
+    T, d, N, f = 16, 8, 4, 5
+    x, wr, w1, w2 = _small_layer(14, T=T, d=d, N=N, f=f)
+    w1[:] = w1[0]
+    w2[:] = w2[0]
+    out = R.moe_layer(x, wr, w1, w2, top_k=2, renormalize=True,
+                      capacity_factor=1.0)  # C = 4 of 8 expected per expert
+    assert out["n_dropped"] > 0
+    mass = (out["topk_w"] * out["keep2d"]).sum(1)
+    dense = _dense_swiglu_loops(x, w1[0], w2[0])
+    np.testing.assert_allclose(out["y"], mass[:, None] * dense, rtol=1e-10,
+                               atol=1e-12)
+
+
+def test_token_subset_matches_full():
+    x, wr, w1, w2 = _small_layer(15, T=12)
+    full = R.moe_layer(x, wr, w1, w2, top_k=2, capacity_factor=1.0)
+    sub = R.moe_layer(x, wr, w1, w2, top_k=2, capacity_factor=1.0,
+                      scores_fp32=full["scores"].astype(f32), tokens=[3, 7])
+    np.testing.assert_allclose(sub["y"], full["y"][[3, 7]], rtol=1e-13)
+    assert (sub["slot"] == full["slot"]).all()
+    # streamed weights give the same answer
+    sub2 = R.moe_layer(x, wr, lambda e: (w1[e], w2[e]), None, top_k=2,
+                       capacity_factor=1.0, scores_fp32=full["scores"].astype(f32),
+                       tokens=[3, 7])
+    np.testing.assert_allclose(sub2["y"], sub["y"], rtol=0, atol=0)
+
+
+def test_silu_matches_expit():
+    z = np.linspace(-20, 20, 101)
+    np.testing.assert_allclose(R.silu(z), z * scipy.special.expit(z), rtol=1e-13,
+                               atol=1e-300)
+
+
+# ------------------------------------------------------------- balancing ---
+
+def test_aux_is_one_for_uniform_top1():
+    N, T = 8, 32
+    base = np.array([3.0, 1.0, 0.5, 0.2, 0.1, 0.0, -0.5, -1.0])
+    l = np.stack([np.roll(base, t % N) for t in range(T)])
+    s = R.scores_from_logits(l, "softmax")
+    idx = R.topk_select(R.selection_keys(s.astype(f32), None), 1)
+    counts = np.bincount(idx.reshape(-1), minlength=N)
+    assert (counts == T // N).all()
+    assert abs(R.aux_statistic(s, counts) - 1.0) < 1e-12
+
+
+def test_aux_uniform_P_gives_k_and_uniform_f_gives_one():
+    N, T, k = 8, 40, 3
+    s = np.full((T, N), 1.0 / N)
+    counts = np.array([30, 0, 20, 10, 15, 5, 20, 20])  # sums to T*k
+    assert abs(R.aux_statistic(s, counts) - k) < 1e-12
+    r = rng(16)
+    s2 = scipy.special.softmax(r.standard_normal((T, N)), axis=1)
+    assert abs(R.aux_statistic(s2, np.full(N, T // N)) - 1.0) < 1e-12
+
+
+def test_bias_update_closed_form():
+    N, T, k = 6, 30, 2  # mean load 10
+    counts = np.array([10, 11, 9, 0, 30, 0])
+    b = np.array([0.0, 0.005, -0.005, 0.0099, -0.0099, 1.0], f32)
+    nb = R.bias_update(b, counts, T, k, 1e-3)
+    expect_sign = [0, 1, -1, -1, 1, -1]
+    for i in range(N):
+        ref = np.float32(np.float32(b[i]) - np.float32(1e-3) * np.float32(expect_sign[i]))
+        assert nb[i] == ref
+        assert nb.dtype == np.float32
+    assert nb[0] == b[0]
+    nbc = R.bias_update(b, counts, T, k, 1e-3, clamp=1e-2)
+    assert nbc[3] == np.float32(1e-2) and nbc[5] == np.float32(1e-2)
+    # non-integer mean load: sign taken exactly, no rounding of T*k/N
+    nb2 = R.bias_update(np.zeros(3, f32), np.array([3, 3, 4]), 5, 2, 1e-3)
+    assert nb2.tolist() == [np.float32(1e-3), np.float32(1e-3), np.float32(-1e-3)]
