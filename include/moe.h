@@ -1,0 +1,212 @@
+/*
+ * moe.h -- C ABI of the sparse MoE FFN layer forward for MI355X (gfx950).
+ *
+ * The layer (one forward, one GPU):
+ *   router affinity  l = x W_r^T (+ logit_add)
+ *   scores           s = softmax(l) per token, or sigmoid(l) per expert
+ *   selection        top-k of key = fl32(s + b) (b: selection-only bias),
+ *                    optionally restricted to the best topk_groups of
+ *                    n_groups contiguous expert groups
+ *   gates            g = s_chosen / sum(s_chosen)  (or raw s)
+ *   capacity         C = floor(cf*T/N) (or max(int(cf*k*T/N), k)); the
+ *                    earliest assignments to an expert keep their slot
+ *   dispatch         flat token-major assignments a = t*k + j, stably grouped
+ *                    by expert into contiguous segments
+ *   experts          E_e(x) = W2_e (silu(W_gate,e x) * (W_up,e x))  (SwiGLU)
+ *   shared expert    always on, weight 1, added
+ *   combine          y_t = sum_{kept j} g_tj E_{e_tj}(x_t) + S(x_t)
+ *   balancing step   b_i -= step * sign(load_i - mean load);  N sum f_i P_i
+ *
+ * Sources (page titles; sections):
+ *   "MoE architecture in practice" (deepseekmodel.com blog): routing math
+ *     (bias-free gate, jitter, softmax, top-k, renormalisation, capacity,
+ *     earliest-arrival drop); load-balancing loss (f_i P_i statistic,
+ *     selection-only bias with a sign update); shared expert; expert
+ *     parallelism and all-to-all (token-major flatten, stable grouping,
+ *     grouped GEMM over contiguous expert segments).
+ *   llm-compass "MoE" page: gate equation g = softmax(TopK(x W_g, k)),
+ *     y = sum g_i E_i(x); aux-loss-free selection TopK(s_i + b_i) with
+ *     weights from s_i; aux loss alpha N sum f_i P_i; capacity =
+ *     capacity_factor * tokens / N.
+ *   "MoE common taste of open models", section 7: sigmoid scores + top-k +
+ *     normalisation; router kept in fp32.
+ *   "MoE industrial evolution" (alishangtian.com), section 4: node/group
+ *     limited routing.
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library never allocates or frees memory.  Scratch space is the
+ *     caller's workspace `ws` of `ws_bytes` >= moe_workspace_bytes(shape),
+ *     256-byte aligned.  Entry points that take a workspace use disjoint
+ *     regions of the same layout, so one workspace serves every call of one
+ *     shape; two calls sharing a workspace must not overlap in time.
+ *   - `stream` is a hipStream_t (NULL = default stream).  Every call only
+ *     enqueues work; it returns before the GPU finishes.  Outputs are valid
+ *     once the stream is synchronised.  No call synchronises the host.
+ *   - Layouts are row-major and dense:
+ *       x, y        [T, d_model]                 dtype
+ *       w_router    [N, d_model]                 fp32
+ *       logit_add   [T, N]                       fp32
+ *       bias        [N]                          fp32
+ *       w1          [N, 2*d_ff, d_model]         dtype (gate rows, then up rows)
+ *       w2          [N, d_model, d_ff]           dtype
+ *       w1_shared   [2*d_ff_shared, d_model]     dtype
+ *       w2_shared   [d_model, d_ff_shared]       dtype
+ *       scores      [T, N]   fp32;   topk_idx, topk_w  [T, k] int32 / fp32
+ *       counts [N], offsets [N+1], slot [T*k], perm [T*k]  int32
+ *     topk columns are in descending key order, ties to the lower expert.
+ *     slot[a] = -1 marks a dropped assignment; perm[0..R) lists the kept
+ *     assignment ids a = t*k + j expert by expert, ascending inside each
+ *     segment; perm[R..T*k) is left unspecified.
+ *   - dtype MOE_DTYPE_F32: activations and expert weights fp32 (all math
+ *     fp32).  MOE_DTYPE_BF16: bf16 activations/weights, bf16 MFMA with fp32
+ *     accumulation, SwiGLU intermediate rounded to bf16, fp32 combine.  The
+ *     router (GEMM, scores, selection, gates) is fp32 in both.
+ *   - Errors: every argument is validated before anything is enqueued; on
+ *     an error nothing is launched and the status says why.  No C++
+ *     exception crosses this interface.  MOE_ERR_HIP reports a failed
+ *     launch (the HIP error is then retrievable with hipGetLastError()).
+ *   - Determinism: every output is bitwise reproducible run to run, and the
+ *     routing of a token does not depend on the other tokens of the batch
+ *     (dropless) -- no atomics decide any value or order.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID = 1,     /* null required pointer or inconsistent shape */
+  MOE_ERR_UNSUPPORTED = 2, /* valid but outside what the kernels handle   */
+  MOE_ERR_WORKSPACE = 3,   /* ws NULL or ws_bytes too small              */
+  MOE_ERR_HIP = 4          /* a kernel launch failed                      */
+} moe_status;
+
+enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
+enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 };
+/* capacity rule: TOKENS  C = floor(cf*T/N)               (llm-compass page)
+ *                ASSIGNMENTS C = max(int(cf*k*T/N), k)    (deepseekmodel.com
+ *                                                          TopKRouter)      */
+enum { MOE_CAP_TOKENS = 0, MOE_CAP_ASSIGNMENTS = 1 };
+
+typedef struct moe_shape {
+  int64_t T;              /* tokens (batch x sequence flattened), >= 1      */
+  int32_t d_model;        /* hidden size d                                  */
+  int32_t n_experts;      /* routed experts N, 1..512                       */
+  int32_t top_k;          /* experts per token k, 1..min(N,16)              */
+  int32_t d_ff;           /* routed expert intermediate size                */
+  int32_t d_ff_shared;    /* shared expert intermediate size; 0 = none      */
+  int32_t score_fn;       /* MOE_SCORE_*                                    */
+  int32_t renormalize;    /* 1: g = s / sum_chosen s; 0: g = s              */
+  int32_t n_groups;       /* expert groups (1 = no group limit); divides N  */
+  int32_t topk_groups;    /* groups kept per token; divides k               */
+  float capacity_factor;  /* <= 0: dropless                                 */
+  int32_t capacity_rule;  /* MOE_CAP_*                                      */
+  int32_t dtype;          /* MOE_DTYPE_* of activations and expert weights  */
+} moe_shape;
+
+/* Version of this interface (MOE_ABI_VERSION). */
+int moe_abi_version(void);
+
+/* Human-readable name of a status. Never NULL. */
+const char* moe_status_string(moe_status status);
+
+/* Validate a shape without touching the GPU: MOE_OK, MOE_ERR_INVALID or
+ * MOE_ERR_UNSUPPORTED.  Invalid: T < 1, N < 1, k < 1 or k > N, d_model or
+ * d_ff < 1, d_ff_shared < 0, unknown enum values, n_groups < 1 or not
+ * dividing N, topk_groups < 1 or > n_groups, k % topk_groups != 0,
+ * k/topk_groups > N/n_groups, NaN capacity_factor.  Unsupported: N > 512,
+ * k > 16, n_groups > 64, d_model, d_ff, d_ff_shared not multiples of 64
+ * (bf16) or 32 (fp32), T*k*max(d_model, d_ff, d_ff_shared) >= 2^31,
+ * 2*d_ff*d_model >= 2^31. */
+moe_status moe_check_shape(const moe_shape* shape);
+
+/* Expert capacity C the dispatch applies, or -1 when dropless.  Host-only. */
+int64_t moe_capacity(const moe_shape* shape);
+
+/* Workspace bytes that every entry point below needs for this shape
+ * (0 on an invalid shape). */
+size_t moe_workspace_bytes(const moe_shape* shape);
+
+/* Router: logits, scores, selection and gates for all T tokens.
+ * x [T,d] dtype; w_router [N,d] fp32; logit_add [T,N] or NULL (added to the
+ * logits: train-time jitter, logit offsets); bias [N] or NULL (selection
+ * only).  scores_in [T,N] fp32 or NULL: when given, the GEMM and score
+ * function are skipped and these scores are selected on (x and w_router
+ * may then be NULL).  Outputs: logits_out [T,N] (NULL: not written; ignored
+ * with scores_in), scores_out [T,N] (NULL: not written), topk_idx [T,k],
+ * topk_w [T,k] (required). */
+moe_status moe_route(const moe_shape* shape, const void* x,
+                     const float* w_router, const float* logit_add,
+                     const float* scores_in, const float* bias,
+                     float* logits_out, float* scores_out, int32_t* topk_idx,
+                     float* topk_w, void* ws, size_t ws_bytes, void* stream);
+
+/* Dispatch: per-expert counts, capacity drop and the stable permutation.
+ * topk_idx [T,k] with values in [0,N).  Outputs (all required): counts [N]
+ * (pre-drop), offsets [N+1] (exclusive scan of kept counts), slot [T*k],
+ * perm [T*k], n_kept_dropped [2] = {R, T*k - R}. */
+moe_status moe_dispatch(const moe_shape* shape, const int32_t* topk_idx,
+                        int32_t* counts, int32_t* offsets, int32_t* slot,
+                        int32_t* perm, int32_t* n_kept_dropped, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/* Expert FFNs over the dispatched rows (one grouped launch per projection).
+ * x [T,d]; perm, offsets from moe_dispatch; w1, w2 routed weights;
+ * w1_shared/w2_shared required iff d_ff_shared > 0.  Outputs: y_perm
+ * [T*k, d] dtype, row s = E_e(x_t) for the kept assignment perm[s]
+ * (rows >= R untouched); y_shared [T,d] dtype = S(x_t) (required iff
+ * d_ff_shared > 0). */
+moe_status moe_expert_ffn(const moe_shape* shape, const void* x,
+                          const int32_t* perm, const int32_t* offsets,
+                          const void* w1, const void* w2,
+                          const void* w1_shared, const void* w2_shared,
+                          void* y_perm, void* y_shared, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/* Combine: y_t = sum_j [slot_tj >= 0] g_tj y_perm[slot_tj] (+ y_shared_t),
+ * fp32 accumulation in ascending j, then the shared term; dropped
+ * assignments add nothing.  y_shared NULL when there is no shared expert. */
+moe_status moe_combine(const moe_shape* shape, const void* y_perm,
+                       const void* y_shared, const int32_t* slot,
+                       const float* topk_w, void* y, void* stream);
+
+/* Balancing step after a forward: with load_i = counts[i] (pre-drop) and
+ * mean load T*k/N,  bias_i <- fl32(bias_i - fl32(step * sign(N*load_i -
+ * T*k))), then clamped to [-clamp, clamp] when clamp > 0.  If scores and
+ * aux_out are given, aux_out[0] = N * sum_i (counts_i / T) * mean_t s_ti
+ * (computed before the bias changes; it does not depend on the bias).
+ * counts, scores [T,N], bias [N], aux_out [1]: device pointers; counts and
+ * bias required, step finite. */
+moe_status moe_bias_update(const moe_shape* shape, const int32_t* counts,
+                           const float* scores, float step, float clamp,
+                           float* bias, float* aux_out, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/* The whole layer: route -> dispatch -> expert FFNs -> combine on `stream`.
+ * Required: x, w_router, w1, w2, y (and the shared weights iff
+ * d_ff_shared > 0).  Optional inputs logit_add, bias; optional outputs
+ * (NULL: kept in the workspace only) scores_out [T,N], topk_idx, topk_w
+ * [T,k], counts [N], offsets [N+1], slot [T*k], n_kept_dropped [2]. */
+moe_status moe_forward(const moe_shape* shape, const void* x,
+                       const float* w_router, const float* logit_add,
+                       const float* bias, const void* w1, const void* w2,
+                       const void* w1_shared, const void* w2_shared, void* y,
+                       float* scores_out, int32_t* topk_idx, float* topk_w,
+                       int32_t* counts, int32_t* offsets, int32_t* slot,
+                       int32_t* n_kept_dropped, void* ws, size_t ws_bytes,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

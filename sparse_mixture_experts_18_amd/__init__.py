@@ -1,0 +1,314 @@
+"""Sparse MoE FFN layer forward on MI355X: Python binding of libmoe.so.
+
+Argument marshalling only.  Every step of the layer runs in the HIP kernels
+of libmoe.so (built in-tree by ``sparse_mixture_experts_18_amd.build``);
+PyTorch supplies device memory and the current HIP stream.  There is no
+fallback: if the library is missing or fails to load, every call raises.
+
+The functions mirror the C ABI in include/moe.h one to one (same names, same
+argument order, tensors in place of pointers):
+
+    moe_route, moe_dispatch, moe_expert_ffn, moe_combine, moe_bias_update,
+    moe_forward, moe_workspace_bytes, moe_check_shape, moe_capacity,
+    moe_status_string, moe_abi_version
+
+plus ``MoeShape`` (the C struct), ``workspace(shape)`` and ``forward(...)``,
+a convenience wrapper that allocates the outputs of one layer forward.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+import torch  # loads the HIP runtime the library binds to
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
+MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
+MOE_CAP_TOKENS, MOE_CAP_ASSIGNMENTS = 0, 1
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {moe_status_string(status)}")
+
+
+class MoeShape(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int64),
+        ("d_model", ctypes.c_int32),
+        ("n_experts", ctypes.c_int32),
+        ("top_k", ctypes.c_int32),
+        ("d_ff", ctypes.c_int32),
+        ("d_ff_shared", ctypes.c_int32),
+        ("score_fn", ctypes.c_int32),
+        ("renormalize", ctypes.c_int32),
+        ("n_groups", ctypes.c_int32),
+        ("topk_groups", ctypes.c_int32),
+        ("capacity_factor", ctypes.c_float),
+        ("capacity_rule", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+    ]
+
+    @classmethod
+    def make(cls, T, d_model, n_experts, top_k, d_ff, d_ff_shared=0,
+             score_fn="softmax", renormalize=True, n_groups=1, topk_groups=1,
+             capacity_factor=0.0, capacity_rule="tokens", dtype="bf16") -> "MoeShape":
+        return cls(int(T), int(d_model), int(n_experts), int(top_k), int(d_ff),
+                   int(d_ff_shared),
+                   MOE_SCORE_SIGMOID if score_fn == "sigmoid" else MOE_SCORE_SOFTMAX,
+                   1 if renormalize else 0, int(n_groups), int(topk_groups),
+                   float(capacity_factor),
+                   MOE_CAP_ASSIGNMENTS if capacity_rule == "assignments" else MOE_CAP_TOKENS,
+                   MOE_DTYPE_F32 if dtype in ("f32", torch.float32) else MOE_DTYPE_BF16)
+
+    @classmethod
+    def from_config(cls, cfg, T: Optional[int] = None) -> "MoeShape":
+        """From a workloads.LayerConfig (or anything with the same fields)."""
+        return cls.make(cfg.T if T is None else T, cfg.d_model, cfg.n_experts, cfg.top_k,
+                        cfg.d_ff, cfg.d_ff_shared, cfg.score_fn, cfg.renormalize,
+                        cfg.n_groups, cfg.topk_groups, cfg.capacity_factor,
+                        cfg.capacity_rule, cfg.dtype)
+
+    def replace(self, **kw) -> "MoeShape":
+        s = MoeShape()
+        ctypes.pointer(s)[0] = self
+        for k, v in kw.items():
+            setattr(s, k, v)
+        return s
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == MOE_DTYPE_F32 else torch.bfloat16
+
+    def __repr__(self):
+        return "MoeShape(" + ", ".join(f"{f}={getattr(self, f)}" for f, _ in self._fields_) + ")"
+
+
+_P = ctypes.c_void_p
+_S = ctypes.POINTER(MoeShape)
+_SIGS = {
+    "moe_abi_version": (ctypes.c_int, []),
+    "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_check_shape": (ctypes.c_int, [_S]),
+    "moe_capacity": (ctypes.c_int64, [_S]),
+    "moe_workspace_bytes": (ctypes.c_size_t, [_S]),
+    "moe_route": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_dispatch": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_expert_ffn": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                      ctypes.c_size_t, _P]),
+    "moe_combine": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P]),
+    "moe_bias_update": (ctypes.c_int, [_S, _P, _P, ctypes.c_float, ctypes.c_float, _P, _P, _P,
+                                       ctypes.c_size_t, _P]),
+    "moe_forward": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                   _P, _P, _P, _P, ctypes.c_size_t, _P]),
+}
+EXPORTED = tuple(_SIGS)
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmoe.so.  Raises if it is not built: there is no fallback."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -m sparse_mixture_experts_18_amd.build`")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(l, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = l
+    return _lib
+
+
+def _check(status: int, where: str):
+    if status != MOE_OK:
+        raise MoeError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype=None, numel=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+# ---- host-only entry points -------------------------------------------------
+
+def moe_abi_version() -> int:
+    return lib().moe_abi_version()
+
+
+def moe_status_string(status: int) -> str:
+    return lib().moe_status_string(int(status)).decode()
+
+
+def moe_check_shape(shape: MoeShape) -> int:
+    return lib().moe_check_shape(ctypes.byref(shape))
+
+
+def moe_capacity(shape: MoeShape) -> int:
+    return lib().moe_capacity(ctypes.byref(shape))
+
+
+def moe_workspace_bytes(shape: MoeShape) -> int:
+    return lib().moe_workspace_bytes(ctypes.byref(shape))
+
+
+def workspace(shape: MoeShape, device="cuda") -> torch.Tensor:
+    """A 256-byte aligned uint8 workspace tensor of moe_workspace_bytes."""
+    n = moe_workspace_bytes(shape)
+    if n == 0:
+        _check(moe_check_shape(shape) or MOE_ERR_INVALID, "moe_workspace_bytes")
+    buf = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    off = (-buf.data_ptr()) % 256
+    return buf[off:off + n]
+
+
+def _ws(ws: torch.Tensor):
+    return ws.data_ptr(), ws.numel()
+
+
+# ---- device entry points (enqueue on the current stream) ---------------------
+
+def _dt(shape):
+    return shape.torch_dtype
+
+
+def moe_route(shape, x, w_router, logit_add, scores_in, bias, logits_out, scores_out,
+              topk_idx, topk_w, ws, stream=None):
+    T, N, k = shape.T, shape.n_experts, shape.top_k
+    p, n = _ws(ws)
+    st = lib().moe_route(
+        ctypes.byref(shape), _ptr(x, "x", _dt(shape), T * shape.d_model),
+        _ptr(w_router, "w_router", torch.float32, N * shape.d_model),
+        _ptr(logit_add, "logit_add", torch.float32, T * N),
+        _ptr(scores_in, "scores_in", torch.float32, T * N),
+        _ptr(bias, "bias", torch.float32, N),
+        _ptr(logits_out, "logits_out", torch.float32, T * N),
+        _ptr(scores_out, "scores_out", torch.float32, T * N),
+        _ptr(topk_idx, "topk_idx", torch.int32, T * k),
+        _ptr(topk_w, "topk_w", torch.float32, T * k), p, n, _stream(stream))
+    _check(st, "moe_route")
+
+
+def moe_dispatch(shape, topk_idx, counts, offsets, slot, perm, n_kept_dropped, ws,
+                 stream=None):
+    T, N, k = shape.T, shape.n_experts, shape.top_k
+    p, n = _ws(ws)
+    st = lib().moe_dispatch(
+        ctypes.byref(shape), _ptr(topk_idx, "topk_idx", torch.int32, T * k),
+        _ptr(counts, "counts", torch.int32, N), _ptr(offsets, "offsets", torch.int32, N + 1),
+        _ptr(slot, "slot", torch.int32, T * k), _ptr(perm, "perm", torch.int32, T * k),
+        _ptr(n_kept_dropped, "n_kept_dropped", torch.int32, 2), p, n, _stream(stream))
+    _check(st, "moe_dispatch")
+
+
+def moe_expert_ffn(shape, x, perm, offsets, w1, w2, w1_shared, w2_shared, y_perm, y_shared,
+                   ws, stream=None):
+    T, N, k, d, f, fs = (shape.T, shape.n_experts, shape.top_k, shape.d_model, shape.d_ff,
+                         shape.d_ff_shared)
+    dt = _dt(shape)
+    p, n = _ws(ws)
+    st = lib().moe_expert_ffn(
+        ctypes.byref(shape), _ptr(x, "x", dt, T * d), _ptr(perm, "perm", torch.int32, T * k),
+        _ptr(offsets, "offsets", torch.int32, N + 1), _ptr(w1, "w1", dt, N * 2 * f * d),
+        _ptr(w2, "w2", dt, N * d * f), _ptr(w1_shared, "w1_shared", dt, 2 * fs * d),
+        _ptr(w2_shared, "w2_shared", dt, d * fs), _ptr(y_perm, "y_perm", dt, T * k * d),
+        _ptr(y_shared, "y_shared", dt, T * d), p, n, _stream(stream))
+    _check(st, "moe_expert_ffn")
+
+
+def moe_combine(shape, y_perm, y_shared, slot, topk_w, y, stream=None):
+    T, k, d = shape.T, shape.top_k, shape.d_model
+    dt = _dt(shape)
+    st = lib().moe_combine(
+        ctypes.byref(shape), _ptr(y_perm, "y_perm", dt, T * k * d),
+        _ptr(y_shared, "y_shared", dt, T * d), _ptr(slot, "slot", torch.int32, T * k),
+        _ptr(topk_w, "topk_w", torch.float32, T * k), _ptr(y, "y", dt, T * d),
+        _stream(stream))
+    _check(st, "moe_combine")
+
+
+def moe_bias_update(shape, counts, scores, step, clamp, bias, aux_out, ws, stream=None):
+    T, N = shape.T, shape.n_experts
+    p, n = _ws(ws)
+    st = lib().moe_bias_update(
+        ctypes.byref(shape), _ptr(counts, "counts", torch.int32, N),
+        _ptr(scores, "scores", torch.float32, T * N), float(step), float(clamp),
+        _ptr(bias, "bias", torch.float32, N), _ptr(aux_out, "aux_out", torch.float32, 1), p, n,
+        _stream(stream))
+    _check(st, "moe_bias_update")
+
+
+def moe_forward(shape, x, w_router, logit_add, bias, w1, w2, w1_shared, w2_shared, y,
+                scores_out, topk_idx, topk_w, counts, offsets, slot, n_kept_dropped, ws,
+                stream=None):
+    T, N, k, d, f, fs = (shape.T, shape.n_experts, shape.top_k, shape.d_model, shape.d_ff,
+                         shape.d_ff_shared)
+    dt = _dt(shape)
+    p, n = _ws(ws)
+    st = lib().moe_forward(
+        ctypes.byref(shape), _ptr(x, "x", dt, T * d),
+        _ptr(w_router, "w_router", torch.float32, N * d),
+        _ptr(logit_add, "logit_add", torch.float32, T * N),
+        _ptr(bias, "bias", torch.float32, N), _ptr(w1, "w1", dt, N * 2 * f * d),
+        _ptr(w2, "w2", dt, N * d * f), _ptr(w1_shared, "w1_shared", dt, 2 * fs * d),
+        _ptr(w2_shared, "w2_shared", dt, d * fs), _ptr(y, "y", dt, T * d),
+        _ptr(scores_out, "scores_out", torch.float32, T * N),
+        _ptr(topk_idx, "topk_idx", torch.int32, T * k),
+        _ptr(topk_w, "topk_w", torch.float32, T * k), _ptr(counts, "counts", torch.int32, N),
+        _ptr(offsets, "offsets", torch.int32, N + 1), _ptr(slot, "slot", torch.int32, T * k),
+        _ptr(n_kept_dropped, "n_kept_dropped", torch.int32, 2), p, n, _stream(stream))
+    _check(st, "moe_forward")
+
+
+# ---- convenience ------------------------------------------------------------
+
+def forward(shape: MoeShape, x, w_router, w1, w2, *, logit_add=None, bias=None,
+            w1_shared=None, w2_shared=None, ws=None, outputs: bool = True,
+            stream=None) -> Dict[str, torch.Tensor]:
+    """Allocate the outputs and run moe_forward on the current stream.
+    Returns y and (if ``outputs``) scores, topk_idx, topk_w, counts, offsets,
+    slot and n_kept_dropped."""
+    dev = x.device
+    T, N, k, d = shape.T, shape.n_experts, shape.top_k, shape.d_model
+    out = {"y": torch.empty((T, d), dtype=shape.torch_dtype, device=dev)}
+    if outputs:
+        out.update(
+            scores=torch.empty((T, N), dtype=torch.float32, device=dev),
+            topk_idx=torch.empty((T, k), dtype=torch.int32, device=dev),
+            topk_w=torch.empty((T, k), dtype=torch.float32, device=dev),
+            counts=torch.empty((N,), dtype=torch.int32, device=dev),
+            offsets=torch.empty((N + 1,), dtype=torch.int32, device=dev),
+            slot=torch.empty((T * k,), dtype=torch.int32, device=dev),
+            n_kept_dropped=torch.empty((2,), dtype=torch.int32, device=dev))
+    if ws is None:
+        ws = workspace(shape, dev)
+    g = out.get
+    moe_forward(shape, x, w_router, logit_add, bias, w1, w2, w1_shared, w2_shared, out["y"],
+                g("scores"), g("topk_idx"), g("topk_w"), g("counts"), g("offsets"), g("slot"),
+                g("n_kept_dropped"), ws, stream)
+    return out

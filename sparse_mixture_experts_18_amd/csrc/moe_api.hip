@@ -1,0 +1,240 @@
+// C ABI entry points: argument validation, workspace layout, launch order.
+#include <math.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+moe_status check_shape(const moe_shape* s) {
+  if (!s) return MOE_ERR_INVALID;
+  if (s->T < 1 || s->n_experts < 1 || s->top_k < 1 || s->top_k > s->n_experts ||
+      s->d_model < 1 || s->d_ff < 1 || s->d_ff_shared < 0)
+    return MOE_ERR_INVALID;
+  if (s->score_fn != MOE_SCORE_SOFTMAX && s->score_fn != MOE_SCORE_SIGMOID)
+    return MOE_ERR_INVALID;
+  if (s->dtype != MOE_DTYPE_F32 && s->dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID;
+  if (s->capacity_rule != MOE_CAP_TOKENS && s->capacity_rule != MOE_CAP_ASSIGNMENTS)
+    return MOE_ERR_INVALID;
+  if (s->renormalize != 0 && s->renormalize != 1) return MOE_ERR_INVALID;
+  if (isnan(s->capacity_factor)) return MOE_ERR_INVALID;
+  if (s->n_groups < 1 || s->n_experts % s->n_groups != 0) return MOE_ERR_INVALID;
+  if (s->topk_groups < 1 || s->topk_groups > s->n_groups) return MOE_ERR_INVALID;
+  if (s->top_k % s->topk_groups != 0) return MOE_ERR_INVALID;
+  if (s->top_k / s->topk_groups > s->n_experts / s->n_groups) return MOE_ERR_INVALID;
+  if (s->n_experts > 512 || s->top_k > 16 || s->n_groups > 64) return MOE_ERR_UNSUPPORTED;
+  const int q = s->dtype == MOE_DTYPE_BF16 ? 64 : 32;
+  if (s->d_model % q || s->d_ff % q || s->d_ff_shared % q) return MOE_ERR_UNSUPPORTED;
+  const long long A = s->T * (long long)s->top_k;
+  long long wmax = s->d_model;
+  if (s->d_ff > wmax) wmax = s->d_ff;
+  if (s->d_ff_shared > wmax) wmax = s->d_ff_shared;
+  if (A * wmax >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
+  if (2LL * s->d_ff * s->d_model >= (1LL << 31) ||
+      2LL * s->d_ff_shared * s->d_model >= (1LL << 31))
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+inline moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+int64_t capacity_of(const moe_shape& s) {
+  const double cf = (double)s.capacity_factor;
+  if (!(cf > 0.0)) return -1;
+  const double T = (double)s.T, N = (double)s.n_experts, k = (double)s.top_k;
+  if (s.capacity_rule == MOE_CAP_TOKENS) return (int64_t)floor(cf * T / N);
+  int64_t c = (int64_t)(k * T / N * cf);
+  return c > s.top_k ? c : s.top_k;
+}
+
+Workspace layout_workspace(const moe_shape& s, void* ws) {
+  Workspace w{};
+  const size_t T = (size_t)s.T, N = (size_t)s.n_experts, k = (size_t)s.top_k;
+  const size_t A = T * k, d = (size_t)s.d_model;
+  const size_t es = s.dtype == MOE_DTYPE_BF16 ? 2 : 4;
+  const size_t nchunks = (A + kDispatchChunk - 1) / kDispatchChunk;
+  plan_caps(s, w.plan1_cap, w.plan2_cap);
+  size_t off = 0;
+  char* base = static_cast<char*>(ws);
+  auto take = [&](size_t bytes) -> void* {
+    void* p = base ? base + off : nullptr;
+    off += align_up(bytes ? bytes : 1);
+    return p;
+  };
+  w.logits = static_cast<float*>(take(T * N * 4));
+  w.scores = static_cast<float*>(take(T * N * 4));
+  w.topk_idx = static_cast<int32_t*>(take(A * 4));
+  w.topk_w = static_cast<float*>(take(A * 4));
+  w.counts = static_cast<int32_t*>(take(N * 4));
+  w.offsets = static_cast<int32_t*>(take((N + 1) * 4));
+  w.slot = static_cast<int32_t*>(take(A * 4));
+  w.perm = static_cast<int32_t*>(take(A * 4));
+  w.nkd = static_cast<int32_t*>(take(2 * 4));
+  w.rank = static_cast<int32_t*>(take(A * 4));
+  w.hist = static_cast<int32_t*>(take(nchunks * N * 4));
+  w.base = static_cast<int32_t*>(take(nchunks * N * 4));
+  w.plan1_count = static_cast<int32_t*>(take(4));
+  w.plan1 = static_cast<WorkItem*>(take((size_t)w.plan1_cap * sizeof(WorkItem)));
+  w.plan2_count = static_cast<int32_t*>(take(4));
+  w.plan2 = static_cast<WorkItem*>(take((size_t)w.plan2_cap * sizeof(WorkItem)));
+  w.h = take(A * (size_t)s.d_ff * es);
+  w.h_shared = take(T * (size_t)s.d_ff_shared * es);
+  w.y_perm = take(A * d * es);
+  w.y_shared = take(T * d * es);
+  w.pmean = static_cast<double*>(take(N * 8));
+  w.total = off;
+  return w;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+namespace {
+moe_status check_ws(const moe_shape* s, const void* ws, size_t ws_bytes, Workspace& w) {
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) % 256) != 0) return MOE_ERR_WORKSPACE;
+  w = layout_workspace(*s, const_cast<void*>(ws));
+  if (ws_bytes < w.total) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_string(moe_status st) {
+  switch (st) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID: return "MOE_ERR_INVALID: null required pointer or inconsistent shape";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape outside the kernels' limits";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: kernel launch failed";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+moe_status moe_check_shape(const moe_shape* shape) { return check_shape(shape); }
+
+int64_t moe_capacity(const moe_shape* shape) {
+  if (check_shape(shape) != MOE_OK) return -1;
+  return capacity_of(*shape);
+}
+
+size_t moe_workspace_bytes(const moe_shape* shape) {
+  if (check_shape(shape) != MOE_OK) return 0;
+  return layout_workspace(*shape, nullptr).total;
+}
+
+moe_status moe_route(const moe_shape* shape, const void* x, const float* w_router,
+                     const float* logit_add, const float* scores_in, const float* bias,
+                     float* logits_out, float* scores_out, int32_t* topk_idx, float* topk_w,
+                     void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!topk_idx || !topk_w) return MOE_ERR_INVALID;
+  if (!scores_in && (!x || !w_router)) return MOE_ERR_INVALID;
+  Workspace w;
+  if ((st = check_ws(shape, ws, ws_bytes, w)) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (scores_in)
+    return hip_status(
+        launch_topk(*shape, scores_in, nullptr, true, bias, scores_out, topk_idx, topk_w, s));
+  float* logits = logits_out ? logits_out : w.logits;
+  hipError_t e = launch_router_gemm(*shape, x, w_router, logits, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(
+      launch_topk(*shape, logits, logit_add, false, bias, scores_out, topk_idx, topk_w, s));
+}
+
+moe_status moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, int32_t* counts,
+                        int32_t* offsets, int32_t* slot, int32_t* perm, int32_t* n_kept_dropped,
+                        void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!topk_idx || !counts || !offsets || !slot || !perm || !n_kept_dropped)
+    return MOE_ERR_INVALID;
+  Workspace w;
+  if ((st = check_ws(shape, ws, ws_bytes, w)) != MOE_OK) return st;
+  return hip_status(launch_dispatch(*shape, topk_idx, counts, offsets, slot, perm,
+                                    n_kept_dropped, w, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_expert_ffn(const moe_shape* shape, const void* x, const int32_t* perm,
+                          const int32_t* offsets, const void* w1, const void* w2,
+                          const void* w1_shared, const void* w2_shared, void* y_perm,
+                          void* y_shared, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!x || !perm || !offsets || !w1 || !w2 || !y_perm) return MOE_ERR_INVALID;
+  if (shape->d_ff_shared > 0 && (!w1_shared || !w2_shared || !y_shared)) return MOE_ERR_INVALID;
+  Workspace w;
+  if ((st = check_ws(shape, ws, ws_bytes, w)) != MOE_OK) return st;
+  return hip_status(launch_expert_ffn(*shape, x, perm, offsets, w1, w2, w1_shared, w2_shared,
+                                      y_perm, shape->d_ff_shared > 0 ? y_shared : nullptr, w,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_combine(const moe_shape* shape, const void* y_perm, const void* y_shared,
+                       const int32_t* slot, const float* topk_w, void* y, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!y_perm || !slot || !topk_w || !y) return MOE_ERR_INVALID;
+  if (shape->d_ff_shared > 0 && !y_shared) return MOE_ERR_INVALID;
+  return hip_status(launch_combine(*shape, y_perm, shape->d_ff_shared > 0 ? y_shared : nullptr,
+                                   slot, topk_w, y, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_bias_update(const moe_shape* shape, const int32_t* counts, const float* scores,
+                           float step, float clamp, float* bias, float* aux_out, void* ws,
+                           size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!counts || !bias || !isfinite(step) || isnan(clamp)) return MOE_ERR_INVALID;
+  Workspace w;
+  if ((st = check_ws(shape, ws, ws_bytes, w)) != MOE_OK) return st;
+  return hip_status(launch_bias_update(*shape, counts, scores, step, clamp, bias, aux_out,
+                                       w.pmean, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_router,
+                       const float* logit_add, const float* bias, const void* w1,
+                       const void* w2, const void* w1_shared, const void* w2_shared, void* y,
+                       float* scores_out, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                       int32_t* offsets, int32_t* slot, int32_t* n_kept_dropped, void* ws,
+                       size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!x || !w_router || !w1 || !w2 || !y) return MOE_ERR_INVALID;
+  if (shape->d_ff_shared > 0 && (!w1_shared || !w2_shared)) return MOE_ERR_INVALID;
+  Workspace w;
+  if ((st = check_ws(shape, ws, ws_bytes, w)) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const moe_shape& sh = *shape;
+  float* sc = scores_out ? scores_out : w.scores;
+  int32_t* ti = topk_idx ? topk_idx : w.topk_idx;
+  float* tw = topk_w ? topk_w : w.topk_w;
+  int32_t* cn = counts ? counts : w.counts;
+  int32_t* of = offsets ? offsets : w.offsets;
+  int32_t* sl = slot ? slot : w.slot;
+  int32_t* nk = n_kept_dropped ? n_kept_dropped : w.nkd;
+  const bool shared = sh.d_ff_shared > 0;
+  if (launch_router_gemm(sh, x, w_router, w.logits, s) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_topk(sh, w.logits, logit_add, false, bias, sc, ti, tw, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (launch_dispatch(sh, ti, cn, of, sl, w.perm, nk, w, s) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_expert_ffn(sh, x, w.perm, of, w1, w2, w1_shared, w2_shared, w.y_perm,
+                        shared ? w.y_shared : nullptr, w, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  return hip_status(
+      launch_combine(sh, w.y_perm, shared ? w.y_shared : nullptr, sl, tw, y, s));
+}
+
+}  // extern "C"

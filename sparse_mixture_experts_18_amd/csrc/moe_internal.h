@@ -1,0 +1,93 @@
+// Internal declarations shared by the HIP translation units of libmoe.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+typedef unsigned short bf16_t;  // raw bf16 bits in memory
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// round to nearest even; NaN stays a quiet NaN
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+constexpr int kWave = 64;
+constexpr int kDispatchChunk = 512;  // assignments ranked by one wave
+
+// Grouped-GEMM tile geometry.  bf16 path: MFMA tiles; fp32 path: VALU tiles.
+constexpr int kBM = 128;       // rows (assignments) per work item, bf16
+constexpr int kBN1 = 128;      // h columns per GEMM1 work item (256 W1 rows)
+constexpr int kBN2 = 128;      // output columns per GEMM2 work item
+constexpr int kBMf = 32;       // fp32 path
+constexpr int kBNf = 32;
+
+// one unit of grouped-GEMM work: rows [row0, row0+nrows) of segment `seg`
+// (seg < N: routed expert, seg == N: shared expert), output column tile `nt`
+struct WorkItem {
+  int seg, row0, nrows, nt;
+};
+
+struct Workspace {
+  float* logits;
+  float* scores;
+  int32_t* topk_idx;
+  float* topk_w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* slot;
+  int32_t* perm;
+  int32_t* nkd;
+  int32_t* rank;
+  int32_t* hist;
+  int32_t* base;
+  int32_t* plan1_count;
+  WorkItem* plan1;
+  int32_t* plan2_count;
+  WorkItem* plan2;
+  void* h;         // routed h [T*k, d_ff], then shared h [T, d_ff_shared]
+  void* h_shared;
+  void* y_perm;    // [T*k, d]
+  void* y_shared;  // [T, d]
+  double* pmean;   // [N] mean score per expert (balancing step)
+  size_t total;
+  int64_t plan1_cap, plan2_cap;
+};
+
+// Carve `ws` (may be NULL to only compute sizes) for a validated shape.
+Workspace layout_workspace(const moe_shape& s, void* ws);
+
+int64_t capacity_of(const moe_shape& s);  // -1 = dropless
+
+// ---- launchers (validated arguments; return hipError_t of the launch) ----
+hipError_t launch_router_gemm(const moe_shape& s, const void* x, const float* w_router,
+                              float* logits, hipStream_t st);
+hipError_t launch_topk(const moe_shape& s, const float* logits, const float* logit_add,
+                       bool logits_are_scores, const float* bias, float* scores_out,
+                       int32_t* topk_idx, float* topk_w, hipStream_t st);
+hipError_t launch_dispatch(const moe_shape& s, const int32_t* topk_idx, int32_t* counts,
+                           int32_t* offsets, int32_t* slot, int32_t* perm, int32_t* nkd,
+                           const Workspace& w, hipStream_t st);
+hipError_t launch_expert_ffn(const moe_shape& s, const void* x, const int32_t* perm,
+                             const int32_t* offsets, const void* w1, const void* w2,
+                             const void* w1s, const void* w2s, void* y_perm, void* y_shared,
+                             const Workspace& w, hipStream_t st);
+hipError_t launch_combine(const moe_shape& s, const void* y_perm, const void* y_shared,
+                          const int32_t* slot, const float* topk_w, void* y, hipStream_t st);
+hipError_t launch_bias_update(const moe_shape& s, const int32_t* counts, const float* scores,
+                              float step, float clamp, float* bias, float* aux_out,
+                              double* p_scratch, hipStream_t st);
+void plan_caps(const moe_shape& s, int64_t& cap1, int64_t& cap2);
+
+}  // namespace moe

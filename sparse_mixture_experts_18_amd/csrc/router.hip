@@ -1,0 +1,299 @@
+// Router: affinity GEMM (fp32) and per-token scores + top-k selection.
+//
+// Affinity l = x W_r^T with a bias-free gate ("MoE architecture in
+// practice", routing-math section; llm-compass MoE page, gate equation).
+// Scores: softmax over experts, or an independent sigmoid per expert
+// ("MoE common taste of open models", section 7).  Selection on
+// key = fl32(s + b) with weights from the raw score (llm-compass MoE page,
+// aux-loss-free section; the article's BiasBalancedRouter), optional group
+// limit ("MoE industrial evolution", section 4), top-k with ties to the lower
+// expert index, renormalised gates.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+// ---------------------------------------------------------------------------
+// K1: logits[T,N] = x[T,d] . W_r[N,d]^T, fp32 FMA.  Each output is a single
+// FMA chain over k = 0..d-1 in order, so a token's logits do not depend on
+// the batch it is in.
+// ---------------------------------------------------------------------------
+constexpr int RT_BM = 64, RT_BN = 64, RT_BK = 16;
+
+template <typename XT>
+__device__ __forceinline__ void load4(const XT* p, float* o);
+template <>
+__device__ __forceinline__ void load4<float>(const float* p, float* o) {
+  float4 v = *reinterpret_cast<const float4*>(p);
+  o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+}
+template <>
+__device__ __forceinline__ void load4<bf16_t>(const bf16_t* p, float* o) {
+  uint2 v = *reinterpret_cast<const uint2*>(p);
+  o[0] = __uint_as_float(v.x << 16);
+  o[1] = __uint_as_float(v.x & 0xffff0000u);
+  o[2] = __uint_as_float(v.y << 16);
+  o[3] = __uint_as_float(v.y & 0xffff0000u);
+}
+
+template <typename XT>
+__global__ __launch_bounds__(256) void router_gemm_kernel(const XT* __restrict__ x,
+                                                          const float* __restrict__ w,
+                                                          float* __restrict__ logits,
+                                                          int T, int N, int d) {
+  __shared__ float As[RT_BK][RT_BM + 4];
+  __shared__ float Bs[RT_BK][RT_BN + 4];
+  const int tid = threadIdx.x;
+  const int m0 = blockIdx.x * RT_BM, n0 = blockIdx.y * RT_BN;
+  const int lr = tid >> 2, lk = (tid & 3) * 4;  // loader: row, k quad
+  const int ty = tid >> 4, tx = tid & 15;       // compute: 4x4 outputs
+  const int am = min(m0 + lr, T - 1), bn = min(n0 + lr, N - 1);
+  const XT* xa = x + (size_t)am * d + lk;
+  const float* wb = w + (size_t)bn * d + lk;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < d; k0 += RT_BK) {
+    float a4[4], b4[4];
+    load4<XT>(xa + k0, a4);
+    load4<float>(wb + k0, b4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      As[lk + i][lr] = a4[i];
+      Bs[lk + i][lr] = b4[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < RT_BK; ++kk) {
+      float4 a = *reinterpret_cast<const float4*>(&As[kk][ty * 4]);
+      float4 b = *reinterpret_cast<const float4*>(&Bs[kk][tx * 4]);
+      float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int m = m0 + ty * 4 + i;
+    if (m >= T) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int n = n0 + tx * 4 + j;
+      if (n < N) logits[(size_t)m * N + n] = acc[i][j];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K2: one wavefront per token.  Lane l holds experts [l*P, l*P+P).
+// ---------------------------------------------------------------------------
+
+// total order used for selection: NaN lowest, -0 == +0; 0 is reserved for
+// "not a candidate"
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 1u;  // NaN
+  if (u == 0x80000000u) u = 0u;
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return u + 1u;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint32_t lo = __shfl_xor((uint32_t)v, o, kWave);
+    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, kWave);
+    uint64_t w = ((uint64_t)hi << 32) | lo;
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+constexpr int TK_WAVES = 4;
+
+template <int P>
+__global__ __launch_bounds__(256) void topk_kernel(
+    const float* __restrict__ logits, const float* __restrict__ logit_add,
+    int logits_are_scores, const float* __restrict__ bias, float* __restrict__ scores_out,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int T, int N, int k,
+    int score_fn, int renorm, int n_groups, int topk_groups) {
+  __shared__ float keys_lds[TK_WAVES][512];
+  __shared__ float gsc[TK_WAVES][64];
+  __shared__ int gsel[TK_WAVES][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int t_raw = blockIdx.x * TK_WAVES + wv;
+  const bool valid = t_raw < T;  // tail waves compute on token T-1, write nothing
+  const int t = valid ? t_raw : T - 1;
+  const float* lrow = logits + (size_t)t * N;
+  float s[P];
+  uint32_t ok[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    int e = lane * P + p;
+    float v = -INFINITY;
+    if (e < N) {
+      v = lrow[e];
+      if (logit_add && !logits_are_scores) v += logit_add[(size_t)t * N + e];
+    }
+    s[p] = v;
+  }
+  if (!logits_are_scores) {
+    if (score_fn == MOE_SCORE_SOFTMAX) {
+      float m = s[0];
+#pragma unroll
+      for (int p = 1; p < P; ++p) m = fmaxf(m, s[p]);
+      m = wave_max(m);
+      float sum = 0.f;
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        int e = lane * P + p;
+        s[p] = e < N ? expf(s[p] - m) : 0.f;
+        sum += s[p];
+      }
+      sum = wave_sum(sum);
+      const float inv = 1.0f / sum;
+#pragma unroll
+      for (int p = 0; p < P; ++p) s[p] = s[p] * inv;
+    } else {
+#pragma unroll
+      for (int p = 0; p < P; ++p) s[p] = 1.0f / (1.0f + expf(-s[p]));
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    int e = lane * P + p;
+    if (e < N) {
+      if (scores_out && valid) scores_out[(size_t)t * N + e] = s[p];
+      float key = bias ? s[p] + bias[e] : s[p];
+      ok[p] = order_key(key);
+      keys_lds[wv][e] = key;
+    } else {
+      ok[p] = 0u;
+    }
+  }
+  if (n_groups > 1) {  // uniform across the block
+    // group score: fl32 sum of the best m keys of the group, best first
+    const int gsz = N / n_groups, m = k / topk_groups;
+    __syncthreads();
+    if (lane < n_groups) {
+      const float* gk = &keys_lds[wv][lane * gsz];
+      float acc = 0.f;
+      uint32_t prev_o = 0xffffffffu;
+      int prev_i = -1;
+      for (int r = 0; r < m; ++r) {
+        // next key after (prev_o, prev_i) in the order (key desc, index asc)
+        uint32_t bo = 0u;
+        int bi = -1;
+        float bv = 0.f;
+        for (int i = 0; i < gsz; ++i) {
+          uint32_t o = order_key(gk[i]);
+          bool after = (o < prev_o) || (o == prev_o && i > prev_i);
+          if (after && (bi < 0 || o > bo)) {
+            bo = o;
+            bi = i;
+            bv = gk[i];
+          }
+        }
+        acc = (r == 0) ? bv : acc + bv;
+        prev_o = bo;
+        prev_i = bi;
+      }
+      gsc[wv][lane] = acc;
+    }
+    __syncthreads();
+    if (lane < n_groups) {
+      uint32_t mine = order_key(gsc[wv][lane]);
+      int rank = 0;
+      for (int g = 0; g < n_groups; ++g) {
+        uint32_t o = order_key(gsc[wv][g]);
+        rank += (o > mine) || (o == mine && g < lane);
+      }
+      gsel[wv][lane] = rank < topk_groups;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      int e = lane * P + p;
+      if (e < N && !gsel[wv][e / gsz]) ok[p] = 0u;
+    }
+  }
+  // k rounds of wave arg-max on (key desc, index asc); lane j keeps round j
+  int my_e = 0;
+  float my_s = 0.f;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      uint64_t c = ((uint64_t)ok[p] << 32) |
+                   (uint32_t)(0xffffffffu - (uint32_t)(lane * P + p));
+      best = c > best ? c : best;
+    }
+    best = wave_max_u64(best);
+    const int e = (int)(0xffffffffu - (uint32_t)best);
+    float sv = 0.f;
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+      if (lane * P + p == e) {
+        sv = s[p];
+        ok[p] = 0u;
+      }
+    sv = __shfl(sv, e / P, kWave);
+    if (lane == j) {
+      my_e = e;
+      my_s = sv;
+    }
+  }
+  // renormalise: fp32 sum in ascending j
+  float sum = 0.f;
+  for (int j = 0; j < k; ++j) sum += __shfl(my_s, j, kWave);
+  if (valid && lane < k) {
+    topk_idx[(size_t)t * k + lane] = my_e;
+    topk_w[(size_t)t * k + lane] = renorm ? my_s / sum : my_s;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_router_gemm(const moe_shape& s, const void* x, const float* w_router,
+                              float* logits, hipStream_t st) {
+  const int T = (int)s.T, N = s.n_experts, d = s.d_model;
+  dim3 grid((T + RT_BM - 1) / RT_BM, (N + RT_BN - 1) / RT_BN);
+  if (s.dtype == MOE_DTYPE_BF16)
+    router_gemm_kernel<bf16_t><<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(x), w_router,
+                                                      logits, T, N, d);
+  else
+    router_gemm_kernel<float><<<grid, 256, 0, st>>>(static_cast<const float*>(x), w_router,
+                                                     logits, T, N, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const moe_shape& s, const float* logits, const float* logit_add,
+                       bool logits_are_scores, const float* bias, float* scores_out,
+                       int32_t* topk_idx, float* topk_w, hipStream_t st) {
+  const int T = (int)s.T, N = s.n_experts;
+  dim3 grid((T + TK_WAVES - 1) / TK_WAVES);
+  const int P = (N + 63) / 64;
+#define MOE_TOPK(PP)                                                                        \
+  topk_kernel<PP><<<grid, 256, 0, st>>>(logits, logit_add, logits_are_scores ? 1 : 0, bias, \
+                                        scores_out, topk_idx, topk_w, T, N, s.top_k,       \
+                                        s.score_fn, s.renormalize, s.n_groups, s.topk_groups)
+  if (P <= 1) MOE_TOPK(1);
+  else if (P <= 2) MOE_TOPK(2);
+  else if (P <= 4) MOE_TOPK(4);
+  else MOE_TOPK(8);
+#undef MOE_TOPK
+  return hipGetLastError();
+}
+
+}  // namespace moe

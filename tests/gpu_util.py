@@ -1,0 +1,144 @@
+"""Helpers shared by the GPU parity tests: run the HIP path through the C ABI
+and compute the oracle's answer on the same seeded inputs."""
+from __future__ import annotations
+
+import sys
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+import torch
+
+import oracle
+import sparse_mixture_experts_18_amd as moe
+import workloads as W
+
+f32 = np.float32
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    t = t.detach()
+    if t.dtype == torch.bfloat16:
+        t = t.float()
+    return t.cpu().numpy()
+
+
+def rel_l2(a, b) -> float:
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    den = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / (den if den > 0 else 1.0))
+
+
+def tol_for(cfg) -> float:
+    """Output tolerance (relative L2): 2e-2 for bf16 layers, 1e-5 for fp32."""
+    return 1e-5 if cfg.dtype == "f32" else 2e-2
+
+
+def run_forward(inp: W.LayerInputs, shape: Optional[moe.MoeShape] = None) -> Dict[str, torch.Tensor]:
+    cfg = inp.cfg
+    shape = shape or moe.MoeShape.from_config(cfg, T=inp.x.shape[0])
+    out = moe.forward(shape, inp.x, inp.w_router, inp.w1, inp.w2, logit_add=inp.logit_add,
+                      bias=inp.bias, w1_shared=inp.w1_shared, w2_shared=inp.w2_shared)
+    torch.cuda.synchronize()
+    return out
+
+
+def run_steps(inp: W.LayerInputs, shape: Optional[moe.MoeShape] = None,
+              scores_in: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """route -> dispatch -> expert_ffn -> combine, each through its own entry point."""
+    cfg = inp.cfg
+    T = inp.x.shape[0]
+    shape = shape or moe.MoeShape.from_config(cfg, T=T)
+    N, k, d = shape.n_experts, shape.top_k, shape.d_model
+    dev = inp.x.device
+    ws = moe.workspace(shape, dev)
+    o = dict(
+        logits=torch.empty((T, N), dtype=torch.float32, device=dev),
+        scores=torch.empty((T, N), dtype=torch.float32, device=dev),
+        topk_idx=torch.empty((T, k), dtype=torch.int32, device=dev),
+        topk_w=torch.empty((T, k), dtype=torch.float32, device=dev),
+        counts=torch.empty((N,), dtype=torch.int32, device=dev),
+        offsets=torch.empty((N + 1,), dtype=torch.int32, device=dev),
+        slot=torch.empty((T * k,), dtype=torch.int32, device=dev),
+        perm=torch.empty((T * k,), dtype=torch.int32, device=dev),
+        n_kept_dropped=torch.empty((2,), dtype=torch.int32, device=dev),
+        y_perm=torch.zeros((T * k, d), dtype=shape.torch_dtype, device=dev),
+        y=torch.empty((T, d), dtype=shape.torch_dtype, device=dev),
+    )
+    o["y_shared"] = (torch.empty((T, d), dtype=shape.torch_dtype, device=dev)
+                     if shape.d_ff_shared > 0 else None)
+    moe.moe_route(shape, inp.x, inp.w_router, inp.logit_add, scores_in, inp.bias,
+                  None if scores_in is not None else o["logits"], o["scores"], o["topk_idx"],
+                  o["topk_w"], ws)
+    moe.moe_dispatch(shape, o["topk_idx"], o["counts"], o["offsets"], o["slot"], o["perm"],
+                     o["n_kept_dropped"], ws)
+    moe.moe_expert_ffn(shape, inp.x, o["perm"], o["offsets"], inp.w1, inp.w2, inp.w1_shared,
+                       inp.w2_shared, o["y_perm"], o["y_shared"], ws)
+    moe.moe_combine(shape, o["y_perm"], o["y_shared"], o["slot"], o["topk_w"], o["y"])
+    torch.cuda.synchronize()
+    return o
+
+
+def oracle_kwargs(inp: W.LayerInputs) -> dict:
+    c = inp.cfg
+    return dict(top_k=c.top_k, score_fn=c.score_fn, renormalize=c.renormalize,
+                n_groups=c.n_groups, topk_groups=c.topk_groups,
+                capacity_factor=c.capacity_factor, capacity_rule=c.capacity_rule,
+                bias=None if inp.bias is None else host(inp.bias))
+
+
+def weight_source(inp: W.LayerInputs):
+    """Stream one expert's weights to host memory at a time (exact fp32 copies
+    of the bf16 values)."""
+    return lambda e: (host(inp.w1[e]), host(inp.w2[e]))
+
+
+def oracle_layer(inp: W.LayerInputs, scores_gpu: torch.Tensor,
+                 tokens: Optional[Sequence[int]] = None, compute_outputs=True):
+    """The oracle on the same inputs, routing from the GPU's fp32 scores
+    (routing parity is defined on identical fp32 scores)."""
+    kw = oracle_kwargs(inp)
+    return oracle.moe_layer(
+        host(inp.x) if compute_outputs else np.zeros((inp.x.shape[0], 1)),
+        host(inp.w_router), weight_source(inp), None,
+        w1_shared=None if inp.w1_shared is None else host(inp.w1_shared),
+        w2_shared=None if inp.w2_shared is None else host(inp.w2_shared),
+        scores_fp32=host(scores_gpu), tokens=tokens, compute_outputs=compute_outputs, **kw)
+
+
+def check_routing_and_dispatch(out: Dict[str, torch.Tensor], ref: dict, T: int, k: int):
+    """Bit-exact: top-k indices, counts, offsets, slots, permutation, drops."""
+    idx = host(out["topk_idx"]).astype(np.int64)
+    assert (idx == ref["topk_idx"]).all(), "topk_idx differs"
+    assert (host(out["counts"]) == ref["counts"]).all(), "counts differ"
+    assert (host(out["offsets"]) == ref["offsets"]).all(), "offsets differ"
+    assert (host(out["slot"]) == ref["slot"]).all(), "slot differs"
+    nkd = host(out["n_kept_dropped"])
+    R = int(ref["offsets"][-1])
+    assert nkd[0] == R and nkd[1] == ref["n_dropped"]
+    if "perm" in out:
+        assert (host(out["perm"])[:R] == ref["perm"]).all(), "perm differs"
+    # gates: fp32 sum and divide vs fp64 from the same fp32 scores
+    g = host(out["topk_w"]).astype(np.float64)
+    assert np.abs(g - ref["topk_w"]).max() <= 4 * k * 2.0 ** -24 * max(1.0, np.abs(ref["topk_w"]).max())
+
+
+def router_tolerance_ok(x: np.ndarray, wr: np.ndarray, logit_add, logits_gpu: np.ndarray):
+    """|l_gpu - l| <= gamma_d * sum_i |x_i w_i| (+ one rounding of the logit
+    offset): the worst-case bound of an fp32 dot product of length d, any
+    summation order; plus a relative L2 check at 5x the random-walk scale
+    sqrt(d) * 2^-24."""
+    d = x.shape[1]
+    u = 2.0 ** -24
+    gamma = d * u / (1 - d * u)
+    ref = oracle.router_logits(x, wr, logit_add)
+    absdot = np.abs(x) @ np.abs(wr).T
+    bound = gamma * absdot + 2 * u * np.abs(ref) + 1e-30
+    err = np.abs(logits_gpu.astype(np.float64) - ref)
+    assert (err <= bound).all(), float((err / bound).max())
+    assert rel_l2(logits_gpu, ref) <= 5 * np.sqrt(d) * u
+    return ref
