@@ -141,8 +141,8 @@ size_t moe_workspace_bytes(const moe_shape* shape);
  * logits: train-time jitter, logit offsets); bias [N] or NULL (selection
  * only).  scores_in [T,N] fp32 or NULL: when given, the GEMM and score
  * function are skipped and these scores are selected on (x and w_router
- * may then be NULL).  Outputs: logits_out [T,N] (NULL: not written; ignored
- * with scores_in), scores_out [T,N] (NULL: not written), topk_idx [T,k],
+ * may then be NULL).  Outputs: logits_out [T,N] = x W_r^T, the affinity
+ * GEMM before logit_add (NULL: not written; ignored with scores_in), scores_out [T,N] (NULL: not written), topk_idx [T,k],
  * topk_w [T,k] (required). */
 moe_status moe_route(const moe_shape* shape, const void* x,
                      const float* w_router, const float* logit_add,

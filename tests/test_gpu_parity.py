@@ -73,9 +73,8 @@ def test_steps_compose_to_forward_and_expert_rows(name):
     for key in ["scores", "topk_idx", "topk_w", "counts", "offsets", "slot", "n_kept_dropped",
                 "y"]:
         assert torch.equal(st[key], fw[key]), key
-    # router GEMM
-    la = None if inp.logit_add is None else host(inp.logit_add)
-    router_tolerance_ok(host(inp.x), host(inp.w_router), la, host(st["logits"]))
+    # router GEMM (logits_out is the affinity x W_r^T, before logit_add)
+    router_tolerance_ok(host(inp.x), host(inp.w_router), None, host(st["logits"]))
     ref = oracle_layer(inp, st["scores"], compute_outputs=False)
     check_routing_and_dispatch(st, ref, T, cfg.top_k)
     kept = ref["kept"]
