@@ -24,7 +24,6 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
 // work-list construction
@@ -51,13 +50,15 @@ __device__ __forceinline__ void block_exclusive_scan2(int* sh0, int* sh1, int v0
 }
 
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int N,
-                                                    int T, int has_shared, int bm, int nt1_r,
+                                                    int T, int has_shared, int bm1, int bm2,
+                                                    int nt1_r,
                                                     int nt1_s, int nt2_r, int nt2_s,
                                                     WorkItem* __restrict__ plan1,
                                                     int32_t* __restrict__ count1,
                                                     WorkItem* __restrict__ plan2,
                                                     int32_t* __restrict__ count2) {
   __shared__ int sh0[1024], sh1[1024];
+  __shared__ int st1s[1025], st2s[1025], mt1s[1024], mt2s[1024], rbases[1024], rowss[1024];
   const int s = threadIdx.x;
   const int S = N + has_shared;
   int rows = 0, rbase = 0, n1t = 0, n2t = 0;
@@ -71,18 +72,40 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     n1t = nt1_s;
     n2t = nt2_s;
   }
-  const int mt = (rows + bm - 1) / bm;
+  const int mt1 = (rows + bm1 - 1) / bm1, mt2 = (rows + bm2 - 1) / bm2;
   int st1, st2, tot1, tot2;
-  block_exclusive_scan2(sh0, sh1, mt * n1t, mt * n2t, st1, st2, tot1, tot2);
-  for (int nt = 0; nt < n1t; ++nt)
-    for (int m = 0; m < mt; ++m)
-      plan1[st1 + nt * mt + m] = WorkItem{s, rbase + m * bm, min(bm, rows - m * bm), nt};
-  for (int nt = 0; nt < n2t; ++nt)
-    for (int m = 0; m < mt; ++m)
-      plan2[st2 + nt * mt + m] = WorkItem{s, rbase + m * bm, min(bm, rows - m * bm), nt};
+  block_exclusive_scan2(sh0, sh1, mt1 * n1t, mt2 * n2t, st1, st2, tot1, tot2);
+  st1s[s] = st1;
+  st2s[s] = st2;
+  mt1s[s] = mt1;
+  mt2s[s] = mt2;
+  rbases[s] = rbase;
+  rowss[s] = rows;
   if (s == 0) {
+    st1s[1024] = tot1;
+    st2s[1024] = tot2;
     *count1 = tot1;
     *count2 = tot2;
+  }
+  __syncthreads();
+  // items in segment-major, then column tile, then row block order; every
+  // thread fills a strided share, locating the segment by binary search
+  for (int pass = 0; pass < 2; ++pass) {
+    const int* st = pass ? st2s : st1s;
+    const int* mts = pass ? mt2s : mt1s;
+    const int bm = pass ? bm2 : bm1;
+    WorkItem* plan = pass ? plan2 : plan1;
+    const int tot = pass ? tot2 : tot1;
+    for (int i = s; i < tot; i += blockDim.x) {
+      int lo = 0, hi = 1023;  // last segment with st[seg] <= i (empty ones skipped)
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (st[mid] <= i) lo = mid;
+        else hi = mid - 1;
+      }
+      const int seg = lo, loc = i - st[seg], m = loc % mts[seg], nt = loc / mts[seg];
+      plan[i] = WorkItem{seg, rbases[seg] + m * bm, min(bm, rowss[seg] - m * bm), nt};
+    }
   }
 }
 
@@ -116,160 +139,257 @@ struct GemmArgs {
 };
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA grouped GEMM.  Block tile 128 rows x 256 weight rows x 64 k,
-// 4 waves in 2x2, each wave 64 rows x 4 column tiles of 32 (GATED: 2 gate +
-// 2 up tiles covering the same 64 h columns).
+// bf16 MFMA grouped GEMM.
+//
+// Block tile: up to BM rows (assignments) x BNW weight rows, k-slices of BK.
+// RG x CG waves: wave (rg, cg) owns the weight rows of column group cg
+// (GATED: gate rows 32cg..32cg+31 and the matching up rows, i.e. 32 h columns,
+// so SwiGLU is applied in registers; plain: 64 output columns) and the 32-row
+// MFMA sub-tiles i with i % RG == rg.  An item with few rows costs MFMA work
+// in proportion to ceil(rows/32), not to the full tile.
+//
+// Operands move global -> LDS with the direct DMA load (global_load_lds, 16
+// bytes per lane, one 1 KiB block of rows per wave instruction) into rings of
+// SA (rows) and SB (weights) buffers, so SA-1 / SB-1 k-slices are in flight
+// while the MFMAs consume one.  Each wave waits only on its own loads (vmcnt); one s_barrier per slice
+// publishes the slice to all waves and retires the buffer that the next DMA
+// overwrites.  Inside an LDS row the 16-byte chunk c of row r sits at position
+// c ^ swz(r), swz(r) = (r / rows-per-256-bytes) % chunks-per-row: the 32 rows
+// of an MFMA fragment read then hit 64 distinct banks per 16 lanes.  The DMA
+// lane -> LDS position map is fixed, so each lane fetches the chunk that
+// belongs at its position.
 // ---------------------------------------------------------------------------
-constexpr int G_BM = 128, G_BNW = 256, G_BK = 64;
+template <int RG_, int CG_, int BK_, int SA_, int SB_>
+struct GCfg {
+  static constexpr int RG = RG_, CG = CG_, BK = BK_;
+  static constexpr int SA = SA_, SB = SB_;      // LDS ring depth of A and of B
+  static constexpr int WAVES = RG * CG, THREADS = WAVES * 64;
+  static constexpr int MSW = 4;               // max 32-row sub-tiles per wave
+  static constexpr int BM = RG * MSW * 32;    // rows per work item
+  static constexpr int BNW = CG * 64;         // weight rows per work item
+  static constexpr int ROWB = BK * 2;         // bytes per LDS row
+  static constexpr int CPR = BK / 8;          // 16-byte chunks per row
+  static constexpr int RP = 256 / ROWB;       // rows per 256-byte bank line
+  static constexpr int DROWS = 1024 / ROWB;   // rows per wave DMA instruction
+  static constexpr int A_BYTES = BM * ROWB, B_BYTES = BNW * ROWB;
+  static constexpr int A_LOADS = A_BYTES / 1024 / WAVES, B_LOADS = B_BYTES / 1024 / WAVES;
+  static constexpr int LDS_BYTES = SA * A_BYTES + SB * B_BYTES;
+  static_assert(A_LOADS * 1024 * WAVES == A_BYTES && B_LOADS * 1024 * WAVES == B_BYTES, "");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  static_assert(SB >= SA && SA >= 2 && SB <= SA + 1, "B runs at most one slice ahead of A");
+  __device__ static __forceinline__ int swz(int r) { return (r / RP) % CPR; }
+};
 
-__device__ __forceinline__ void gload_tile(u32x4_t (&ra)[4], u32x4_t (&rb)[8],
-                                           const bf16_t* __restrict__ A,
-                                           const bf16_t* __restrict__ B,
-                                           const uint32_t (&a_off)[4],
-                                           const uint32_t (&b_off)[8], int k0) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(A + a_off[i] + k0);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) rb[i] = *reinterpret_cast<const u32x4_t*>(B + b_off[i] + k0);
+#ifndef MOE_GEMM1_CFG
+#define MOE_GEMM1_CFG 2, 4, 64, 2, 2
+#endif
+#ifndef MOE_GEMM2_CFG
+#define MOE_GEMM2_CFG 2, 4, 64, 2, 2
+#endif
+using Cfg1 = GCfg<MOE_GEMM1_CFG>;
+using Cfg2 = GCfg<MOE_GEMM2_CFG>;
+
+typedef __attribute__((address_space(1))) void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+__device__ __forceinline__ void dma16(const bf16_t* src, unsigned char* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((gptr_t)(src), (lptr_t)(lds_wave_base), 16, 0, 0);
 }
 
-// one BK slice of the block tile: 4 k-steps of 16, 2 x 4 MFMA 32x32x16 per wave
-__device__ __forceinline__ void mma_tile(f32x16_t (&acc)[2][4], const unsigned char* As,
-                                         const unsigned char* Bs, const int (&a_row)[2],
-                                         const int (&b_row)[4], int fh) {
-#pragma unroll
-  for (int ks = 0; ks < G_BK / 16; ++ks) {
-    const int ch = 2 * ks + fh;
-    bf16x8_t af[2], bf[4];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      af[i] = *reinterpret_cast<const bf16x8_t*>(As + a_row[i] * (G_BK * 2) +
-                                                 ((ch ^ (a_row[i] & 7)) << 4));
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      bf[j] = *reinterpret_cast<const bf16x8_t*>(Bs + b_row[j] * (G_BK * 2) +
-                                                 ((ch ^ (b_row[j] & 7)) << 4));
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
-  }
+// wait until at most n vector-memory ops of this wave are outstanding
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-__device__ __forceinline__ void lstore_tile(const u32x4_t (&ra)[4], const u32x4_t (&rb)[8],
-                                            unsigned char* As, unsigned char* Bs, int lds_off) {
+// MFMA operand fragments of k-step ks (16 k) from one LDS stage: this wave's
+// A sub-tiles (rows a_row[j]) and weight rows b_row[0..1]; 16-byte chunk
+// 2ks + lane/32 of each row
+template <class C, int MS>
+__device__ __forceinline__ void load_frags(const unsigned char* As, const unsigned char* Bs,
+                                           const int (&a_row)[MS], const int (&b_row)[2],
+                                           int fh, int ks, bf16x8_t (&af)[MS],
+                                           bf16x8_t (&bf)[2]) {
+  const int ch = 2 * ks + fh;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    *reinterpret_cast<u32x4_t*>(As + lds_off + i * 32 * G_BK * 2) = ra[i];
+  for (int j = 0; j < 2; ++j)
+    bf[j] = *reinterpret_cast<const bf16x8_t*>(Bs + b_row[j] * C::ROWB +
+                                               ((ch ^ C::swz(b_row[j])) << 4));
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    *reinterpret_cast<u32x4_t*>(Bs + lds_off + i * 32 * G_BK * 2) = rb[i];
+  for (int i = 0; i < MS; ++i)
+    af[i] = *reinterpret_cast<const bf16x8_t*>(As + a_row[i] * C::ROWB +
+                                               ((ch ^ C::swz(a_row[i])) << 4));
 }
 
-template <bool GATED>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[(G_BM + G_BNW) * G_BK * 2];
-  unsigned char* As = lds;
-  unsigned char* Bs = lds + G_BM * G_BK * 2;
-
-  const int item_id = xcd_item(*g.count);
-  if (item_id < 0) return;
-  const WorkItem it = g.items[item_id];
+// main loop + epilogue for items whose waves hold MS row sub-tiles (the last
+// one only if `last` is set for this wave)
+template <bool GATED, class C, int MS>
+__device__ __forceinline__ void gemm_bf16_body(const GemmArgs& g, const WorkItem& it,
+                                               unsigned char* lds, int msub) {
   const bool shared = it.seg == g.N;
   const int K = shared ? g.K_s : g.K_r;
   const int Nout = shared ? g.Nout_s : g.Nout_r;
   const bf16_t* A = shared ? g.a_shared : g.a_routed;
   const bf16_t* B = shared ? g.b_shared : g.b_routed + (long long)it.seg * g.b_stride;
   bf16_t* Cm = shared ? g.c_shared : g.c_routed;
-  const int n0 = it.nt * (GATED ? G_BNW / 2 : G_BNW);
+  const int n0 = it.nt * (GATED ? C::BNW / 2 : C::BNW);
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int rg = w / C::CG, cg = w % C::CG;
+  // this wave's last row sub-tile is live iff (MS-1)*RG + rg < msub
+  const bool last = (MS - 1) * C::RG + rg < msub;
 
-  // loader geometry: rows (tid>>3) + 32 i, 16-byte chunk tid&7
-  const int lrow = tid >> 3, lcc = tid & 7;
-  const int lds_off = lrow * (G_BK * 2) + ((lcc ^ (lrow & 7)) << 4);
-  uint32_t a_off[4], b_off[8];
+  // DMA geometry: wave load q covers tile rows DROWS*q .. +DROWS-1; lane ->
+  // tile row DROWS*q + lane/CPR at LDS position lane%CPR, so it fetches global
+  // chunk (lane%CPR) ^ swz(row)
+  const int drow = lane / C::CPR, dpos = lane % C::CPR;
+  uint32_t a_off[C::A_LOADS], b_off[C::B_LOADS];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int r = min(lrow + 32 * i, it.nrows - 1);
+  for (int j = 0; j < C::A_LOADS; ++j) {
+    const int tr = (w * C::A_LOADS + j) * C::DROWS + drow;
+    const int r = min(tr, it.nrows - 1);
     int src = it.row0 + r;
     if (g.perm && !shared) src = g.perm[src] / g.k;
-    a_off[i] = (uint32_t)src * (uint32_t)K + lcc * 8;
+    a_off[j] = (uint32_t)src * (uint32_t)K + (dpos ^ C::swz(tr)) * 8;
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int r = lrow + 32 * i;
+  for (int j = 0; j < C::B_LOADS; ++j) {
+    const int r = (w * C::B_LOADS + j) * C::DROWS + drow;
     int wrow;
-    if (GATED) {
-      wrow = r < G_BNW / 2 ? min(n0 + r, Nout - 1) : Nout + min(n0 + r - G_BNW / 2, Nout - 1);
-    } else {
+    if (GATED)
+      wrow = r < C::BNW / 2 ? min(n0 + r, Nout - 1) : Nout + min(n0 + r - C::BNW / 2, Nout - 1);
+    else
       wrow = min(n0 + r, Nout - 1);
-    }
-    b_off[i] = (uint32_t)wrow * (uint32_t)K + lcc * 8;
+    b_off[j] = (uint32_t)wrow * (uint32_t)K + (dpos ^ C::swz(r)) * 8;
   }
 
-  f32x16_t acc[2][4];
+  // LDS: SA buffers of the A slice, then SB buffers of the B slice.  B (the
+  // weight stream) is fetched SB-1 slices ahead, A (rows shared through L2)
+  // SA-1 slices ahead.
+  unsigned char* const Abuf = lds;
+  unsigned char* const Bbuf = lds + C::SA * C::A_BYTES;
+  const int nk = K / C::BK;
+  auto issue_a = [&](int kt) {
+    unsigned char* st = Abuf + (kt % C::SA) * C::A_BYTES;
+    const int k0 = kt * C::BK;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < C::A_LOADS; ++j)
+      dma16(A + a_off[j] + k0, st + (w * C::A_LOADS + j) * 1024);
+  };
+  auto issue_b = [&](int kt) {
+    unsigned char* st = Bbuf + (kt % C::SB) * C::B_BYTES;
+    const int k0 = kt * C::BK;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < C::B_LOADS; ++j)
+      dma16(B + b_off[j] + k0, st + (w * C::B_LOADS + j) * 1024);
+  };
+
+  f32x16_t acc[MS][2];
+#pragma unroll
+  for (int i = 0; i < MS; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  u32x4_t ra[4], rb[8];
-  // fragment geometry: row (lane & 31) of a 32-row tile, chunk 2*ks + (lane >> 5)
   const int fr = lane & 31, fh = lane >> 5;
-  int a_row[2], b_row[4];
+  int a_row[MS], b_row[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) a_row[i] = wm * 64 + i * 32 + fr;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (GATED)
-      b_row[j] = (j < 2 ? wn * 64 + j * 32 : G_BNW / 2 + wn * 64 + (j - 2) * 32) + fr;
-    else
-      b_row[j] = wn * 128 + j * 32 + fr;
+  for (int i = 0; i < MS; ++i) a_row[i] = (i * C::RG + rg) * 32 + fr;
+  if (GATED) {
+    b_row[0] = cg * 32 + fr;
+    b_row[1] = C::BNW / 2 + cg * 32 + fr;
+  } else {
+    b_row[0] = cg * 64 + fr;
+    b_row[1] = cg * 64 + 32 + fr;
   }
 
-  const int nk = K / G_BK;
-  gload_tile(ra, rb, A, B, a_off, b_off, 0);
-  lstore_tile(ra, rb, As, Bs, lds_off);
-  __syncthreads();
-  for (int kt = 1; kt < nk; ++kt) {
-    gload_tile(ra, rb, A, B, a_off, b_off, kt * G_BK);  // in flight during the MFMAs
-    mma_tile(acc, As, Bs, a_row, b_row, fh);
-    __syncthreads();
-    lstore_tile(ra, rb, As, Bs, lds_off);
-    __syncthreads();
+  // Issue order: iteration j issues A(j+SA-1), then B(j+SB-1); the prologue
+  // plays iterations -(SB-1) .. -1.  Vector-memory loads retire in order, so
+  // at iteration kt the loads of slice kt are complete once no more than the
+  // younger ones are outstanding: B(kt+1) .. B(kt+SB-2) and A(kt+1) ..
+  // A(kt+SA-2) when B leads by one slice, A/B(kt+1 .. kt+SA-2) otherwise.
+  constexpr int LEAD = C::SB - C::SA;
+  constexpr int YOUNGER = (C::SA - 2) * (C::A_LOADS + C::B_LOADS) + LEAD * C::B_LOADS;
+#pragma unroll
+  for (int j = -(C::SB - 1); j < 0; ++j) {
+    if (j + C::SA - 1 >= 0 && j + C::SA - 1 < nk) issue_a(j + C::SA - 1);
+    if (j + C::SB - 1 < nk) issue_b(j + C::SB - 1);
   }
-  mma_tile(acc, As, Bs, a_row, b_row, fh);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + C::SB - 2 < nk) wait_vm<YOUNGER>();
+    else wait_vm<0>();
+    // every wave's part of slice kt is now in LDS, and every wave is done
+    // with slice kt-1, whose buffers the next loads overwrite
+    __builtin_amdgcn_s_barrier();
+    if (kt + C::SA - 1 < nk) issue_a(kt + C::SA - 1);
+    if (kt + C::SB - 1 < nk) issue_b(kt + C::SB - 1);
+    const unsigned char* As = Abuf + (kt % C::SA) * C::A_BYTES;
+    const unsigned char* Bs = Bbuf + (kt % C::SB) * C::B_BYTES;
+    // fragments of k-step ks+1 are read while the MFMAs of k-step ks run
+    bf16x8_t bf[2][2], af[2][MS];
+    load_frags<C, MS>(As, Bs, a_row, b_row, fh, 0, af[0], bf[0]);
+#pragma unroll
+    for (int ks = 0; ks < C::BK / 16; ++ks) {
+      const int cur = ks & 1;
+      if (ks + 1 < C::BK / 16)
+        load_frags<C, MS>(As, Bs, a_row, b_row, fh, ks + 1, af[cur ^ 1], bf[cur ^ 1]);
+#pragma unroll
+      for (int i = 0; i < MS - 1; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bf[cur][j], acc[i][j],
+                                                              0, 0, 0);
+      if (last) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[MS - 1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              af[cur][MS - 1], bf[cur][j], acc[MS - 1][j], 0, 0, 0);
+      }
+    }
+  }
 
   // epilogue.  32x32 accumulator layout: column = lane & 31,
   // row = 8*(r/4) + 4*(lane/32) + r%4 for register r.
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < MS; ++i) {
+    if (i == MS - 1 && !last) continue;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * fh + (r & 3);
+      const int row = (i * C::RG + rg) * 32 + 8 * (r >> 2) + 4 * fh + (r & 3);
       if (row >= it.nrows) continue;
       bf16_t* crow = Cm + (size_t)(it.row0 + row) * Nout;
       if (GATED) {
-#pragma unroll
-        for (int jn = 0; jn < 2; ++jn) {
-          const int col = n0 + wn * 64 + jn * 32 + fr;
-          const float gv = acc[i][jn][r], uv = acc[i][jn + 2][r];
-          const float hv = gv / (1.0f + expf(-gv)) * uv;
-          if (col < Nout) crow[col] = f32_to_bf16(hv);
-        }
+        const int col = n0 + cg * 32 + fr;
+        const float gv = acc[i][0][r], uv = acc[i][1][r];
+        const float hv = gv / (1.0f + expf(-gv)) * uv;
+        if (col < Nout) crow[col] = f32_to_bf16(hv);
       } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = n0 + wn * 128 + j * 32 + fr;
+        for (int j = 0; j < 2; ++j) {
+          const int col = n0 + cg * 64 + j * 32 + fr;
           if (col < Nout) crow[col] = f32_to_bf16(acc[i][j][r]);
         }
       }
     }
+  }
+}
+
+template <bool GATED, class C>
+__global__ __launch_bounds__(C::THREADS) void gemm_bf16_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[C::LDS_BYTES];
+  const int item_id = xcd_item(*g.count);
+  if (item_id < 0) return;
+  const WorkItem it = g.items[item_id];
+  const int msub = (it.nrows + 31) >> 5;  // live 32-row sub-tiles, block-uniform
+  switch ((msub + C::RG - 1) / C::RG) {   // sub-tiles of the busiest wave
+    case 1: gemm_bf16_body<GATED, C, 1>(g, it, lds, msub); break;
+    case 2: gemm_bf16_body<GATED, C, 2>(g, it, lds, msub); break;
+    case 3: gemm_bf16_body<GATED, C, 3>(g, it, lds, msub); break;
+    default: gemm_bf16_body<GATED, C, 4>(g, it, lds, msub); break;
   }
 }
 
@@ -352,6 +472,20 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgsF g) {
 
 inline int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 
+struct PlanGeom {
+  int bm1, bm2, nt1_r, nt1_s, nt2_r, nt2_s;
+};
+
+// row-block size and column-tile counts of the two work lists
+PlanGeom plan_geom(const moe_shape& s) {
+  const bool bf = s.dtype == MOE_DTYPE_BF16;
+  const int bm1 = bf ? Cfg1::BM : kBMf, bm2 = bf ? Cfg2::BM : kBMf;
+  const int bn1 = bf ? Cfg1::BNW / 2 : kBNf, bn2 = bf ? Cfg2::BNW : kBNf;
+  const bool sh = s.d_ff_shared > 0;
+  return PlanGeom{bm1, bm2, cdiv(s.d_ff, bn1), sh ? cdiv(s.d_ff_shared, bn1) : 0,
+                  cdiv(s.d_model, bn2), sh ? cdiv(s.d_model, bn2) : 0};
+}
+
 }  // namespace
 
 hipError_t launch_expert_ffn(const moe_shape& s, const void* x, const int32_t* perm,
@@ -361,25 +495,23 @@ hipError_t launch_expert_ffn(const moe_shape& s, const void* x, const int32_t* p
   const int T = (int)s.T, N = s.n_experts, d = s.d_model, f = s.d_ff, fs = s.d_ff_shared;
   const bool bf = s.dtype == MOE_DTYPE_BF16;
   const int has_shared = fs > 0 ? 1 : 0;
-  const int bm = bf ? G_BM : kBMf;
-  const int bn1 = bf ? G_BNW / 2 : kBNf, bn2 = bf ? G_BNW : kBNf;
-  const int nt1_r = cdiv(f, bn1), nt1_s = has_shared ? cdiv(fs, bn1) : 0;
-  const int nt2_r = cdiv(d, bn2), nt2_s = has_shared ? cdiv(d, bn2) : 0;
-  plan_kernel<<<1, 1024, 0, st>>>(offsets, N, T, has_shared, bm, nt1_r, nt1_s, nt2_r, nt2_s,
-                                  w.plan1, w.plan1_count, w.plan2, w.plan2_count);
+  PlanGeom pg = plan_geom(s);
+  plan_kernel<<<1, 1024, 0, st>>>(offsets, N, T, has_shared, pg.bm1, pg.bm2, pg.nt1_r,
+                                  pg.nt1_s, pg.nt2_r, pg.nt2_s, w.plan1, w.plan1_count, w.plan2,
+                                  w.plan2_count);
   const int grid1 = (int)((w.plan1_cap + 7) / 8 * 8), grid2 = (int)((w.plan2_cap + 7) / 8 * 8);
   if (bf) {
     GemmArgs g1{static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(x), perm, s.top_k,
                 static_cast<const bf16_t*>(w1), static_cast<const bf16_t*>(w1s),
                 static_cast<bf16_t*>(w.h), static_cast<bf16_t*>(w.h_shared), d, d, f, fs,
                 (long long)2 * f * d, N, w.plan1, w.plan1_count};
-    gemm_bf16_kernel<true><<<grid1, 256, 0, st>>>(g1);
+    gemm_bf16_kernel<true, Cfg1><<<grid1, Cfg1::THREADS, 0, st>>>(g1);
     GemmArgs g2{static_cast<const bf16_t*>(w.h), static_cast<const bf16_t*>(w.h_shared),
                 nullptr, s.top_k, static_cast<const bf16_t*>(w2),
                 static_cast<const bf16_t*>(w2s), static_cast<bf16_t*>(y_perm),
                 static_cast<bf16_t*>(y_shared), f, fs, d, d, (long long)d * f, N, w.plan2,
                 w.plan2_count};
-    gemm_bf16_kernel<false><<<grid2, 256, 0, st>>>(g2);
+    gemm_bf16_kernel<false, Cfg2><<<grid2, Cfg2::THREADS, 0, st>>>(g2);
   } else {
     GemmArgsF g1{static_cast<const float*>(x), static_cast<const float*>(x), perm, s.top_k,
                  static_cast<const float*>(w1), static_cast<const float*>(w1s),
@@ -398,15 +530,14 @@ hipError_t launch_expert_ffn(const moe_shape& s, const void* x, const int32_t* p
 
 // work-list capacities for a shape (upper bounds of the plan sizes)
 void plan_caps(const moe_shape& s, int64_t& cap1, int64_t& cap2) {
-  const bool bf = s.dtype == MOE_DTYPE_BF16;
+  const PlanGeom pg = plan_geom(s);
   const int64_t A = s.T * s.top_k;
-  const int bm = bf ? G_BM : kBMf;
-  const int bn1 = bf ? G_BNW / 2 : kBNf, bn2 = bf ? G_BNW : kBNf;
-  const int64_t mt_r = (A + bm - 1) / bm + s.n_experts;
-  const int64_t mt_s = s.d_ff_shared > 0 ? (s.T + bm - 1) / bm : 0;
-  cap1 = mt_r * ((s.d_ff + bn1 - 1) / bn1) +
-         mt_s * (s.d_ff_shared > 0 ? (s.d_ff_shared + bn1 - 1) / bn1 : 0);
-  cap2 = mt_r * ((s.d_model + bn2 - 1) / bn2) + mt_s * ((s.d_model + bn2 - 1) / bn2);
+  const int64_t mt1 = (A + pg.bm1 - 1) / pg.bm1 + s.n_experts;
+  const int64_t mt2 = (A + pg.bm2 - 1) / pg.bm2 + s.n_experts;
+  const int64_t ms1 = s.d_ff_shared > 0 ? (s.T + pg.bm1 - 1) / pg.bm1 : 0;
+  const int64_t ms2 = s.d_ff_shared > 0 ? (s.T + pg.bm2 - 1) / pg.bm2 : 0;
+  cap1 = mt1 * pg.nt1_r + ms1 * pg.nt1_s;
+  cap2 = mt2 * pg.nt2_r + ms2 * pg.nt2_s;
 }
 
 }  // namespace moe
