@@ -49,14 +49,24 @@ __device__ __forceinline__ void block_exclusive_scan2(int* sh0, int* sh1, int v0
   tot1 = sh1[n - 1];
 }
 
+// Cost of an item for the XCD split: (live 32-row sub-tiles + a fixed part for
+// the weight slice every item streams) x k-slices.
+#ifndef MOE_COST_FIXED
+#define MOE_COST_FIXED 8
+#endif
+
+// Work-list header (int32): [0] item count, [1..9] XCD range starts
+// (xcd x owns items [hdr[1+x], hdr[2+x])), [16..23] per-XCD item counters.
+constexpr int kHdrStart = 1, kHdrCtr = 16;  // header: 32 ints
+
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int N,
                                                     int T, int has_shared, int bm1, int bm2,
-                                                    int nt1_r,
-                                                    int nt1_s, int nt2_r, int nt2_s,
+                                                    int nt1_r, int nt1_s, int nt2_r, int nt2_s,
+                                                    int k1_r, int k1_s, int k2_r, int k2_s,
                                                     WorkItem* __restrict__ plan1,
-                                                    int32_t* __restrict__ count1,
+                                                    int32_t* __restrict__ hdr1,
                                                     WorkItem* __restrict__ plan2,
-                                                    int32_t* __restrict__ count2) {
+                                                    int32_t* __restrict__ hdr2) {
   __shared__ int sh0[1024], sh1[1024];
   __shared__ int st1s[1025], st2s[1025], mt1s[1024], mt2s[1024], rbases[1024], rowss[1024];
   const int s = threadIdx.x;
@@ -84,19 +94,22 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   if (s == 0) {
     st1s[1024] = tot1;
     st2s[1024] = tot2;
-    *count1 = tot1;
-    *count2 = tot2;
   }
   __syncthreads();
-  // items in segment-major, then column tile, then row block order; every
-  // thread fills a strided share, locating the segment by binary search
+  // Items in segment-major, then column tile, then row block order.  Thread s
+  // fills a contiguous chunk; an item's cost is its 32-row sub-tiles times its
+  // k-slices.  The list is then cut into 8 ranges of equal cost, one per XCD.
   for (int pass = 0; pass < 2; ++pass) {
     const int* st = pass ? st2s : st1s;
     const int* mts = pass ? mt2s : mt1s;
     const int bm = pass ? bm2 : bm1;
+    const int kr = (pass ? k2_r : k1_r) / 64, ks = (pass ? k2_s : k1_s) / 64;
     WorkItem* plan = pass ? plan2 : plan1;
+    int32_t* hdr = pass ? hdr2 : hdr1;
     const int tot = pass ? tot2 : tot1;
-    for (int i = s; i < tot; i += blockDim.x) {
+    const int chunk = (tot + 1023) / 1024;
+    const int i0 = min(tot, s * chunk), i1 = min(tot, i0 + chunk);
+    auto item_at = [&](int i, int& cost) {
       int lo = 0, hi = 1023;  // last segment with st[seg] <= i (empty ones skipped)
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -104,14 +117,45 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
         else hi = mid - 1;
       }
       const int seg = lo, loc = i - st[seg], m = loc % mts[seg], nt = loc / mts[seg];
-      plan[i] = WorkItem{seg, rbases[seg] + m * bm, min(bm, rowss[seg] - m * bm), nt};
+      const int nr = min(bm, rowss[seg] - m * bm);
+      cost = (((nr + 31) >> 5) + MOE_COST_FIXED) * (seg < N ? kr : ks);
+      return WorkItem{seg, rbases[seg] + m * bm, nr, nt};
+    };
+    int local = 0;
+    for (int i = i0; i < i1; ++i) {
+      int c;
+      plan[i] = item_at(i, c);
+      local += c;
     }
+    int pre, dummy_ex, total, dummy_tot;
+    block_exclusive_scan2(sh0, sh1, local, 0, pre, dummy_ex, total, dummy_tot);
+    // boundary x = first item i with 8 * cost(items < i) >= x * total
+    if (s == 0) {
+      hdr[0] = tot;
+      hdr[kHdrStart] = 0;
+      hdr[kHdrStart + 8] = tot;
+      for (int x = 0; x < 8; ++x) hdr[kHdrCtr + x] = 0;
+      if (total == 0)
+        for (int x = 1; x < 8; ++x) hdr[kHdrStart + x] = 0;
+    }
+    if (total > 0) {
+      long long cum = pre;
+      for (int i = i0; i < i1; ++i) {
+        int c;
+        item_at(i, c);
+        for (int x = 1; x < 8; ++x) {
+          const long long tgt = (long long)x * total;
+          if (8 * cum < tgt && tgt <= 8 * (cum + c)) hdr[kHdrStart + x] = i + 1;
+        }
+        cum += c;
+      }
+    }
+    __syncthreads();
   }
 }
 
-// XCD-aware item index: the hardware deals blocks round-robin over the 8
-// XCDs, so block b runs on XCD b % 8.  Give XCD x the contiguous item range
-// [x*per, (x+1)*per).  Returns -1 for blocks without work.
+// Non-persistent item index (fp32 path): block b runs on XCD b % 8; XCD x takes
+// the contiguous range [x*per, (x+1)*per).  -1 for blocks without work.
 __device__ __forceinline__ int xcd_item(int count) {
   const int per = (count + 7) >> 3;
   const int b = blockIdx.x;
@@ -135,7 +179,7 @@ struct GemmArgs {
   long long b_stride;      // elements per routed expert weight matrix
   int N;
   const WorkItem* items;
-  const int32_t* count;
+  int32_t* hdr;
 };
 
 // ---------------------------------------------------------------------------
@@ -159,14 +203,14 @@ struct GemmArgs {
 // lane -> LDS position map is fixed, so each lane fetches the chunk that
 // belongs at its position.
 // ---------------------------------------------------------------------------
-template <int RG_, int CG_, int BK_, int SA_, int SB_>
+template <int RG_, int CG_, int NTW_, int BK_, int SA_, int SB_>
 struct GCfg {
-  static constexpr int RG = RG_, CG = CG_, BK = BK_;
+  static constexpr int RG = RG_, CG = CG_, NTW = NTW_, BK = BK_;
   static constexpr int SA = SA_, SB = SB_;      // LDS ring depth of A and of B
   static constexpr int WAVES = RG * CG, THREADS = WAVES * 64;
   static constexpr int MSW = 4;               // max 32-row sub-tiles per wave
   static constexpr int BM = RG * MSW * 32;    // rows per work item
-  static constexpr int BNW = CG * 64;         // weight rows per work item
+  static constexpr int BNW = CG * NTW * 32;   // weight rows per work item
   static constexpr int ROWB = BK * 2;         // bytes per LDS row
   static constexpr int CPR = BK / 8;          // 16-byte chunks per row
   static constexpr int RP = 256 / ROWB;       // rows per 256-byte bank line
@@ -181,10 +225,10 @@ struct GCfg {
 };
 
 #ifndef MOE_GEMM1_CFG
-#define MOE_GEMM1_CFG 2, 4, 64, 2, 2
+#define MOE_GEMM1_CFG 2, 4, 2, 64, 2, 2
 #endif
 #ifndef MOE_GEMM2_CFG
-#define MOE_GEMM2_CFG 2, 4, 64, 2, 2
+#define MOE_GEMM2_CFG 2, 4, 2, 64, 2, 2
 #endif
 using Cfg1 = GCfg<MOE_GEMM1_CFG>;
 using Cfg2 = GCfg<MOE_GEMM2_CFG>;
@@ -208,12 +252,12 @@ __device__ __forceinline__ void wait_vm() {
 // 2ks + lane/32 of each row
 template <class C, int MS>
 __device__ __forceinline__ void load_frags(const unsigned char* As, const unsigned char* Bs,
-                                           const int (&a_row)[MS], const int (&b_row)[2],
+                                           const int (&a_row)[MS], const int (&b_row)[C::NTW],
                                            int fh, int ks, bf16x8_t (&af)[MS],
-                                           bf16x8_t (&bf)[2]) {
+                                           bf16x8_t (&bf)[C::NTW]) {
   const int ch = 2 * ks + fh;
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < C::NTW; ++j)
     bf[j] = *reinterpret_cast<const bf16x8_t*>(Bs + b_row[j] * C::ROWB +
                                                ((ch ^ C::swz(b_row[j])) << 4));
 #pragma unroll
@@ -245,10 +289,13 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& g, const WorkItem
   // tile row DROWS*q + lane/CPR at LDS position lane%CPR, so it fetches global
   // chunk (lane%CPR) ^ swz(row)
   const int drow = lane / C::CPR, dpos = lane % C::CPR;
-  uint32_t a_off[C::A_LOADS], b_off[C::B_LOADS];
+  // only the rows of the MS*RG live sub-tiles are fetched
+  constexpr int AL = C::RG * MS * 32 * C::ROWB / 1024 / C::WAVES;
+  static_assert(AL * 1024 * C::WAVES == C::RG * MS * 32 * C::ROWB, "A rows per wave load");
+  uint32_t a_off[AL], b_off[C::B_LOADS];
 #pragma unroll
-  for (int j = 0; j < C::A_LOADS; ++j) {
-    const int tr = (w * C::A_LOADS + j) * C::DROWS + drow;
+  for (int j = 0; j < AL; ++j) {
+    const int tr = (w * AL + j) * C::DROWS + drow;
     const int r = min(tr, it.nrows - 1);
     int src = it.row0 + r;
     if (g.perm && !shared) src = g.perm[src] / g.k;
@@ -275,8 +322,7 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& g, const WorkItem
     unsigned char* st = Abuf + (kt % C::SA) * C::A_BYTES;
     const int k0 = kt * C::BK;
 #pragma unroll
-    for (int j = 0; j < C::A_LOADS; ++j)
-      dma16(A + a_off[j] + k0, st + (w * C::A_LOADS + j) * 1024);
+    for (int j = 0; j < AL; ++j) dma16(A + a_off[j] + k0, st + (w * AL + j) * 1024);
   };
   auto issue_b = [&](int kt) {
     unsigned char* st = Bbuf + (kt % C::SB) * C::B_BYTES;
@@ -286,24 +332,27 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& g, const WorkItem
       dma16(B + b_off[j] + k0, st + (w * C::B_LOADS + j) * 1024);
   };
 
-  f32x16_t acc[MS][2];
+  constexpr int NT = C::NTW, HT = NT / 2;  // weight tiles per wave; GATED: gate tiles
+  f32x16_t acc[MS][NT];
 #pragma unroll
   for (int i = 0; i < MS; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NT; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // GATED: tiles 0..HT-1 are gate rows cg*HT*32 + 32j, tiles HT..NT-1 the
+  // matching up rows (same h columns); plain: NT consecutive tiles
   const int fr = lane & 31, fh = lane >> 5;
-  int a_row[MS], b_row[2];
+  int a_row[MS], b_row[NT];
 #pragma unroll
   for (int i = 0; i < MS; ++i) a_row[i] = (i * C::RG + rg) * 32 + fr;
-  if (GATED) {
-    b_row[0] = cg * 32 + fr;
-    b_row[1] = C::BNW / 2 + cg * 32 + fr;
-  } else {
-    b_row[0] = cg * 64 + fr;
-    b_row[1] = cg * 64 + 32 + fr;
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    if (GATED)
+      b_row[j] = (j < HT ? 0 : C::BNW / 2) + (cg * HT + (j % HT)) * 32 + fr;
+    else
+      b_row[j] = (cg * NT + j) * 32 + fr;
   }
 
   // Issue order: iteration j issues A(j+SA-1), then B(j+SB-1); the prologue
@@ -312,7 +361,7 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& g, const WorkItem
   // younger ones are outstanding: B(kt+1) .. B(kt+SB-2) and A(kt+1) ..
   // A(kt+SA-2) when B leads by one slice, A/B(kt+1 .. kt+SA-2) otherwise.
   constexpr int LEAD = C::SB - C::SA;
-  constexpr int YOUNGER = (C::SA - 2) * (C::A_LOADS + C::B_LOADS) + LEAD * C::B_LOADS;
+  constexpr int YOUNGER = (C::SA - 2) * (AL + C::B_LOADS) + LEAD * C::B_LOADS;
 #pragma unroll
   for (int j = -(C::SB - 1); j < 0; ++j) {
     if (j + C::SA - 1 >= 0 && j + C::SA - 1 < nk) issue_a(j + C::SA - 1);
@@ -330,7 +379,7 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& g, const WorkItem
     const unsigned char* As = Abuf + (kt % C::SA) * C::A_BYTES;
     const unsigned char* Bs = Bbuf + (kt % C::SB) * C::B_BYTES;
     // fragments of k-step ks+1 are read while the MFMAs of k-step ks run
-    bf16x8_t bf[2][2], af[2][MS];
+    bf16x8_t bf[2][NT], af[2][MS];
     load_frags<C, MS>(As, Bs, a_row, b_row, fh, 0, af[0], bf[0]);
 #pragma unroll
     for (int ks = 0; ks < C::BK / 16; ++ks) {
@@ -340,12 +389,12 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& g, const WorkItem
 #pragma unroll
       for (int i = 0; i < MS - 1; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NT; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bf[cur][j], acc[i][j],
                                                               0, 0, 0);
       if (last) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NT; ++j)
           acc[MS - 1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               af[cur][MS - 1], bf[cur][j], acc[MS - 1][j], 0, 0, 0);
       }
@@ -363,14 +412,17 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& g, const WorkItem
       if (row >= it.nrows) continue;
       bf16_t* crow = Cm + (size_t)(it.row0 + row) * Nout;
       if (GATED) {
-        const int col = n0 + cg * 32 + fr;
-        const float gv = acc[i][0][r], uv = acc[i][1][r];
-        const float hv = gv / (1.0f + expf(-gv)) * uv;
-        if (col < Nout) crow[col] = f32_to_bf16(hv);
+#pragma unroll
+        for (int j = 0; j < HT; ++j) {
+          const int col = n0 + (cg * HT + j) * 32 + fr;
+          const float gv = acc[i][j][r], uv = acc[i][j + HT][r];
+          const float hv = gv / (1.0f + expf(-gv)) * uv;
+          if (col < Nout) crow[col] = f32_to_bf16(hv);
+        }
       } else {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = n0 + cg * 64 + j * 32 + fr;
+        for (int j = 0; j < NT; ++j) {
+          const int col = n0 + (cg * NT + j) * 32 + fr;
           if (col < Nout) crow[col] = f32_to_bf16(acc[i][j][r]);
         }
       }
@@ -378,19 +430,232 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& g, const WorkItem
   }
 }
 
+// Work distribution.  Block b runs on XCD b % 8 (the hardware deals blocks
+// round-robin over the XCDs).  Persistent mode: one block per CU takes items
+// of its XCD's equal-cost range from a per-XCD counter.  Otherwise: one block
+// per item, XCD x running the contiguous range [x*per, (x+1)*per) in order.
+// Either way siblings that share a weight slab or a row block run close
+// together on one L2, and an item's result does not depend on which block
+// computes it.
+#ifndef MOE_PERSISTENT
+#define MOE_PERSISTENT 0
+#endif
+
+// Variant main loop: operands go global -> registers -> LDS.  Two register
+// sets hold the two slices in flight (loads are issued two slices ahead), and
+// the LDS double buffer holds the slice being multiplied and the next one.
+// Thread t moves 16-byte chunks t + THREADS*j of the row-major slice (row =
+// chunk / CPR), writing chunk c of row r at LDS position c ^ swz(r).
+template <bool GATED, class C, int MS>
+__device__ __forceinline__ void gemm_bf16_body_rp(const GemmArgs& g, const WorkItem& it,
+                                                  unsigned char* lds, int msub) {
+  const bool shared = it.seg == g.N;
+  const int K = shared ? g.K_s : g.K_r;
+  const int Nout = shared ? g.Nout_s : g.Nout_r;
+  const bf16_t* A = shared ? g.a_shared : g.a_routed;
+  const bf16_t* B = shared ? g.b_shared : g.b_routed + (long long)it.seg * g.b_stride;
+  bf16_t* Cm = shared ? g.c_shared : g.c_routed;
+  const int n0 = it.nt * (GATED ? C::BNW / 2 : C::BNW);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rg = w / C::CG, cg = w % C::CG;
+  const bool last = (MS - 1) * C::RG + rg < msub;
+
+  constexpr int ROWS_A = C::RG * MS * 32;
+  constexpr int RPT = C::THREADS / C::CPR;                 // rows per thread round
+  constexpr int AL = ROWS_A * C::CPR / C::THREADS, BL = C::BNW * C::CPR / C::THREADS;
+  static_assert(AL * C::THREADS == ROWS_A * C::CPR && BL * C::THREADS == C::BNW * C::CPR, "");
+  constexpr int STAGE = C::A_BYTES + C::B_BYTES;
+  static_assert(2 * STAGE <= C::LDS_BYTES, "LDS double buffer");
+  const int trow = tid / C::CPR, tch = tid % C::CPR;
+  uint32_t a_off[AL], b_off[BL];
+#pragma unroll
+  for (int j = 0; j < AL; ++j) {
+    const int tr = trow + RPT * j;
+    int src = it.row0 + min(tr, it.nrows - 1);
+    if (g.perm && !shared) src = g.perm[src] / g.k;
+    a_off[j] = (uint32_t)src * (uint32_t)K + tch * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < BL; ++j) {
+    const int r = trow + RPT * j;
+    int wrow;
+    if (GATED)
+      wrow = r < C::BNW / 2 ? min(n0 + r, Nout - 1) : Nout + min(n0 + r - C::BNW / 2, Nout - 1);
+    else
+      wrow = min(n0 + r, Nout - 1);
+    b_off[j] = (uint32_t)wrow * (uint32_t)K + tch * 8;
+  }
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  u32x4_t ra0[AL], rb0[BL], ra1[AL], rb1[BL];
+  const int nk = K / C::BK;
+#define MOE_RP_LOAD(RA, RB, KT)                                                              \
+  do {                                                                                       \
+    const int k0_ = (KT) * C::BK;                                                            \
+    _Pragma("unroll") for (int j = 0; j < AL; ++j) RA[j] =                                   \
+        *reinterpret_cast<const u32x4_t*>(A + a_off[j] + k0_);                               \
+    _Pragma("unroll") for (int j = 0; j < BL; ++j) RB[j] =                                   \
+        *reinterpret_cast<const u32x4_t*>(B + b_off[j] + k0_);                               \
+  } while (0)
+#define MOE_RP_STORE(RA, RB, BUF)                                                            \
+  do {                                                                                       \
+    unsigned char* st_ = lds + (BUF) * STAGE;                                                \
+    _Pragma("unroll") for (int j = 0; j < AL; ++j) {                                         \
+      const int r_ = trow + RPT * j;                                                         \
+      *reinterpret_cast<u32x4_t*>(st_ + r_ * C::ROWB + ((tch ^ C::swz(r_)) << 4)) = RA[j];   \
+    }                                                                                        \
+    _Pragma("unroll") for (int j = 0; j < BL; ++j) {                                         \
+      const int r_ = trow + RPT * j;                                                         \
+      *reinterpret_cast<u32x4_t*>(st_ + C::A_BYTES + r_ * C::ROWB +                          \
+                                  ((tch ^ C::swz(r_)) << 4)) = RB[j];                        \
+    }                                                                                        \
+  } while (0)
+
+  constexpr int NT = C::NTW, HT = NT / 2;
+  f32x16_t acc[MS][NT];
+#pragma unroll
+  for (int i = 0; i < MS; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  const int fr = lane & 31, fh = lane >> 5;
+  int a_row[MS], b_row[NT];
+#pragma unroll
+  for (int i = 0; i < MS; ++i) a_row[i] = (i * C::RG + rg) * 32 + fr;
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    if (GATED)
+      b_row[j] = (j < HT ? 0 : C::BNW / 2) + (cg * HT + (j % HT)) * 32 + fr;
+    else
+      b_row[j] = (cg * NT + j) * 32 + fr;
+  }
+  auto compute = [&](int buf) {
+    const unsigned char* As = lds + buf * STAGE;
+    const unsigned char* Bs = As + C::A_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < C::BK / 16; ++ks) {
+      bf16x8_t bf[NT], af[MS];
+      load_frags<C, MS>(As, Bs, a_row, b_row, fh, ks, af, bf);
+#pragma unroll
+      for (int i = 0; i < MS - 1; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+      if (last) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          acc[MS - 1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[MS - 1], bf[j],
+                                                                   acc[MS - 1][j], 0, 0, 0);
+      }
+    }
+  };
+  constexpr int LPS = AL + BL;  // loads per slice per thread
+
+  // prologue: slices 0 and 1 in flight, slice 0 into LDS buffer 0
+  MOE_RP_LOAD(ra0, rb0, 0);
+  if (nk > 1) MOE_RP_LOAD(ra1, rb1, 1);
+  if (nk > 1) wait_vm<LPS>();
+  else wait_vm<0>();
+  MOE_RP_STORE(ra0, rb0, 0);
+  if (nk > 2) MOE_RP_LOAD(ra0, rb0, 2);
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
+  __builtin_amdgcn_s_barrier();
+  // iteration kt: multiply slice kt (LDS kt%2); slice kt+1 (registers
+  // (kt+1)%2) goes to LDS (kt+1)%2, whose previous slice kt-1 every wave has
+  // finished; its register set then takes slice kt+3
+  for (int kt = 0; kt < nk; kt += 2) {
+    compute(0);
+    if (kt + 1 < nk) {
+      if (kt + 2 < nk) wait_vm<LPS>();
+      else wait_vm<0>();
+      MOE_RP_STORE(ra1, rb1, 1);
+      if (kt + 3 < nk) MOE_RP_LOAD(ra1, rb1, kt + 3);
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_s_barrier();
+      compute(1);
+      if (kt + 2 < nk) {
+        if (kt + 3 < nk) wait_vm<LPS>();
+        else wait_vm<0>();
+        MOE_RP_STORE(ra0, rb0, 0);
+        if (kt + 4 < nk) MOE_RP_LOAD(ra0, rb0, kt + 4);
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_s_barrier();
+      }
+    }
+  }
+#undef MOE_RP_LOAD
+#undef MOE_RP_STORE
+
+#pragma unroll
+  for (int i = 0; i < MS; ++i) {
+    if (i == MS - 1 && !last) continue;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = (i * C::RG + rg) * 32 + 8 * (r >> 2) + 4 * fh + (r & 3);
+      if (row >= it.nrows) continue;
+      bf16_t* crow = Cm + (size_t)(it.row0 + row) * Nout;
+      if (GATED) {
+#pragma unroll
+        for (int j = 0; j < HT; ++j) {
+          const int col = n0 + (cg * HT + j) * 32 + fr;
+          const float gv = acc[i][j][r], uv = acc[i][j + HT][r];
+          const float hv = gv / (1.0f + expf(-gv)) * uv;
+          if (col < Nout) crow[col] = f32_to_bf16(hv);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          const int col = n0 + (cg * NT + j) * 32 + fr;
+          if (col < Nout) crow[col] = f32_to_bf16(acc[i][j][r]);
+        }
+      }
+    }
+  }
+}
+
+#ifndef MOE_GEMM_RP
+#define MOE_GEMM_RP 0
+#endif
+#if MOE_GEMM_RP
+#define MOE_GEMM_BODY gemm_bf16_body_rp
+#else
+#define MOE_GEMM_BODY gemm_bf16_body
+#endif
+
+template <bool GATED, class C>
+__device__ __forceinline__ void gemm_bf16_item(const GemmArgs& g, int item, unsigned char* lds) {
+  const WorkItem it = g.items[item];
+  const int msub = (it.nrows + 31) >> 5;  // live 32-row sub-tiles
+  switch ((msub + C::RG - 1) / C::RG) {   // sub-tiles of the busiest wave
+    case 1: MOE_GEMM_BODY<GATED, C, 1>(g, it, lds, msub); break;
+    case 2: MOE_GEMM_BODY<GATED, C, 2>(g, it, lds, msub); break;
+    case 3: MOE_GEMM_BODY<GATED, C, 3>(g, it, lds, msub); break;
+    default: MOE_GEMM_BODY<GATED, C, 4>(g, it, lds, msub); break;
+  }
+}
+
 template <bool GATED, class C>
 __global__ __launch_bounds__(C::THREADS) void gemm_bf16_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds[C::LDS_BYTES];
-  const int item_id = xcd_item(*g.count);
-  if (item_id < 0) return;
-  const WorkItem it = g.items[item_id];
-  const int msub = (it.nrows + 31) >> 5;  // live 32-row sub-tiles, block-uniform
-  switch ((msub + C::RG - 1) / C::RG) {   // sub-tiles of the busiest wave
-    case 1: gemm_bf16_body<GATED, C, 1>(g, it, lds, msub); break;
-    case 2: gemm_bf16_body<GATED, C, 2>(g, it, lds, msub); break;
-    case 3: gemm_bf16_body<GATED, C, 3>(g, it, lds, msub); break;
-    default: gemm_bf16_body<GATED, C, 4>(g, it, lds, msub); break;
+#if MOE_PERSISTENT
+  __shared__ int s_item;
+  const int x = blockIdx.x & 7;
+  const int beg = g.hdr[kHdrStart + x], end = g.hdr[kHdrStart + x + 1];
+  for (;;) {
+    if (threadIdx.x == 0) s_item = beg + atomicAdd(&g.hdr[kHdrCtr + x], 1);
+    __syncthreads();  // also: every wave is done with the previous item's LDS
+    const int item = s_item;
+    __syncthreads();
+    if (item >= end) break;
+    gemm_bf16_item<GATED, C>(g, item, lds);
   }
+#else
+  const int item = xcd_item(g.hdr[0]);
+  if (item < 0) return;
+  gemm_bf16_item<GATED, C>(g, item, lds);
+#endif
 }
 
 // ---------------------------------------------------------------------------
@@ -409,7 +674,7 @@ struct GemmArgsF {
   long long b_stride;
   int N;
   const WorkItem* items;
-  const int32_t* count;
+  const int32_t* hdr;
 };
 
 template <bool GATED>
@@ -418,7 +683,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgsF g) {
   __shared__ float As[kBMf][BK + 1];
   __shared__ float Bg[kBNf][BK + 1];
   __shared__ float Bu[kBNf][BK + 1];
-  const int item_id = xcd_item(*g.count);
+  const int item_id = xcd_item(g.hdr[0]);
   if (item_id < 0) return;
   const WorkItem it = g.items[item_id];
   const bool shared = it.seg == g.N;
@@ -472,6 +737,21 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgsF g) {
 
 inline int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 
+// one persistent block per compute unit, a multiple of the 8 XCDs
+int persistent_grid() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    cached[dev] = (cus + 7) / 8 * 8;
+  }
+  return cached[dev];
+}
+
 struct PlanGeom {
   int bm1, bm2, nt1_r, nt1_s, nt2_r, nt2_s;
 };
@@ -497,32 +777,33 @@ hipError_t launch_expert_ffn(const moe_shape& s, const void* x, const int32_t* p
   const int has_shared = fs > 0 ? 1 : 0;
   PlanGeom pg = plan_geom(s);
   plan_kernel<<<1, 1024, 0, st>>>(offsets, N, T, has_shared, pg.bm1, pg.bm2, pg.nt1_r,
-                                  pg.nt1_s, pg.nt2_r, pg.nt2_s, w.plan1, w.plan1_count, w.plan2,
-                                  w.plan2_count);
+                                  pg.nt1_s, pg.nt2_r, pg.nt2_s, d, d, f, fs > 0 ? fs : 64,
+                                  w.plan1, w.plan1_hdr, w.plan2, w.plan2_hdr);
   const int grid1 = (int)((w.plan1_cap + 7) / 8 * 8), grid2 = (int)((w.plan2_cap + 7) / 8 * 8);
+  const int grid_bf = MOE_PERSISTENT ? persistent_grid() : 0;
   if (bf) {
     GemmArgs g1{static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(x), perm, s.top_k,
                 static_cast<const bf16_t*>(w1), static_cast<const bf16_t*>(w1s),
                 static_cast<bf16_t*>(w.h), static_cast<bf16_t*>(w.h_shared), d, d, f, fs,
-                (long long)2 * f * d, N, w.plan1, w.plan1_count};
-    gemm_bf16_kernel<true, Cfg1><<<grid1, Cfg1::THREADS, 0, st>>>(g1);
+                (long long)2 * f * d, N, w.plan1, w.plan1_hdr};
+    gemm_bf16_kernel<true, Cfg1><<<grid_bf ? grid_bf : grid1, Cfg1::THREADS, 0, st>>>(g1);
     GemmArgs g2{static_cast<const bf16_t*>(w.h), static_cast<const bf16_t*>(w.h_shared),
                 nullptr, s.top_k, static_cast<const bf16_t*>(w2),
                 static_cast<const bf16_t*>(w2s), static_cast<bf16_t*>(y_perm),
                 static_cast<bf16_t*>(y_shared), f, fs, d, d, (long long)d * f, N, w.plan2,
-                w.plan2_count};
-    gemm_bf16_kernel<false, Cfg2><<<grid2, Cfg2::THREADS, 0, st>>>(g2);
+                w.plan2_hdr};
+    gemm_bf16_kernel<false, Cfg2><<<grid_bf ? grid_bf : grid2, Cfg2::THREADS, 0, st>>>(g2);
   } else {
     GemmArgsF g1{static_cast<const float*>(x), static_cast<const float*>(x), perm, s.top_k,
                  static_cast<const float*>(w1), static_cast<const float*>(w1s),
                  static_cast<float*>(w.h), static_cast<float*>(w.h_shared), d, d, f, fs,
-                 (long long)2 * f * d, N, w.plan1, w.plan1_count};
+                 (long long)2 * f * d, N, w.plan1, w.plan1_hdr};
     gemm_f32_kernel<true><<<grid1, 256, 0, st>>>(g1);
     GemmArgsF g2{static_cast<const float*>(w.h), static_cast<const float*>(w.h_shared),
                  nullptr, s.top_k, static_cast<const float*>(w2),
                  static_cast<const float*>(w2s), static_cast<float*>(y_perm),
                  static_cast<float*>(y_shared), f, fs, d, d, (long long)d * f, N, w.plan2,
-                 w.plan2_count};
+                 w.plan2_hdr};
     gemm_f32_kernel<false><<<grid2, 256, 0, st>>>(g2);
   }
   return hipGetLastError();

@@ -80,9 +80,9 @@ Workspace layout_workspace(const moe_shape& s, void* ws) {
   w.rank = static_cast<int32_t*>(take(A * 4));
   w.hist = static_cast<int32_t*>(take(nchunks * N * 4));
   w.base = static_cast<int32_t*>(take(nchunks * N * 4));
-  w.plan1_count = static_cast<int32_t*>(take(4));
+  w.plan1_hdr = static_cast<int32_t*>(take(32 * 4));
   w.plan1 = static_cast<WorkItem*>(take((size_t)w.plan1_cap * sizeof(WorkItem)));
-  w.plan2_count = static_cast<int32_t*>(take(4));
+  w.plan2_hdr = static_cast<int32_t*>(take(32 * 4));
   w.plan2 = static_cast<WorkItem*>(take((size_t)w.plan2_cap * sizeof(WorkItem)));
   w.h = take(A * (size_t)s.d_ff * es);
   w.h_shared = take(T * (size_t)s.d_ff_shared * es);

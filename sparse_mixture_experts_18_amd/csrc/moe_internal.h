@@ -52,9 +52,9 @@ struct Workspace {
   int32_t* rank;
   int32_t* hist;
   int32_t* base;
-  int32_t* plan1_count;
+  int32_t* plan1_hdr;
   WorkItem* plan1;
-  int32_t* plan2_count;
+  int32_t* plan2_hdr;
   WorkItem* plan2;
   void* h;         // routed h [T*k, d_ff], then shared h [T, d_ff_shared]
   void* h_shared;
