@@ -89,6 +89,7 @@ Workspace layout_workspace(const moe_shape& s, void* ws) {
   w.y_perm = take(A * d * es);
   w.y_shared = take(T * d * es);
   w.pmean = static_cast<double*>(take(N * 8));
+  w.wsplit = static_cast<bf16_t*>(take(s.dtype == MOE_DTYPE_BF16 ? 3 * N * d * 2 : 0));
   w.total = off;
   return w;
 }
@@ -148,7 +149,7 @@ moe_status moe_route(const moe_shape* shape, const void* x, const float* w_route
     return hip_status(
         launch_topk(*shape, scores_in, nullptr, true, bias, scores_out, topk_idx, topk_w, s));
   float* logits = logits_out ? logits_out : w.logits;
-  hipError_t e = launch_router_gemm(*shape, x, w_router, logits, s);
+  hipError_t e = launch_router_gemm(*shape, x, w_router, logits, w, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   return hip_status(
       launch_topk(*shape, logits, logit_add, false, bias, scores_out, topk_idx, topk_w, s));
@@ -226,7 +227,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_rou
   int32_t* sl = slot ? slot : w.slot;
   int32_t* nk = n_kept_dropped ? n_kept_dropped : w.nkd;
   const bool shared = sh.d_ff_shared > 0;
-  if (launch_router_gemm(sh, x, w_router, w.logits, s) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_router_gemm(sh, x, w_router, w.logits, w, s) != hipSuccess) return MOE_ERR_HIP;
   if (launch_topk(sh, w.logits, logit_add, false, bias, sc, ti, tw, s) != hipSuccess)
     return MOE_ERR_HIP;
   if (launch_dispatch(sh, ti, cn, of, sl, w.perm, nk, w, s) != hipSuccess) return MOE_ERR_HIP;

@@ -61,6 +61,7 @@ struct Workspace {
   void* y_perm;    // [T*k, d]
   void* y_shared;  // [T, d]
   double* pmean;   // [N] mean score per expert (balancing step)
+  bf16_t* wsplit;  // [3][N][d] bf16 terms of the fp32 router weight (bf16 layers)
   size_t total;
   int64_t plan1_cap, plan2_cap;
 };
@@ -72,7 +73,7 @@ int64_t capacity_of(const moe_shape& s);  // -1 = dropless
 
 // ---- launchers (validated arguments; return hipError_t of the launch) ----
 hipError_t launch_router_gemm(const moe_shape& s, const void* x, const float* w_router,
-                              float* logits, hipStream_t st);
+                              float* logits, const Workspace& w, hipStream_t st);
 hipError_t launch_topk(const moe_shape& s, const float* logits, const float* logit_add,
                        bool logits_are_scores, const float* bias, float* scores_out,
                        int32_t* topk_idx, float* topk_w, hipStream_t st);

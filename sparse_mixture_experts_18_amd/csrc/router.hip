@@ -86,6 +86,106 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const XT* __restrict__
 }
 
 // ---------------------------------------------------------------------------
+// K1, bf16 activations: the same fp32 GEMM on the matrix cores.  x is exactly
+// bf16; W_r (fp32) is split into three bf16 terms w = w1 + w2 + w3 with
+// w1 = bf16(w), w2 = bf16(w - w1), w3 = bf16(w - w1 - w2), which represent w
+// to within 2^-27 |w|.  Every product x*wi is exact in fp32; the three partial
+// GEMMs accumulate in fp32 and are summed smallest first (Henry, Tang &
+// Heinecke 2019, "Leveraging the bfloat16 AI datatype for higher-precision
+// computations").  The k order of every output is fixed, so a token's logits
+// do not depend on the batch.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__global__ __launch_bounds__(256) void split3_kernel(const float* __restrict__ w,
+                                                     bf16_t* __restrict__ ws, long long n) {
+  for (long long i = blockIdx.x * 256LL + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
+    const float v = w[i];
+    const bf16_t h1 = f32_to_bf16(v);
+    const float r1 = v - bf16_to_f32(h1);
+    const bf16_t h2 = f32_to_bf16(r1);
+    const float r2 = r1 - bf16_to_f32(h2);
+    ws[i] = h1;
+    ws[n + i] = h2;
+    ws[2 * n + i] = f32_to_bf16(r2);
+  }
+}
+
+// block: 64 tokens x 64 experts, 4 waves of 32 x 32; k-slices of 64 through
+// LDS (rows of 128 bytes, 16-byte chunk c of row r at c ^ ((r >> 1) & 7))
+constexpr int RM_BM = 64, RM_BN = 64, RM_BK = 64;
+
+__device__ __forceinline__ int rswz(int r) { return (r >> 1) & 7; }
+
+__global__ __launch_bounds__(256) void router_mfma_kernel(const bf16_t* __restrict__ x,
+                                                          const bf16_t* __restrict__ ws,
+                                                          float* __restrict__ logits, int T,
+                                                          int N, int d) {
+  __shared__ __attribute__((aligned(16))) unsigned char As[RM_BM * 128];
+  __shared__ __attribute__((aligned(16))) unsigned char Bs[3][RM_BN * 128];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int m0 = blockIdx.x * RM_BM, n0 = blockIdx.y * RM_BN;
+  const long long plane = (long long)N * d;
+  // loader: 64 rows x 8 chunks = 512 chunks per tile, 2 per thread
+  const int lr = tid >> 3, lc = tid & 7;
+  const bf16_t* ap[2];
+  const bf16_t* bp[2];
+  int lofs[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = lr + 32 * i;
+    ap[i] = x + (size_t)min(m0 + r, T - 1) * d + lc * 8;
+    bp[i] = ws + (size_t)min(n0 + r, N - 1) * d + lc * 8;
+    lofs[i] = r * 128 + ((lc ^ rswz(r)) << 4);
+  }
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const int wm = w >> 1, wn = w & 1, fr = lane & 31, fh = lane >> 5;
+  const int ar = wm * 32 + fr, br = wn * 32 + fr;
+  f32x16_t acc[3];
+#pragma unroll
+  for (int t = 0; t < 3; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+  for (int k0 = 0; k0 < d; k0 += RM_BK) {
+    u32x4_t va[2], vb[3][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      va[i] = *reinterpret_cast<const u32x4_t*>(ap[i] + k0);
+#pragma unroll
+      for (int t = 0; t < 3; ++t)
+        vb[t][i] = *reinterpret_cast<const u32x4_t*>(bp[i] + t * plane + k0);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      *reinterpret_cast<u32x4_t*>(As + lofs[i]) = va[i];
+#pragma unroll
+      for (int t = 0; t < 3; ++t) *reinterpret_cast<u32x4_t*>(Bs[t] + lofs[i]) = vb[t][i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < RM_BK / 16; ++ks) {
+      const int ch = 2 * ks + fh;
+      const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(As + ar * 128 + ((ch ^ rswz(ar)) << 4));
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        const bf16x8_t bf =
+            *reinterpret_cast<const bf16x8_t*>(Bs[t] + br * 128 + ((ch ^ rswz(br)) << 4));
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc[t], 0, 0, 0);
+      }
+    }
+  }
+  // 32x32 accumulator layout: column = lane & 31, row = 8*(r/4) + 4*(lane/32) + r%4
+  const int col = n0 + wn * 32 + fr;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = m0 + wm * 32 + 8 * (r >> 2) + 4 * fh + (r & 3);
+    if (row < T && col < N) logits[(size_t)row * N + col] = (acc[2][r] + acc[1][r]) + acc[0][r];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // K2: one wavefront per token.  Lane l holds experts [l*P, l*P+P).
 // ---------------------------------------------------------------------------
 
@@ -266,15 +366,19 @@ __global__ __launch_bounds__(256) void topk_kernel(
 }  // namespace
 
 hipError_t launch_router_gemm(const moe_shape& s, const void* x, const float* w_router,
-                              float* logits, hipStream_t st) {
+                              float* logits, const Workspace& w, hipStream_t st) {
   const int T = (int)s.T, N = s.n_experts, d = s.d_model;
-  dim3 grid((T + RT_BM - 1) / RT_BM, (N + RT_BN - 1) / RT_BN);
-  if (s.dtype == MOE_DTYPE_BF16)
-    router_gemm_kernel<bf16_t><<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(x), w_router,
-                                                      logits, T, N, d);
-  else
+  if (s.dtype == MOE_DTYPE_BF16) {
+    const long long n = (long long)N * d;
+    split3_kernel<<<(int)min((n + 255) / 256, 2048LL), 256, 0, st>>>(w_router, w.wsplit, n);
+    dim3 grid((T + RM_BM - 1) / RM_BM, (N + RM_BN - 1) / RM_BN);
+    router_mfma_kernel<<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(x), w.wsplit, logits,
+                                             T, N, d);
+  } else {
+    dim3 grid((T + RT_BM - 1) / RT_BM, (N + RT_BN - 1) / RT_BN);
     router_gemm_kernel<float><<<grid, 256, 0, st>>>(static_cast<const float*>(x), w_router,
                                                      logits, T, N, d);
+  }
   return hipGetLastError();
 }
 

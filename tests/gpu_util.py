@@ -127,12 +127,14 @@ def check_routing_and_dispatch(out: Dict[str, torch.Tensor], ref: dict, T: int, 
     assert np.abs(g - ref["topk_w"]).max() <= 4 * k * 2.0 ** -24 * max(1.0, np.abs(ref["topk_w"]).max())
 
 
-def router_tolerance_ok(x: np.ndarray, wr: np.ndarray, logit_add, logits_gpu: np.ndarray):
-    """|l_gpu - l| <= gamma_d * sum_i |x_i w_i| (+ one rounding of the logit
-    offset): the worst-case bound of an fp32 dot product of length d, any
-    summation order; plus a relative L2 check at 5x the random-walk scale
-    sqrt(d) * 2^-24."""
-    d = x.shape[1]
+def router_tolerance_ok(x: np.ndarray, wr: np.ndarray, logit_add, logits_gpu: np.ndarray,
+                        terms: int = 1):
+    """|l_gpu - l| <= gamma_n * sum_i |x_i w_i| (+ one rounding of the logit
+    offset): the worst-case bound of an fp32 sum of n = terms*d products, any
+    summation order (terms = 3 when each fp32 weight is carried as three
+    exact bf16 parts, whose representation error 2^-27 |w| is far below it);
+    plus a relative L2 check at 5x the random-walk scale sqrt(n) * 2^-24."""
+    d = x.shape[1] * terms
     u = 2.0 ** -24
     gamma = d * u / (1 - d * u)
     ref = oracle.router_logits(x, wr, logit_add)
