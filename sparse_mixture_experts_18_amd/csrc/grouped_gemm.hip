@@ -52,7 +52,7 @@ __device__ __forceinline__ void block_exclusive_scan2(int* sh0, int* sh1, int v0
 // Cost of an item for the XCD split: (live 32-row sub-tiles + a fixed part for
 // the weight slice every item streams) x k-slices.
 #ifndef MOE_COST_FIXED
-#define MOE_COST_FIXED 8
+#define MOE_COST_FIXED 2
 #endif
 
 // Work-list header (int32): [0] item count, [1..9] XCD range starts
@@ -217,9 +217,10 @@ struct GCfg {
   static constexpr int DROWS = 1024 / ROWB;   // rows per wave DMA instruction
   static constexpr int A_BYTES = BM * ROWB, B_BYTES = BNW * ROWB;
   static constexpr int A_LOADS = A_BYTES / 1024 / WAVES, B_LOADS = B_BYTES / 1024 / WAVES;
-  static constexpr int LDS_BYTES = SA * A_BYTES + SB * B_BYTES;
+  // the whole 160 KiB: items with few rows use it for deeper rings
+  static constexpr int LDS_BYTES = 160 * 1024;
   static_assert(A_LOADS * 1024 * WAVES == A_BYTES && B_LOADS * 1024 * WAVES == B_BYTES, "");
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  static_assert(SA * A_BYTES + SB * B_BYTES <= LDS_BYTES, "LDS");
   static_assert(SB >= SA && SA >= 2 && SB <= SA + 1, "B runs at most one slice ahead of A");
   __device__ static __forceinline__ int swz(int r) { return (r / RP) % CPR; }
 };
@@ -312,20 +313,26 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& g, const WorkItem
     b_off[j] = (uint32_t)wrow * (uint32_t)K + (dpos ^ C::swz(r)) * 8;
   }
 
-  // LDS: SA buffers of the A slice, then SB buffers of the B slice.  B (the
-  // weight stream) is fetched SB-1 slices ahead, A (rows shared through L2)
-  // SA-1 slices ahead.
+  // LDS: SA buffers of the A slice (only the live rows), then SB buffers of
+  // the B slice.  Items with fewer rows have smaller A slices and get deeper
+  // rings (their short MFMA phase hides less latency per slice).
+  constexpr int A_SL = C::RG * MS * 32 * C::ROWB;  // bytes of one A slice
+  constexpr int SDEEP = (C::LDS_BYTES / (A_SL + C::B_BYTES)) < 4
+                            ? (C::LDS_BYTES / (A_SL + C::B_BYTES)) : 4;
+  constexpr int SA = SDEEP > C::SA ? SDEEP : C::SA;
+  constexpr int SB = SDEEP > C::SB ? SDEEP : C::SB;
+  static_assert(SA * A_SL + SB * C::B_BYTES <= C::LDS_BYTES, "LDS");
   unsigned char* const Abuf = lds;
-  unsigned char* const Bbuf = lds + C::SA * C::A_BYTES;
+  unsigned char* const Bbuf = lds + SA * A_SL;
   const int nk = K / C::BK;
   auto issue_a = [&](int kt) {
-    unsigned char* st = Abuf + (kt % C::SA) * C::A_BYTES;
+    unsigned char* st = Abuf + (kt % SA) * A_SL;
     const int k0 = kt * C::BK;
 #pragma unroll
     for (int j = 0; j < AL; ++j) dma16(A + a_off[j] + k0, st + (w * AL + j) * 1024);
   };
   auto issue_b = [&](int kt) {
-    unsigned char* st = Bbuf + (kt % C::SB) * C::B_BYTES;
+    unsigned char* st = Bbuf + (kt % SB) * C::B_BYTES;
     const int k0 = kt * C::BK;
 #pragma unroll
     for (int j = 0; j < C::B_LOADS; ++j)
@@ -360,24 +367,24 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& g, const WorkItem
   // at iteration kt the loads of slice kt are complete once no more than the
   // younger ones are outstanding: B(kt+1) .. B(kt+SB-2) and A(kt+1) ..
   // A(kt+SA-2) when B leads by one slice, A/B(kt+1 .. kt+SA-2) otherwise.
-  constexpr int LEAD = C::SB - C::SA;
-  constexpr int YOUNGER = (C::SA - 2) * (AL + C::B_LOADS) + LEAD * C::B_LOADS;
+  constexpr int LEAD = SB - SA;
+  constexpr int YOUNGER = (SA - 2) * (AL + C::B_LOADS) + LEAD * C::B_LOADS;
 #pragma unroll
-  for (int j = -(C::SB - 1); j < 0; ++j) {
-    if (j + C::SA - 1 >= 0 && j + C::SA - 1 < nk) issue_a(j + C::SA - 1);
-    if (j + C::SB - 1 < nk) issue_b(j + C::SB - 1);
+  for (int j = -(SB - 1); j < 0; ++j) {
+    if (j + SA - 1 >= 0 && j + SA - 1 < nk) issue_a(j + SA - 1);
+    if (j + SB - 1 < nk) issue_b(j + SB - 1);
   }
 
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + C::SB - 2 < nk) wait_vm<YOUNGER>();
+    if (kt + SB - 2 < nk) wait_vm<YOUNGER>();
     else wait_vm<0>();
     // every wave's part of slice kt is now in LDS, and every wave is done
     // with slice kt-1, whose buffers the next loads overwrite
     __builtin_amdgcn_s_barrier();
-    if (kt + C::SA - 1 < nk) issue_a(kt + C::SA - 1);
-    if (kt + C::SB - 1 < nk) issue_b(kt + C::SB - 1);
-    const unsigned char* As = Abuf + (kt % C::SA) * C::A_BYTES;
-    const unsigned char* Bs = Bbuf + (kt % C::SB) * C::B_BYTES;
+    if (kt + SA - 1 < nk) issue_a(kt + SA - 1);
+    if (kt + SB - 1 < nk) issue_b(kt + SB - 1);
+    const unsigned char* As = Abuf + (kt % SA) * A_SL;
+    const unsigned char* Bs = Bbuf + (kt % SB) * C::B_BYTES;
     // fragments of k-step ks+1 are read while the MFMAs of k-step ks run
     bf16x8_t bf[2][NT], af[2][MS];
     load_frags<C, MS>(As, Bs, a_row, b_row, fh, 0, af[0], bf[0]);
@@ -438,7 +445,7 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& g, const WorkItem
 // together on one L2, and an item's result does not depend on which block
 // computes it.
 #ifndef MOE_PERSISTENT
-#define MOE_PERSISTENT 0
+#define MOE_PERSISTENT 1
 #endif
 
 // Variant main loop: operands go global -> registers -> LDS.  Two register
@@ -640,7 +647,7 @@ template <bool GATED, class C>
 __global__ __launch_bounds__(C::THREADS) void gemm_bf16_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds[C::LDS_BYTES];
 #if MOE_PERSISTENT
-  __shared__ int s_item;
+  int& s_item = *reinterpret_cast<int*>(lds);  // LDS is idle between items
   const int x = blockIdx.x & 7;
   const int beg = g.hdr[kHdrStart + x], end = g.hdr[kHdrStart + x + 1];
   for (;;) {
