@@ -117,9 +117,12 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
         else hi = mid - 1;
       }
       const int seg = lo, loc = i - st[seg], m = loc % mts[seg], nt = loc / mts[seg];
-      const int nr = min(bm, rowss[seg] - m * bm);
+      // a segment's rows are cut into mt near-equal, 32-aligned row blocks,
+      // so the row blocks that share a weight slab run at the same pace
+      const int part = ((rowss[seg] + mts[seg] - 1) / mts[seg] + 31) / 32 * 32;
+      const int nr = min(part, rowss[seg] - m * part);
       cost = (((nr + 31) >> 5) + MOE_COST_FIXED) * (seg < N ? kr : ks);
-      return WorkItem{seg, rbases[seg] + m * bm, nr, nt};
+      return WorkItem{seg, rbases[seg] + m * part, nr, nt};
     };
     int local = 0;
     for (int i = i0; i < i1; ++i) {
