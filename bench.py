@@ -7,10 +7,11 @@ grouped SwiGLU expert GEMMs incl. the shared expert, combine) over one batch
 of synthetic, seeded inputs already resident in HBM.  Prints ONE JSON line.
 
 Extra fields beside the contract's:
-  roofline      the grouped expert-GEMM stage (GEMM1+SwiGLU and GEMM2 over
-                every expert segment incl. the shared expert), timed live with
-                HIP events on the stream it runs on; algorithmic FLOPs / time
-                against the dense bf16 MFMA peak
+  roofline      the dominant kernel, the gate/up grouped GEMM with the SwiGLU
+                epilogue (every expert segment and the shared expert), timed
+                live with HIP events on the stream it runs on: algorithmic
+                FLOPs / time against the dense bf16 MFMA peak (decode shape:
+                algorithmic bytes / time against the HBM peak)
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload,
                 timed on this host's cores
 """
@@ -50,6 +51,30 @@ def algorithmic_flops(cfg, n_kept: int) -> dict:
     shared = 6.0 * T * d * cfg.d_ff_shared
     return dict(router=router, experts=experts, shared=shared,
                 total=router + experts + shared)
+
+
+def committed_traffic(workload: str):
+    """HBM bytes per launch of the gate/up GEMM on this workload, from the
+    committed rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, each scaled
+    by the same counter on a plain 1 GiB copy); None when there is none or the
+    kernel source changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"gemm_gate_up_{workload}_hbm_traffic.md")
+    src = os.path.join(ROOT, "sparse_mixture_experts_18_amd", "csrc", "grouped_gemm.hip")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and line.strip().startswith("- "):
+            k_, v_ = line.strip()[2:].split(":", 1)
+            vals[k_.strip()] = v_.strip().strip("`")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if vals.get("grouped_gemm.hip sha256") != sha:
+        return None
+    try:
+        return int(float(vals["hbm bytes per launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(cfg, inp, n_tokens: int) -> dict:
@@ -149,7 +174,7 @@ def main():
     tflops = fl["total"] / (ms * 1e-3) / 1e12
     print(f"[bench] {ms:.3f} ms/step", file=sys.stderr, flush=True)
 
-    # ---- stage timing: the grouped expert GEMMs alone, same stream ----
+    # ---- per-kernel timing of the expert GEMMs, same stream, HIP events ----
     sc = torch.empty((T, N), dtype=torch.float32, device=dev)
     ti = torch.empty((T, k), dtype=torch.int32, device=dev)
     tw = torch.empty((T, k), dtype=torch.float32, device=dev)
@@ -158,32 +183,62 @@ def main():
     sl = torch.empty((T * k,), dtype=torch.int32, device=dev)
     pm = torch.empty((T * k,), dtype=torch.int32, device=dev)
     nkd = torch.empty((2,), dtype=torch.int32, device=dev)
-    yp = torch.empty((T * k, d), dtype=shape.torch_dtype, device=dev)
-    ysh = (torch.empty((T, d), dtype=shape.torch_dtype, device=dev)
-           if cfg.d_ff_shared else None)
+    dt = shape.torch_dtype
+    h = torch.empty((T * k, cfg.d_ff), dtype=dt, device=dev)
+    hs = torch.empty((T, cfg.d_ff_shared), dtype=dt, device=dev) if cfg.d_ff_shared else None
+    yp = torch.empty((T * k, d), dtype=dt, device=dev)
+    ysh = torch.empty((T, d), dtype=dt, device=dev) if cfg.d_ff_shared else None
     moe.moe_route(shape, inp.x, inp.w_router, inp.logit_add, None, inp.bias, None, sc, ti, tw,
                   ws)
     moe.moe_dispatch(shape, ti, cn, of, sl, pm, nkd, ws)
-    stage = []
-    for _ in range(2 + args.stage_iters):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        moe.moe_expert_ffn(shape, inp.x, pm, of, inp.w1, inp.w2, inp.w1_shared,
-                           inp.w2_shared, yp, ysh, ws)
-        b.record(stream)
-        stage.append((a, b))
-    torch.cuda.synchronize()
-    st_ms = sorted(a.elapsed_time(b) for a, b in stage[2:])
-    st_avg = sum(st_ms) / len(st_ms)
-    gemm_flops = fl["experts"] + fl["shared"]
-    achieved = gemm_flops / (st_avg * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": None,
-                "kernel": "grouped expert GEMM stage (gemm_bf16_kernel<true> + <false>)",
-                "avg_ms": round(st_avg, 4),
-                "flops_per_launch": gemm_flops}
+
+    def timed(fn, iters):
+        evs = []
+        for _ in range(2 + iters):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        t = [a.elapsed_time(b) for a, b in evs[2:]]
+        return sum(t) / len(t)
+
+    g1_ms = timed(lambda: moe.moe_expert_gate_up(shape, inp.x, pm, of, inp.w1, inp.w1_shared,
+                                                 h, hs, ws), args.stage_iters)
+    g2_ms = timed(lambda: moe.moe_expert_down(shape, h, hs, of, inp.w2, inp.w2_shared, yp, ysh,
+                                              ws), args.stage_iters)
+    counts = cn.cpu().numpy()
+    g1_flops = 4.0 * d * cfg.d_ff * n_kept + 4.0 * T * d * cfg.d_ff_shared
+    g2_flops = 2.0 * d * cfg.d_ff * n_kept + 2.0 * T * d * cfg.d_ff_shared
+    touched = int((counts > 0).sum())
+    esz = 2 if cfg.dtype == "bf16" else 4
+    g1_bytes = esz * (touched * 2 * cfg.d_ff * d + 2 * cfg.d_ff_shared * d + T * d
+                      + n_kept * cfg.d_ff + T * cfg.d_ff_shared)
+    traffic = committed_traffic(cfg.name)
+    if cfg.name == "decode":
+        # weight streaming bounds this layer: algorithmic bytes = touched experts' W1, x, h
+        achieved = g1_bytes / (g1_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                    "traffic": traffic}
+    else:
+        achieved = g1_flops / (g1_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                    "traffic": traffic}
+    roofline.update({
+        "kernel": "gemm_bf16_kernel<true> (gate/up projection + SwiGLU, all expert segments "
+                  "and the shared expert; timed through moe_expert_gate_up, which also builds "
+                  "the work list)",
+        "avg_ms": round(g1_ms, 4),
+        "flops_per_launch": g1_flops,
+        "algorithmic_bytes_per_launch": g1_bytes,
+        "touched_experts": touched,
+    })
+    gemm2 = {"kernel": "gemm_bf16_kernel<false> (down projection)", "avg_ms": round(g2_ms, 4),
+             "tflops": round(g2_flops / (g2_ms * 1e-3) / 1e12, 2)}
 
     res = {
         "metric": METRIC,
@@ -207,6 +262,7 @@ def main():
         "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "n_kept": n_kept,
         "roofline": roofline,
+        "gemm2": gemm2,
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

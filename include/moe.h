@@ -172,6 +172,25 @@ moe_status moe_expert_ffn(const moe_shape* shape, const void* x,
                           void* y_perm, void* y_shared, void* ws,
                           size_t ws_bytes, void* stream);
 
+/* The two projections of moe_expert_ffn as separate calls (same kernels).
+ * gate_up: h[s] = silu(x_t W_gate,e^T) * (x_t W_up,e^T) for every kept row s
+ * (t = perm[s] / k, e its expert), h [T*k, d_ff] dtype (rows >= R untouched),
+ * and h_shared [T, d_ff_shared] for the shared expert (required iff
+ * d_ff_shared > 0).  down: y_perm[s] = h[s] W2_e^T, y_shared = h_shared
+ * W2s^T.  offsets as produced by moe_dispatch; all pointers device memory.
+ * Source: "MoE architecture in practice", expert-parallelism section (one
+ * grouped GEMM over the contiguous expert segments); the SwiGLU expert. */
+moe_status moe_expert_gate_up(const moe_shape* shape, const void* x,
+                              const int32_t* perm, const int32_t* offsets,
+                              const void* w1, const void* w1_shared, void* h,
+                              void* h_shared, void* ws, size_t ws_bytes,
+                              void* stream);
+moe_status moe_expert_down(const moe_shape* shape, const void* h,
+                           const void* h_shared, const int32_t* offsets,
+                           const void* w2, const void* w2_shared, void* y_perm,
+                           void* y_shared, void* ws, size_t ws_bytes,
+                           void* stream);
+
 /* Combine: y_t = sum_j [slot_tj >= 0] g_tj y_perm[slot_tj] (+ y_shared_t),
  * fp32 accumulation in ascending j, then the shared term; dropped
  * assignments add nothing.  y_shared NULL when there is no shared expert. */

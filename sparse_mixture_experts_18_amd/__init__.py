@@ -8,9 +8,10 @@ fallback: if the library is missing or fails to load, every call raises.
 The functions mirror the C ABI in include/moe.h one to one (same names, same
 argument order, tensors in place of pointers):
 
-    moe_route, moe_dispatch, moe_expert_ffn, moe_combine, moe_bias_update,
-    moe_forward, moe_workspace_bytes, moe_check_shape, moe_capacity,
-    moe_status_string, moe_abi_version
+    moe_route, moe_dispatch, moe_expert_ffn, moe_expert_gate_up,
+    moe_expert_down, moe_combine, moe_bias_update, moe_forward,
+    moe_workspace_bytes, moe_check_shape, moe_capacity, moe_status_string,
+    moe_abi_version
 
 plus ``MoeShape`` (the C struct), ``workspace(shape)`` and ``forward(...)``,
 a convenience wrapper that allocates the outputs of one layer forward.
@@ -102,6 +103,10 @@ _SIGS = {
     "moe_dispatch": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_expert_ffn": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                       ctypes.c_size_t, _P]),
+    "moe_expert_gate_up": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P,
+                                          ctypes.c_size_t, _P]),
+    "moe_expert_down": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                       _P]),
     "moe_combine": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P]),
     "moe_bias_update": (ctypes.c_int, [_S, _P, _P, ctypes.c_float, ctypes.c_float, _P, _P, _P,
                                        ctypes.c_size_t, _P]),
@@ -239,6 +244,33 @@ def moe_expert_ffn(shape, x, perm, offsets, w1, w2, w1_shared, w2_shared, y_perm
         _ptr(w2_shared, "w2_shared", dt, d * fs), _ptr(y_perm, "y_perm", dt, T * k * d),
         _ptr(y_shared, "y_shared", dt, T * d), p, n, _stream(stream))
     _check(st, "moe_expert_ffn")
+
+
+def moe_expert_gate_up(shape, x, perm, offsets, w1, w1_shared, h, h_shared, ws, stream=None):
+    T, N, k, d, f, fs = (shape.T, shape.n_experts, shape.top_k, shape.d_model, shape.d_ff,
+                         shape.d_ff_shared)
+    dt = _dt(shape)
+    p, n = _ws(ws)
+    st = lib().moe_expert_gate_up(
+        ctypes.byref(shape), _ptr(x, "x", dt, T * d), _ptr(perm, "perm", torch.int32, T * k),
+        _ptr(offsets, "offsets", torch.int32, N + 1), _ptr(w1, "w1", dt, N * 2 * f * d),
+        _ptr(w1_shared, "w1_shared", dt, 2 * fs * d), _ptr(h, "h", dt, T * k * f),
+        _ptr(h_shared, "h_shared", dt, T * fs), p, n, _stream(stream))
+    _check(st, "moe_expert_gate_up")
+
+
+def moe_expert_down(shape, h, h_shared, offsets, w2, w2_shared, y_perm, y_shared, ws,
+                    stream=None):
+    T, N, k, d, f, fs = (shape.T, shape.n_experts, shape.top_k, shape.d_model, shape.d_ff,
+                         shape.d_ff_shared)
+    dt = _dt(shape)
+    p, n = _ws(ws)
+    st = lib().moe_expert_down(
+        ctypes.byref(shape), _ptr(h, "h", dt, T * k * f), _ptr(h_shared, "h_shared", dt, T * fs),
+        _ptr(offsets, "offsets", torch.int32, N + 1), _ptr(w2, "w2", dt, N * d * f),
+        _ptr(w2_shared, "w2_shared", dt, d * fs), _ptr(y_perm, "y_perm", dt, T * k * d),
+        _ptr(y_shared, "y_shared", dt, T * d), p, n, _stream(stream))
+    _check(st, "moe_expert_down")
 
 
 def moe_combine(shape, y_perm, y_shared, slot, topk_w, y, stream=None):

@@ -778,43 +778,57 @@ PlanGeom plan_geom(const moe_shape& s) {
 
 }  // namespace
 
-hipError_t launch_expert_ffn(const moe_shape& s, const void* x, const int32_t* perm,
-                             const int32_t* offsets, const void* w1, const void* w2,
-                             const void* w1s, const void* w2s, void* y_perm, void* y_shared,
-                             const Workspace& w, hipStream_t st) {
-  const int T = (int)s.T, N = s.n_experts, d = s.d_model, f = s.d_ff, fs = s.d_ff_shared;
-  const bool bf = s.dtype == MOE_DTYPE_BF16;
-  const int has_shared = fs > 0 ? 1 : 0;
+hipError_t launch_plan(const moe_shape& s, const int32_t* offsets, const Workspace& w,
+                       hipStream_t st) {
+  const int fs = s.d_ff_shared;
   PlanGeom pg = plan_geom(s);
-  plan_kernel<<<1, 1024, 0, st>>>(offsets, N, T, has_shared, pg.bm1, pg.bm2, pg.nt1_r,
-                                  pg.nt1_s, pg.nt2_r, pg.nt2_s, d, d, f, fs > 0 ? fs : 64,
-                                  w.plan1, w.plan1_hdr, w.plan2, w.plan2_hdr);
-  const int grid1 = (int)((w.plan1_cap + 7) / 8 * 8), grid2 = (int)((w.plan2_cap + 7) / 8 * 8);
-  const int grid_bf = MOE_PERSISTENT ? persistent_grid() : 0;
-  if (bf) {
+  plan_kernel<<<1, 1024, 0, st>>>(offsets, s.n_experts, (int)s.T, fs > 0 ? 1 : 0, pg.bm1,
+                                  pg.bm2, pg.nt1_r, pg.nt1_s, pg.nt2_r, pg.nt2_s, s.d_model,
+                                  s.d_model, s.d_ff, fs > 0 ? fs : 64, w.plan1, w.plan1_hdr,
+                                  w.plan2, w.plan2_hdr);
+  return hipGetLastError();
+}
+
+// h = silu(x W_gate^T) * (x W_up^T) over the work list built by launch_plan
+hipError_t launch_gemm1(const moe_shape& s, const void* x, const int32_t* perm, const void* w1,
+                        const void* w1s, void* h, void* hs, const Workspace& w,
+                        hipStream_t st) {
+  const int N = s.n_experts, d = s.d_model, f = s.d_ff, fs = s.d_ff_shared;
+  if (s.dtype == MOE_DTYPE_BF16) {
     GemmArgs g1{static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(x), perm, s.top_k,
                 static_cast<const bf16_t*>(w1), static_cast<const bf16_t*>(w1s),
-                static_cast<bf16_t*>(w.h), static_cast<bf16_t*>(w.h_shared), d, d, f, fs,
+                static_cast<bf16_t*>(h), static_cast<bf16_t*>(hs), d, d, f, fs,
                 (long long)2 * f * d, N, w.plan1, w.plan1_hdr};
-    gemm_bf16_kernel<true, Cfg1><<<grid_bf ? grid_bf : grid1, Cfg1::THREADS, 0, st>>>(g1);
-    GemmArgs g2{static_cast<const bf16_t*>(w.h), static_cast<const bf16_t*>(w.h_shared),
-                nullptr, s.top_k, static_cast<const bf16_t*>(w2),
-                static_cast<const bf16_t*>(w2s), static_cast<bf16_t*>(y_perm),
-                static_cast<bf16_t*>(y_shared), f, fs, d, d, (long long)d * f, N, w.plan2,
-                w.plan2_hdr};
-    gemm_bf16_kernel<false, Cfg2><<<grid_bf ? grid_bf : grid2, Cfg2::THREADS, 0, st>>>(g2);
+    const int grid = MOE_PERSISTENT ? persistent_grid() : (int)((w.plan1_cap + 7) / 8 * 8);
+    gemm_bf16_kernel<true, Cfg1><<<grid, Cfg1::THREADS, 0, st>>>(g1);
   } else {
     GemmArgsF g1{static_cast<const float*>(x), static_cast<const float*>(x), perm, s.top_k,
                  static_cast<const float*>(w1), static_cast<const float*>(w1s),
-                 static_cast<float*>(w.h), static_cast<float*>(w.h_shared), d, d, f, fs,
+                 static_cast<float*>(h), static_cast<float*>(hs), d, d, f, fs,
                  (long long)2 * f * d, N, w.plan1, w.plan1_hdr};
-    gemm_f32_kernel<true><<<grid1, 256, 0, st>>>(g1);
-    GemmArgsF g2{static_cast<const float*>(w.h), static_cast<const float*>(w.h_shared),
-                 nullptr, s.top_k, static_cast<const float*>(w2),
-                 static_cast<const float*>(w2s), static_cast<float*>(y_perm),
-                 static_cast<float*>(y_shared), f, fs, d, d, (long long)d * f, N, w.plan2,
-                 w.plan2_hdr};
-    gemm_f32_kernel<false><<<grid2, 256, 0, st>>>(g2);
+    gemm_f32_kernel<true><<<(int)((w.plan1_cap + 7) / 8 * 8), 256, 0, st>>>(g1);
+  }
+  return hipGetLastError();
+}
+
+// y_perm = h W2^T (and y_shared = h_shared W2s^T) over the second work list
+hipError_t launch_gemm2(const moe_shape& s, const void* h, const void* hs, const void* w2,
+                        const void* w2s, void* y_perm, void* y_shared, const Workspace& w,
+                        hipStream_t st) {
+  const int N = s.n_experts, d = s.d_model, f = s.d_ff, fs = s.d_ff_shared;
+  if (s.dtype == MOE_DTYPE_BF16) {
+    GemmArgs g2{static_cast<const bf16_t*>(h), static_cast<const bf16_t*>(hs), nullptr,
+                s.top_k, static_cast<const bf16_t*>(w2), static_cast<const bf16_t*>(w2s),
+                static_cast<bf16_t*>(y_perm), static_cast<bf16_t*>(y_shared), f, fs, d, d,
+                (long long)d * f, N, w.plan2, w.plan2_hdr};
+    const int grid = MOE_PERSISTENT ? persistent_grid() : (int)((w.plan2_cap + 7) / 8 * 8);
+    gemm_bf16_kernel<false, Cfg2><<<grid, Cfg2::THREADS, 0, st>>>(g2);
+  } else {
+    GemmArgsF g2{static_cast<const float*>(h), static_cast<const float*>(hs), nullptr,
+                 s.top_k, static_cast<const float*>(w2), static_cast<const float*>(w2s),
+                 static_cast<float*>(y_perm), static_cast<float*>(y_shared), f, fs, d, d,
+                 (long long)d * f, N, w.plan2, w.plan2_hdr};
+    gemm_f32_kernel<false><<<(int)((w.plan2_cap + 7) / 8 * 8), 256, 0, st>>>(g2);
   }
   return hipGetLastError();
 }

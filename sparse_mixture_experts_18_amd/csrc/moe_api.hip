@@ -178,9 +178,46 @@ moe_status moe_expert_ffn(const moe_shape* shape, const void* x, const int32_t* 
   if (shape->d_ff_shared > 0 && (!w1_shared || !w2_shared || !y_shared)) return MOE_ERR_INVALID;
   Workspace w;
   if ((st = check_ws(shape, ws, ws_bytes, w)) != MOE_OK) return st;
-  return hip_status(launch_expert_ffn(*shape, x, perm, offsets, w1, w2, w1_shared, w2_shared,
-                                      y_perm, shape->d_ff_shared > 0 ? y_shared : nullptr, w,
-                                      static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool sh = shape->d_ff_shared > 0;
+  if (launch_plan(*shape, offsets, w, s) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_gemm1(*shape, x, perm, w1, w1_shared, w.h, w.h_shared, w, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  return hip_status(launch_gemm2(*shape, w.h, w.h_shared, w2, w2_shared, y_perm,
+                                 sh ? y_shared : nullptr, w, s));
+}
+
+moe_status moe_expert_gate_up(const moe_shape* shape, const void* x, const int32_t* perm,
+                              const int32_t* offsets, const void* w1, const void* w1_shared,
+                              void* h, void* h_shared, void* ws, size_t ws_bytes,
+                              void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!x || !perm || !offsets || !w1 || !h) return MOE_ERR_INVALID;
+  if (shape->d_ff_shared > 0 && (!w1_shared || !h_shared)) return MOE_ERR_INVALID;
+  Workspace w;
+  if ((st = check_ws(shape, ws, ws_bytes, w)) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (launch_plan(*shape, offsets, w, s) != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(launch_gemm1(*shape, x, perm, w1, w1_shared, h,
+                                 shape->d_ff_shared > 0 ? h_shared : nullptr, w, s));
+}
+
+moe_status moe_expert_down(const moe_shape* shape, const void* h, const void* h_shared,
+                           const int32_t* offsets, const void* w2, const void* w2_shared,
+                           void* y_perm, void* y_shared, void* ws, size_t ws_bytes,
+                           void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!h || !offsets || !w2 || !y_perm) return MOE_ERR_INVALID;
+  if (shape->d_ff_shared > 0 && (!h_shared || !w2_shared || !y_shared)) return MOE_ERR_INVALID;
+  Workspace w;
+  if ((st = check_ws(shape, ws, ws_bytes, w)) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (launch_plan(*shape, offsets, w, s) != hipSuccess) return MOE_ERR_HIP;
+  const bool sh = shape->d_ff_shared > 0;
+  return hip_status(launch_gemm2(*shape, h, sh ? h_shared : nullptr, w2, w2_shared, y_perm,
+                                 sh ? y_shared : nullptr, w, s));
 }
 
 moe_status moe_combine(const moe_shape* shape, const void* y_perm, const void* y_shared,
@@ -231,8 +268,11 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_rou
   if (launch_topk(sh, w.logits, logit_add, false, bias, sc, ti, tw, s) != hipSuccess)
     return MOE_ERR_HIP;
   if (launch_dispatch(sh, ti, cn, of, sl, w.perm, nk, w, s) != hipSuccess) return MOE_ERR_HIP;
-  if (launch_expert_ffn(sh, x, w.perm, of, w1, w2, w1_shared, w2_shared, w.y_perm,
-                        shared ? w.y_shared : nullptr, w, s) != hipSuccess)
+  if (launch_plan(sh, of, w, s) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_gemm1(sh, x, w.perm, w1, w1_shared, w.h, w.h_shared, w, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (launch_gemm2(sh, w.h, w.h_shared, w2, w2_shared, w.y_perm,
+                   shared ? w.y_shared : nullptr, w, s) != hipSuccess)
     return MOE_ERR_HIP;
   return hip_status(
       launch_combine(sh, w.y_perm, shared ? w.y_shared : nullptr, sl, tw, y, s));

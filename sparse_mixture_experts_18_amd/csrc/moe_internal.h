@@ -80,10 +80,14 @@ hipError_t launch_topk(const moe_shape& s, const float* logits, const float* log
 hipError_t launch_dispatch(const moe_shape& s, const int32_t* topk_idx, int32_t* counts,
                            int32_t* offsets, int32_t* slot, int32_t* perm, int32_t* nkd,
                            const Workspace& w, hipStream_t st);
-hipError_t launch_expert_ffn(const moe_shape& s, const void* x, const int32_t* perm,
-                             const int32_t* offsets, const void* w1, const void* w2,
-                             const void* w1s, const void* w2s, void* y_perm, void* y_shared,
-                             const Workspace& w, hipStream_t st);
+hipError_t launch_plan(const moe_shape& s, const int32_t* offsets, const Workspace& w,
+                       hipStream_t st);
+hipError_t launch_gemm1(const moe_shape& s, const void* x, const int32_t* perm, const void* w1,
+                        const void* w1s, void* h, void* hs, const Workspace& w,
+                        hipStream_t st);
+hipError_t launch_gemm2(const moe_shape& s, const void* h, const void* hs, const void* w2,
+                        const void* w2s, void* y_perm, void* y_shared, const Workspace& w,
+                        hipStream_t st);
 hipError_t launch_combine(const moe_shape& s, const void* y_perm, const void* y_shared,
                           const int32_t* slot, const float* topk_w, void* y, hipStream_t st);
 hipError_t launch_bias_update(const moe_shape& s, const int32_t* counts, const float* scores,

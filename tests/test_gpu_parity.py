@@ -100,6 +100,45 @@ def test_steps_compose_to_forward_and_expert_rows(name):
         assert err <= tol_for(cfg)
 
 
+@pytest.mark.parametrize("name", ["tiny", "dsv3"])
+def test_gate_up_then_down_equals_expert_ffn(name):
+    """moe_expert_gate_up + moe_expert_down through caller buffers give
+    moe_expert_ffn's rows bit for bit, and h matches the oracle's SwiGLU
+    intermediate on sampled rows."""
+    cfg = W.CONFIGS[name]
+    T = min(cfg.T, 1024)
+    inp = W.make_inputs(cfg, seed=6, device="cuda", T=T)
+    shape = moe.MoeShape.from_config(cfg, T=T)
+    st = run_steps(inp, shape)
+    k, d, f, fs = cfg.top_k, cfg.d_model, cfg.d_ff, cfg.d_ff_shared
+    dt = shape.torch_dtype
+    ws = moe.workspace(shape)
+    h = torch.zeros((T * k, f), dtype=dt, device="cuda")
+    hs = torch.zeros((T, fs), dtype=dt, device="cuda") if fs else None
+    yp = torch.zeros((T * k, d), dtype=dt, device="cuda")
+    ysh = torch.zeros((T, d), dtype=dt, device="cuda") if fs else None
+    moe.moe_expert_gate_up(shape, inp.x, st["perm"], st["offsets"], inp.w1, inp.w1_shared, h,
+                           hs, ws)
+    moe.moe_expert_down(shape, h, hs, st["offsets"], inp.w2, inp.w2_shared, yp, ysh, ws)
+    torch.cuda.synchronize()
+    R = int(st["n_kept_dropped"][0])
+    assert torch.equal(yp[:R], st["y_perm"][:R])
+    if fs:
+        assert torch.equal(ysh, st["y_shared"])
+    # h rows of the first kept assignments vs the oracle's silu(x Wg) * (x Wu)
+    perm = host(st["perm"])[:R]
+    offs = host(st["offsets"])
+    x = host(inp.x)
+    for s_ in sorted(set([0, R // 2, R - 1])):
+        e = int(np.searchsorted(offs, s_, side="right") - 1)
+        t = perm[s_] // k
+        w1e = host(inp.w1[e]).astype(np.float64)
+        a = x[t] @ w1e[:f].T
+        u = x[t] @ w1e[f:].T
+        ref = oracle.silu(a) * u
+        assert rel_l2(host(h[s_]), ref) <= (1e-5 if cfg.dtype == "f32" else 1e-2)
+
+
 def _small_cfg(name, **kw):
     base = dict(T=300, d_model=128, n_experts=8, top_k=2, d_ff=128)
     base.update(kw)
