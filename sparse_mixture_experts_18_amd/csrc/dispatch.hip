@@ -10,9 +10,9 @@
 // sections; llm-compass MoE page, capacity = capacity_factor * tokens / N).
 //
 // Three launches, none of whose results depends on atomic ordering:
-//   rank   one wavefront per chunk of 512 assignments: position inside the
-//          chunk (wave-wide equality counting, 64 lanes at a time) and the
-//          chunk's per-expert histogram
+//   rank   one block per chunk of 512 assignments: position inside the chunk
+//          (wave-wide equality counting per 64 assignments, then a prefix over
+//          the chunk's 8 waves) and the chunk's per-expert histogram
 //   scan   per expert, a running sum over chunks -> chunk base positions and
 //          pre-drop counts; kept = min(count, C); offsets = exclusive scan
 //   place  pos = base + rank; slot / perm
@@ -21,45 +21,46 @@
 namespace moe {
 namespace {
 
-constexpr int RK_WAVES = 4;
+constexpr int RK_WAVES = kDispatchChunk / kWave;  // 8 waves, one per 64 assignments
 
-__global__ __launch_bounds__(256) void rank_kernel(const int32_t* __restrict__ topk_idx,
-                                                   int32_t* __restrict__ rank,
-                                                   int32_t* __restrict__ hist, int A, int N,
-                                                   int nchunks) {
+// one block per chunk of 512 assignments; wave w ranks assignments 64w..64w+63
+// of the chunk (wave-wide equality counting), then a per-expert prefix over
+// the 8 waves turns those into positions inside the chunk
+__global__ __launch_bounds__(kDispatchChunk) void rank_kernel(const int32_t* __restrict__ topk_idx,
+                                                              int32_t* __restrict__ rank,
+                                                              int32_t* __restrict__ hist, int A,
+                                                              int N, int nchunks) {
   __shared__ int cnt[RK_WAVES][512];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int c = blockIdx.x * RK_WAVES + wv;
-  if (c >= nchunks) return;  // wave-uniform; no block barrier in this kernel
-  int* my = cnt[wv];
-  for (int e = lane; e < N; e += kWave) my[e] = 0;
-  __builtin_amdgcn_s_waitcnt(0);
-  __builtin_amdgcn_wave_barrier();
-  for (int step = 0; step < kDispatchChunk / kWave; ++step) {
-    const int a = c * kDispatchChunk + step * kWave + lane;
-    int e = a < A ? topk_idx[a] : -1;
-    if (e >= N) e = -1;  // out-of-range ids are not placed
-    int r = 0;
-    bool last = true;
-    for (int j = 0; j < kWave; ++j) {
-      const int ej = __shfl(e, j, kWave);
-      if (ej == e) {
-        r += j < lane;
-        last = last && !(j > lane);
-      }
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int c = blockIdx.x;
+  for (int i = tid; i < RK_WAVES * 512; i += kDispatchChunk) (&cnt[0][0])[i] = 0;
+  __syncthreads();
+  const int a = c * kDispatchChunk + tid;
+  int e = a < A ? topk_idx[a] : -1;
+  if (e >= N || e < 0) e = -1;  // out-of-range ids are not placed
+  int r = 0;
+  bool last = true;
+  for (int j = 0; j < kWave; ++j) {
+    const int ej = __shfl(e, j, kWave);
+    if (ej == e) {
+      r += j < lane;
+      last = last && !(j > lane);
     }
-    int base = 0;
-    if (e >= 0) base = my[e];
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_wave_barrier();
-    if (e >= 0) {
-      rank[a] = base + r;
-      if (last) my[e] = base + r + 1;
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_wave_barrier();
   }
-  for (int e = lane; e < N; e += kWave) hist[(size_t)c * N + e] = my[e];
+  if (e >= 0 && last) cnt[wv][e] = r + 1;  // this wave's count of expert e
+  __syncthreads();
+  for (int x = tid; x < N; x += kDispatchChunk) {
+    int run = 0;
+#pragma unroll
+    for (int w = 0; w < RK_WAVES; ++w) {
+      const int v = cnt[w][x];
+      cnt[w][x] = run;
+      run += v;
+    }
+    hist[(size_t)c * N + x] = run;
+  }
+  __syncthreads();
+  if (e >= 0) rank[a] = cnt[wv][e] + r;
 }
 
 __global__ __launch_bounds__(512) void scan_kernel(const int32_t* __restrict__ hist,
@@ -72,10 +73,18 @@ __global__ __launch_bounds__(512) void scan_kernel(const int32_t* __restrict__ h
   const int e = threadIdx.x;
   int run = 0;
   if (e < N) {
-    for (int c = 0; c < nchunks; ++c) {
-      const int h = hist[(size_t)c * N + e];
-      base[(size_t)c * N + e] = run;
-      run += h;
+    // per expert, a running sum over the chunks; loads batched so that 16 are
+    // in flight at a time
+    constexpr int BATCH = 16;
+    for (int c0 = 0; c0 < nchunks; c0 += BATCH) {
+      int v[BATCH];
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) v[i] = c0 + i < nchunks ? hist[(size_t)(c0 + i) * N + e] : 0;
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
+        if (c0 + i < nchunks) base[(size_t)(c0 + i) * N + e] = run;
+        run += v[i];
+      }
     }
     counts[e] = run;
   }
@@ -127,8 +136,7 @@ hipError_t launch_dispatch(const moe_shape& s, const int32_t* topk_idx, int32_t*
   const int A = (int)(s.T * s.top_k), N = s.n_experts;
   const int nchunks = (A + kDispatchChunk - 1) / kDispatchChunk;
   const long long C = capacity_of(s);
-  rank_kernel<<<(nchunks + RK_WAVES - 1) / RK_WAVES, 256, 0, st>>>(topk_idx, w.rank, w.hist, A,
-                                                                   N, nchunks);
+  rank_kernel<<<nchunks, kDispatchChunk, 0, st>>>(topk_idx, w.rank, w.hist, A, N, nchunks);
   scan_kernel<<<1, 512, 0, st>>>(w.hist, w.base, counts, offsets, nkd, A, N, nchunks, C);
   const int blocks = min((A + 255) / 256, 4096);
   place_kernel<<<blocks, 256, 0, st>>>(topk_idx, w.rank, w.base, offsets, slot, perm, A, N, C);

@@ -96,40 +96,61 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     st2s[1024] = tot2;
   }
   __syncthreads();
-  // Items in segment-major, then column tile, then row block order.  Thread s
-  // fills a contiguous chunk; an item's cost is its 32-row sub-tiles times its
-  // k-slices.  The list is then cut into 8 ranges of equal cost, one per XCD.
-  for (int pass = 0; pass < 2; ++pass) {
+  // Items in segment-major, then column tile, then row block order.  Block p
+  // builds work list p.  Thread s fills a contiguous chunk of the list; an
+  // item's cost is its 32-row sub-tiles (plus a fixed part) times its k-slices.
+  // The list is then cut into 8 ranges of equal cost, one per XCD.
+  {
+    const int pass = blockIdx.x;
     const int* st = pass ? st2s : st1s;
     const int* mts = pass ? mt2s : mt1s;
-    const int bm = pass ? bm2 : bm1;
     const int kr = (pass ? k2_r : k1_r) / 64, ks = (pass ? k2_s : k1_s) / 64;
     WorkItem* plan = pass ? plan2 : plan1;
     int32_t* hdr = pass ? hdr2 : hdr1;
     const int tot = pass ? tot2 : tot1;
     const int chunk = (tot + 1023) / 1024;
     const int i0 = min(tot, s * chunk), i1 = min(tot, i0 + chunk);
-    auto item_at = [&](int i, int& cost) {
-      int lo = 0, hi = 1023;  // last segment with st[seg] <= i (empty ones skipped)
+    // segment of item i0: the last segment with st[seg] <= i0 (empty ones skipped)
+    int seg0 = 0;
+    {
+      int lo = 0, hi = 1023;
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (st[mid] <= i) lo = mid;
+        if (st[mid] <= i0) lo = mid;
         else hi = mid - 1;
       }
-      const int seg = lo, loc = i - st[seg], m = loc % mts[seg], nt = loc / mts[seg];
-      // a segment's rows are cut into mt near-equal, 32-aligned row blocks,
-      // so the row blocks that share a weight slab run at the same pace
-      const int part = ((rowss[seg] + mts[seg] - 1) / mts[seg] + 31) / 32 * 32;
-      const int nr = min(part, rowss[seg] - m * part);
-      cost = (((nr + 31) >> 5) + MOE_COST_FIXED) * (seg < N ? kr : ks);
-      return WorkItem{seg, rbases[seg] + m * part, nr, nt};
+      seg0 = lo;
+    }
+    // walk the chunk: (segment, column tile, row block) advance incrementally
+    auto walk = [&](auto&& visit) {
+      int seg = seg0;
+      int loc = i0 - st[seg];
+      int mt = max(mts[seg], 1);
+      int m = loc % mt, nt = loc / mt;
+      for (int i = i0; i < i1; ++i) {
+        while (i >= st[seg + 1]) {  // next non-empty segment
+          ++seg;
+          mt = max(mts[seg], 1);
+          m = 0;
+          nt = 0;
+        }
+        // a segment's rows are cut into mt near-equal, 32-aligned row blocks,
+        // so the row blocks that share a weight slab run at the same pace
+        const int part = ((rowss[seg] + mt - 1) / mt + 31) / 32 * 32;
+        const int nr = min(part, rowss[seg] - m * part);
+        const int cost = (((nr + 31) >> 5) + MOE_COST_FIXED) * (seg < N ? kr : ks);
+        visit(i, WorkItem{seg, rbases[seg] + m * part, nr, nt}, cost);
+        if (++m == mt) {
+          m = 0;
+          ++nt;
+        }
+      }
     };
     int local = 0;
-    for (int i = i0; i < i1; ++i) {
-      int c;
-      plan[i] = item_at(i, c);
+    walk([&](int i, const WorkItem& it, int c) {
+      plan[i] = it;
       local += c;
-    }
+    });
     int pre, dummy_ex, total, dummy_tot;
     block_exclusive_scan2(sh0, sh1, local, 0, pre, dummy_ex, total, dummy_tot);
     // boundary x = first item i with 8 * cost(items < i) >= x * total
@@ -143,17 +164,14 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     }
     if (total > 0) {
       long long cum = pre;
-      for (int i = i0; i < i1; ++i) {
-        int c;
-        item_at(i, c);
+      walk([&](int i, const WorkItem&, int c) {
         for (int x = 1; x < 8; ++x) {
           const long long tgt = (long long)x * total;
           if (8 * cum < tgt && tgt <= 8 * (cum + c)) hdr[kHdrStart + x] = i + 1;
         }
         cum += c;
-      }
+      });
     }
-    __syncthreads();
   }
 }
 
@@ -782,7 +800,7 @@ hipError_t launch_plan(const moe_shape& s, const int32_t* offsets, const Workspa
                        hipStream_t st) {
   const int fs = s.d_ff_shared;
   PlanGeom pg = plan_geom(s);
-  plan_kernel<<<1, 1024, 0, st>>>(offsets, s.n_experts, (int)s.T, fs > 0 ? 1 : 0, pg.bm1,
+  plan_kernel<<<2, 1024, 0, st>>>(offsets, s.n_experts, (int)s.T, fs > 0 ? 1 : 0, pg.bm1,
                                   pg.bm2, pg.nt1_r, pg.nt1_s, pg.nt2_r, pg.nt2_s, s.d_model,
                                   s.d_model, s.d_ff, fs > 0 ? fs : 64, w.plan1, w.plan1_hdr,
                                   w.plan2, w.plan2_hdr);

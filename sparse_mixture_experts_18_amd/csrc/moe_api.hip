@@ -90,6 +90,7 @@ Workspace layout_workspace(const moe_shape& s, void* ws) {
   w.y_shared = take(T * d * es);
   w.pmean = static_cast<double*>(take(N * 8));
   w.wsplit = static_cast<bf16_t*>(take(s.dtype == MOE_DTYPE_BF16 ? 3 * N * d * 2 : 0));
+  w.router_part = static_cast<float*>(take((size_t)router_split_chunks(s) * T * N * 4));
   w.total = off;
   return w;
 }

@@ -24,7 +24,7 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
 }
 
 constexpr int kWave = 64;
-constexpr int kDispatchChunk = 512;  // assignments ranked by one wave
+constexpr int kDispatchChunk = 512;  // assignments ranked by one block
 
 // Grouped-GEMM tile geometry.  bf16 path: MFMA tiles; fp32 path: VALU tiles.
 constexpr int kBM = 128;       // rows (assignments) per work item, bf16
@@ -62,6 +62,7 @@ struct Workspace {
   void* y_shared;  // [T, d]
   double* pmean;   // [N] mean score per expert (balancing step)
   bf16_t* wsplit;  // [3][N][d] bf16 terms of the fp32 router weight (bf16 layers)
+  float* router_part;  // [chunks][T][N] partial logits of the split router GEMM
   size_t total;
   int64_t plan1_cap, plan2_cap;
 };
@@ -94,5 +95,6 @@ hipError_t launch_bias_update(const moe_shape& s, const int32_t* counts, const f
                               float step, float clamp, float* bias, float* aux_out,
                               double* p_scratch, hipStream_t st);
 void plan_caps(const moe_shape& s, int64_t& cap1, int64_t& cap2);
+int router_split_chunks(const moe_shape& s);  // 0: router GEMM not split
 
 }  // namespace moe

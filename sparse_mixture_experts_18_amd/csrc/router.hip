@@ -118,15 +118,26 @@ constexpr int RM_BM = 64, RM_BN = 64, RM_BK = 64;
 
 __device__ __forceinline__ int rswz(int r) { return (r >> 1) & 7; }
 
+// The k range is cut into chunks of RM_KC: each chunk's three partial GEMMs
+// start from zero, are summed smallest first, and the chunk results are added
+// in chunk order.  A block either walks all chunks (out = logits) or, for
+// small batches, one chunk (out = partials [chunk][T][N], summed in chunk order
+// by router_reduce_kernel): the same fp32 operations in the same order either
+// way, so the logits of a token never depend on the batch size.
+constexpr int RM_KC = 512;
+
 __global__ __launch_bounds__(256) void router_mfma_kernel(const bf16_t* __restrict__ x,
                                                           const bf16_t* __restrict__ ws,
-                                                          float* __restrict__ logits, int T,
-                                                          int N, int d) {
+                                                          float* __restrict__ out, int T,
+                                                          int N, int d, int chunks_per_block) {
   __shared__ __attribute__((aligned(16))) unsigned char As[RM_BM * 128];
   __shared__ __attribute__((aligned(16))) unsigned char Bs[3][RM_BN * 128];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int m0 = blockIdx.x * RM_BM, n0 = blockIdx.y * RM_BN;
   const long long plane = (long long)N * d;
+  const int nkc = (d + RM_KC - 1) / RM_KC;
+  const int c_begin = blockIdx.z * chunks_per_block;
+  const int c_end = min(nkc, c_begin + chunks_per_block);
   // loader: 64 rows x 8 chunks = 512 chunks per tile, 2 per thread
   const int lr = tid >> 3, lc = tid & 7;
   const bf16_t* ap[2];
@@ -142,46 +153,67 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const bf16_t* __restri
   typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
   const int wm = w >> 1, wn = w & 1, fr = lane & 31, fh = lane >> 5;
   const int ar = wm * 32 + fr, br = wn * 32 + fr;
-  f32x16_t acc[3];
+  f32x16_t tot;
+  for (int c = c_begin; c < c_end; ++c) {
+    f32x16_t acc[3];
 #pragma unroll
-  for (int t = 0; t < 3; ++t)
+    for (int t = 0; t < 3; ++t)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
-  for (int k0 = 0; k0 < d; k0 += RM_BK) {
-    u32x4_t va[2], vb[3][2];
+      for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+    const int k_end = min(d, (c + 1) * RM_KC);
+    for (int k0 = c * RM_KC; k0 < k_end; k0 += RM_BK) {
+      u32x4_t va[2], vb[3][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      va[i] = *reinterpret_cast<const u32x4_t*>(ap[i] + k0);
+      for (int i = 0; i < 2; ++i) {
+        va[i] = *reinterpret_cast<const u32x4_t*>(ap[i] + k0);
 #pragma unroll
-      for (int t = 0; t < 3; ++t)
-        vb[t][i] = *reinterpret_cast<const u32x4_t*>(bp[i] + t * plane + k0);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      *reinterpret_cast<u32x4_t*>(As + lofs[i]) = va[i];
-#pragma unroll
-      for (int t = 0; t < 3; ++t) *reinterpret_cast<u32x4_t*>(Bs[t] + lofs[i]) = vb[t][i];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < RM_BK / 16; ++ks) {
-      const int ch = 2 * ks + fh;
-      const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(As + ar * 128 + ((ch ^ rswz(ar)) << 4));
-#pragma unroll
-      for (int t = 0; t < 3; ++t) {
-        const bf16x8_t bf =
-            *reinterpret_cast<const bf16x8_t*>(Bs[t] + br * 128 + ((ch ^ rswz(br)) << 4));
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc[t], 0, 0, 0);
+        for (int t = 0; t < 3; ++t)
+          vb[t][i] = *reinterpret_cast<const u32x4_t*>(bp[i] + t * plane + k0);
       }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        *reinterpret_cast<u32x4_t*>(As + lofs[i]) = va[i];
+#pragma unroll
+        for (int t = 0; t < 3; ++t) *reinterpret_cast<u32x4_t*>(Bs[t] + lofs[i]) = vb[t][i];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int ks = 0; ks < RM_BK / 16; ++ks) {
+        const int ch = 2 * ks + fh;
+        const bf16x8_t af =
+            *reinterpret_cast<const bf16x8_t*>(As + ar * 128 + ((ch ^ rswz(ar)) << 4));
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+          const bf16x8_t bf =
+              *reinterpret_cast<const bf16x8_t*>(Bs[t] + br * 128 + ((ch ^ rswz(br)) << 4));
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc[t], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = (acc[2][r] + acc[1][r]) + acc[0][r];
+      tot[r] = c == c_begin ? p : tot[r] + p;
     }
   }
   // 32x32 accumulator layout: column = lane & 31, row = 8*(r/4) + 4*(lane/32) + r%4
+  float* o = out + (size_t)blockIdx.z * T * N;
   const int col = n0 + wn * 32 + fr;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int row = m0 + wm * 32 + 8 * (r >> 2) + 4 * fh + (r & 3);
-    if (row < T && col < N) logits[(size_t)row * N + col] = (acc[2][r] + acc[1][r]) + acc[0][r];
+    if (row < T && col < N) o[(size_t)row * N + col] = tot[r];
+  }
+}
+
+__global__ __launch_bounds__(256) void router_reduce_kernel(const float* __restrict__ part,
+                                                            float* __restrict__ logits,
+                                                            long long n, int nkc) {
+  for (long long i = blockIdx.x * 256LL + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
+    float v = part[i];
+    for (int c = 1; c < nkc; ++c) v += part[(size_t)c * n + i];
+    logits[i] = v;
   }
 }
 
@@ -365,15 +397,33 @@ __global__ __launch_bounds__(256) void topk_kernel(
 
 }  // namespace
 
+// chunks of the split router GEMM for small batches (0: one pass per block)
+int router_split_chunks(const moe_shape& s) {
+  if (s.dtype != MOE_DTYPE_BF16) return 0;
+  const long long blocks = ((s.T + RM_BM - 1) / RM_BM) * ((s.n_experts + RM_BN - 1) / RM_BN);
+  const int nkc = (s.d_model + RM_KC - 1) / RM_KC;
+  return (blocks < 128 && nkc > 1) ? nkc : 0;
+}
+
 hipError_t launch_router_gemm(const moe_shape& s, const void* x, const float* w_router,
                               float* logits, const Workspace& w, hipStream_t st) {
   const int T = (int)s.T, N = s.n_experts, d = s.d_model;
   if (s.dtype == MOE_DTYPE_BF16) {
     const long long n = (long long)N * d;
     split3_kernel<<<(int)min((n + 255) / 256, 2048LL), 256, 0, st>>>(w_router, w.wsplit, n);
-    dim3 grid((T + RM_BM - 1) / RM_BM, (N + RM_BN - 1) / RM_BN);
-    router_mfma_kernel<<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(x), w.wsplit, logits,
-                                             T, N, d);
+    const int nkc = router_split_chunks(s);
+    if (nkc) {
+      dim3 grid((T + RM_BM - 1) / RM_BM, (N + RM_BN - 1) / RM_BN, nkc);
+      router_mfma_kernel<<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(x), w.wsplit,
+                                               w.router_part, T, N, d, 1);
+      const long long tn = (long long)T * N;
+      router_reduce_kernel<<<(int)min((tn + 255) / 256, 4096LL), 256, 0, st>>>(
+          w.router_part, logits, tn, nkc);
+    } else {
+      dim3 grid((T + RM_BM - 1) / RM_BM, (N + RM_BN - 1) / RM_BN, 1);
+      router_mfma_kernel<<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(x), w.wsplit, logits,
+                                               T, N, d, (d + RM_KC - 1) / RM_KC);
+    }
   } else {
     dim3 grid((T + RT_BM - 1) / RT_BM, (N + RT_BN - 1) / RT_BN);
     router_gemm_kernel<float><<<grid, 256, 0, st>>>(static_cast<const float*>(x), w_router,

@@ -234,11 +234,12 @@ def test_determinism_bitwise():
 
 def test_batch_invariance_dropless():
     """A token's scores, choice and gates do not depend on the batch it is in
-    (batch of 1, of 64 and the full batch)."""
+    (batch of 1, of 64 and a batch of 4096, which runs the router GEMM without
+    the small-batch k split)."""
     cfg = W.CONFIGS["dsv3"]
-    inp = W.make_inputs(cfg, seed=4, device="cuda", T=512)
+    inp = W.make_inputs(cfg, seed=4, device="cuda", T=4096)
     full = run_forward(inp)
-    for lo, hi in [(0, 1), (100, 164), (511, 512)]:
+    for lo, hi in [(0, 1), (100, 164), (4095, 4096)]:
         sub = W.LayerInputs(cfg, inp.x[lo:hi].contiguous(), inp.w_router, inp.w1, inp.w2,
                             inp.w1_shared, inp.w2_shared, inp.bias, None)
         o = run_forward(sub, moe.MoeShape.from_config(cfg, T=hi - lo))
