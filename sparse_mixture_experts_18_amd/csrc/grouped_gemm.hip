@@ -24,6 +24,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
 // work-list construction
@@ -224,12 +225,12 @@ struct GemmArgs {
 // lane -> LDS position map is fixed, so each lane fetches the chunk that
 // belongs at its position.
 // ---------------------------------------------------------------------------
-template <int RG_, int CG_, int NTW_, int BK_, int SA_, int SB_>
+template <int RG_, int CG_, int NTW_, int BK_, int SA_, int SB_, int MSW_ = 4, int LDS_KIB_ = 160>
 struct GCfg {
   static constexpr int RG = RG_, CG = CG_, NTW = NTW_, BK = BK_;
   static constexpr int SA = SA_, SB = SB_;      // LDS ring depth of A and of B
   static constexpr int WAVES = RG * CG, THREADS = WAVES * 64;
-  static constexpr int MSW = 4;               // max 32-row sub-tiles per wave
+  static constexpr int MSW = MSW_;            // max 32-row sub-tiles per wave
   static constexpr int BM = RG * MSW * 32;    // rows per work item
   static constexpr int BNW = CG * NTW * 32;   // weight rows per work item
   static constexpr int ROWB = BK * 2;         // bytes per LDS row
@@ -238,8 +239,10 @@ struct GCfg {
   static constexpr int DROWS = 1024 / ROWB;   // rows per wave DMA instruction
   static constexpr int A_BYTES = BM * ROWB, B_BYTES = BNW * ROWB;
   static constexpr int A_LOADS = A_BYTES / 1024 / WAVES, B_LOADS = B_BYTES / 1024 / WAVES;
-  // the whole 160 KiB: items with few rows use it for deeper rings
-  static constexpr int LDS_BYTES = 160 * 1024;
+  // LDS per block; items with few rows use it for deeper rings.  160 KiB is
+  // the whole CU (one block per CU); 80 KiB lets two blocks share a CU.
+  static constexpr int LDS_BYTES = LDS_KIB_ * 1024;
+  static constexpr int BLOCKS_PER_CU = 160 / LDS_KIB_;
   static_assert(A_LOADS * 1024 * WAVES == A_BYTES && B_LOADS * 1024 * WAVES == B_BYTES, "");
   static_assert(SA * A_BYTES + SB * B_BYTES <= LDS_BYTES, "LDS");
   static_assert(SB >= SA && SA >= 2 && SB <= SA + 1, "B runs at most one slice ahead of A");
@@ -254,6 +257,27 @@ struct GCfg {
 #endif
 using Cfg1 = GCfg<MOE_GEMM1_CFG>;
 using Cfg2 = GCfg<MOE_GEMM2_CFG>;
+// Layers with few rows per expert (decode batches) stream the weights with
+// short items: one 32-row sub-tile per wave, half the LDS, two blocks per CU.
+// The weight slabs of the touched experts then spread over every CU instead
+// of leaving most CUs idle behind the few that hold a second item.  The k
+// order of every output is the same as with the wide tiles, so the choice
+// never changes a result.
+#ifndef MOE_GEMM1_SMALL_CFG
+#define MOE_GEMM1_SMALL_CFG 2, 4, 2, 64, 2, 2, 1, 80
+#endif
+#ifndef MOE_GEMM2_SMALL_CFG
+#define MOE_GEMM2_SMALL_CFG 2, 4, 2, 64, 2, 2, 1, 80
+#endif
+using Cfg1n = GCfg<MOE_GEMM1_SMALL_CFG>;
+using Cfg2n = GCfg<MOE_GEMM2_SMALL_CFG>;
+static_assert(Cfg1n::BK == Cfg1::BK && Cfg2n::BK == Cfg2::BK, "same k slicing");
+
+// mean rows per expert at or below which the small-row tiles are used
+#ifndef MOE_SMALL_ROWS
+#define MOE_SMALL_ROWS 64
+#endif
+constexpr int kNarrowRows = MOE_SMALL_ROWS;
 
 typedef __attribute__((address_space(1))) void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
@@ -414,45 +438,54 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& g, const WorkItem
       const int cur = ks & 1;
       if (ks + 1 < C::BK / 16)
         load_frags<C, MS>(As, Bs, a_row, b_row, fh, ks + 1, af[cur ^ 1], bf[cur ^ 1]);
+      // weight fragment first: the accumulator holds the tile transposed
 #pragma unroll
       for (int i = 0; i < MS - 1; ++i)
 #pragma unroll
         for (int j = 0; j < NT; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bf[cur][j], acc[i][j],
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[cur][j], af[cur][i], acc[i][j],
                                                               0, 0, 0);
       if (last) {
 #pragma unroll
         for (int j = 0; j < NT; ++j)
           acc[MS - 1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              af[cur][MS - 1], bf[cur][j], acc[MS - 1][j], 0, 0, 0);
+              bf[cur][j], af[cur][MS - 1], acc[MS - 1][j], 0, 0, 0);
       }
     }
   }
 
-  // epilogue.  32x32 accumulator layout: column = lane & 31,
-  // row = 8*(r/4) + 4*(lane/32) + r%4 for register r.
+  // epilogue.  32x32 accumulator layout of the transposed tile: lane l holds
+  // token row l & 31 of the sub-tile; register r holds output column
+  // 8*(r/4) + 4*(l/32) + r%4 of the 32-column weight tile, so each group of
+  // four registers is four consecutive columns: one 8-byte store.
+  constexpr int OT = GATED ? HT : NT;  // output tiles per wave
 #pragma unroll
   for (int i = 0; i < MS; ++i) {
     if (i == MS - 1 && !last) continue;
+    const int row = (i * C::RG + rg) * 32 + fr;
+    if (row >= it.nrows) continue;
+    bf16_t* crow = Cm + (size_t)(it.row0 + row) * Nout;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = (i * C::RG + rg) * 32 + 8 * (r >> 2) + 4 * fh + (r & 3);
-      if (row >= it.nrows) continue;
-      bf16_t* crow = Cm + (size_t)(it.row0 + row) * Nout;
-      if (GATED) {
+    for (int j = 0; j < OT; ++j) {
+      const int c0 = n0 + (cg * OT + j) * 32;  // Nout is a multiple of 32
+      if (c0 >= Nout) continue;
 #pragma unroll
-        for (int j = 0; j < HT; ++j) {
-          const int col = n0 + (cg * HT + j) * 32 + fr;
-          const float gv = acc[i][j][r], uv = acc[i][j + HT][r];
-          const float hv = gv / (1.0f + expf(-gv)) * uv;
-          if (col < Nout) crow[col] = f32_to_bf16(hv);
+      for (int q = 0; q < 4; ++q) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float gv = acc[i][j][4 * q + e];
+          if (GATED) {
+            const float uv = acc[i][j + HT][4 * q + e];
+            v[e] = gv / (1.0f + expf(-gv)) * uv;
+          } else {
+            v[e] = gv;
+          }
         }
-      } else {
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          const int col = n0 + (cg * NT + j) * 32 + fr;
-          if (col < Nout) crow[col] = f32_to_bf16(acc[i][j][r]);
-        }
+        u32x2_t pk;
+        pk[0] = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+        pk[1] = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        *reinterpret_cast<u32x2_t*>(crow + c0 + 8 * q + 4 * fh) = pk;
       }
     }
   }
@@ -469,203 +502,23 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& g, const WorkItem
 #define MOE_PERSISTENT 1
 #endif
 
-// Variant main loop: operands go global -> registers -> LDS.  Two register
-// sets hold the two slices in flight (loads are issued two slices ahead), and
-// the LDS double buffer holds the slice being multiplied and the next one.
-// Thread t moves 16-byte chunks t + THREADS*j of the row-major slice (row =
-// chunk / CPR), writing chunk c of row r at LDS position c ^ swz(r).
-template <bool GATED, class C, int MS>
-__device__ __forceinline__ void gemm_bf16_body_rp(const GemmArgs& g, const WorkItem& it,
-                                                  unsigned char* lds, int msub) {
-  const bool shared = it.seg == g.N;
-  const int K = shared ? g.K_s : g.K_r;
-  const int Nout = shared ? g.Nout_s : g.Nout_r;
-  const bf16_t* A = shared ? g.a_shared : g.a_routed;
-  const bf16_t* B = shared ? g.b_shared : g.b_routed + (long long)it.seg * g.b_stride;
-  bf16_t* Cm = shared ? g.c_shared : g.c_routed;
-  const int n0 = it.nt * (GATED ? C::BNW / 2 : C::BNW);
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rg = w / C::CG, cg = w % C::CG;
-  const bool last = (MS - 1) * C::RG + rg < msub;
-
-  constexpr int ROWS_A = C::RG * MS * 32;
-  constexpr int RPT = C::THREADS / C::CPR;                 // rows per thread round
-  constexpr int AL = ROWS_A * C::CPR / C::THREADS, BL = C::BNW * C::CPR / C::THREADS;
-  static_assert(AL * C::THREADS == ROWS_A * C::CPR && BL * C::THREADS == C::BNW * C::CPR, "");
-  constexpr int STAGE = C::A_BYTES + C::B_BYTES;
-  static_assert(2 * STAGE <= C::LDS_BYTES, "LDS double buffer");
-  const int trow = tid / C::CPR, tch = tid % C::CPR;
-  uint32_t a_off[AL], b_off[BL];
-#pragma unroll
-  for (int j = 0; j < AL; ++j) {
-    const int tr = trow + RPT * j;
-    int src = it.row0 + min(tr, it.nrows - 1);
-    if (g.perm && !shared) src = g.perm[src] / g.k;
-    a_off[j] = (uint32_t)src * (uint32_t)K + tch * 8;
-  }
-#pragma unroll
-  for (int j = 0; j < BL; ++j) {
-    const int r = trow + RPT * j;
-    int wrow;
-    if (GATED)
-      wrow = r < C::BNW / 2 ? min(n0 + r, Nout - 1) : Nout + min(n0 + r - C::BNW / 2, Nout - 1);
-    else
-      wrow = min(n0 + r, Nout - 1);
-    b_off[j] = (uint32_t)wrow * (uint32_t)K + tch * 8;
-  }
-  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-  u32x4_t ra0[AL], rb0[BL], ra1[AL], rb1[BL];
-  const int nk = K / C::BK;
-#define MOE_RP_LOAD(RA, RB, KT)                                                              \
-  do {                                                                                       \
-    const int k0_ = (KT) * C::BK;                                                            \
-    _Pragma("unroll") for (int j = 0; j < AL; ++j) RA[j] =                                   \
-        *reinterpret_cast<const u32x4_t*>(A + a_off[j] + k0_);                               \
-    _Pragma("unroll") for (int j = 0; j < BL; ++j) RB[j] =                                   \
-        *reinterpret_cast<const u32x4_t*>(B + b_off[j] + k0_);                               \
-  } while (0)
-#define MOE_RP_STORE(RA, RB, BUF)                                                            \
-  do {                                                                                       \
-    unsigned char* st_ = lds + (BUF) * STAGE;                                                \
-    _Pragma("unroll") for (int j = 0; j < AL; ++j) {                                         \
-      const int r_ = trow + RPT * j;                                                         \
-      *reinterpret_cast<u32x4_t*>(st_ + r_ * C::ROWB + ((tch ^ C::swz(r_)) << 4)) = RA[j];   \
-    }                                                                                        \
-    _Pragma("unroll") for (int j = 0; j < BL; ++j) {                                         \
-      const int r_ = trow + RPT * j;                                                         \
-      *reinterpret_cast<u32x4_t*>(st_ + C::A_BYTES + r_ * C::ROWB +                          \
-                                  ((tch ^ C::swz(r_)) << 4)) = RB[j];                        \
-    }                                                                                        \
-  } while (0)
-
-  constexpr int NT = C::NTW, HT = NT / 2;
-  f32x16_t acc[MS][NT];
-#pragma unroll
-  for (int i = 0; i < MS; ++i)
-#pragma unroll
-    for (int j = 0; j < NT; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  const int fr = lane & 31, fh = lane >> 5;
-  int a_row[MS], b_row[NT];
-#pragma unroll
-  for (int i = 0; i < MS; ++i) a_row[i] = (i * C::RG + rg) * 32 + fr;
-#pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    if (GATED)
-      b_row[j] = (j < HT ? 0 : C::BNW / 2) + (cg * HT + (j % HT)) * 32 + fr;
-    else
-      b_row[j] = (cg * NT + j) * 32 + fr;
-  }
-  auto compute = [&](int buf) {
-    const unsigned char* As = lds + buf * STAGE;
-    const unsigned char* Bs = As + C::A_BYTES;
-#pragma unroll
-    for (int ks = 0; ks < C::BK / 16; ++ks) {
-      bf16x8_t bf[NT], af[MS];
-      load_frags<C, MS>(As, Bs, a_row, b_row, fh, ks, af, bf);
-#pragma unroll
-      for (int i = 0; i < MS - 1; ++i)
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
-      if (last) {
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-          acc[MS - 1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[MS - 1], bf[j],
-                                                                   acc[MS - 1][j], 0, 0, 0);
-      }
-    }
-  };
-  constexpr int LPS = AL + BL;  // loads per slice per thread
-
-  // prologue: slices 0 and 1 in flight, slice 0 into LDS buffer 0
-  MOE_RP_LOAD(ra0, rb0, 0);
-  if (nk > 1) MOE_RP_LOAD(ra1, rb1, 1);
-  if (nk > 1) wait_vm<LPS>();
-  else wait_vm<0>();
-  MOE_RP_STORE(ra0, rb0, 0);
-  if (nk > 2) MOE_RP_LOAD(ra0, rb0, 2);
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
-  __builtin_amdgcn_s_barrier();
-  // iteration kt: multiply slice kt (LDS kt%2); slice kt+1 (registers
-  // (kt+1)%2) goes to LDS (kt+1)%2, whose previous slice kt-1 every wave has
-  // finished; its register set then takes slice kt+3
-  for (int kt = 0; kt < nk; kt += 2) {
-    compute(0);
-    if (kt + 1 < nk) {
-      if (kt + 2 < nk) wait_vm<LPS>();
-      else wait_vm<0>();
-      MOE_RP_STORE(ra1, rb1, 1);
-      if (kt + 3 < nk) MOE_RP_LOAD(ra1, rb1, kt + 3);
-      __builtin_amdgcn_s_waitcnt(0xc07f);
-      __builtin_amdgcn_s_barrier();
-      compute(1);
-      if (kt + 2 < nk) {
-        if (kt + 3 < nk) wait_vm<LPS>();
-        else wait_vm<0>();
-        MOE_RP_STORE(ra0, rb0, 0);
-        if (kt + 4 < nk) MOE_RP_LOAD(ra0, rb0, kt + 4);
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        __builtin_amdgcn_s_barrier();
-      }
-    }
-  }
-#undef MOE_RP_LOAD
-#undef MOE_RP_STORE
-
-#pragma unroll
-  for (int i = 0; i < MS; ++i) {
-    if (i == MS - 1 && !last) continue;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = (i * C::RG + rg) * 32 + 8 * (r >> 2) + 4 * fh + (r & 3);
-      if (row >= it.nrows) continue;
-      bf16_t* crow = Cm + (size_t)(it.row0 + row) * Nout;
-      if (GATED) {
-#pragma unroll
-        for (int j = 0; j < HT; ++j) {
-          const int col = n0 + (cg * HT + j) * 32 + fr;
-          const float gv = acc[i][j][r], uv = acc[i][j + HT][r];
-          const float hv = gv / (1.0f + expf(-gv)) * uv;
-          if (col < Nout) crow[col] = f32_to_bf16(hv);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          const int col = n0 + (cg * NT + j) * 32 + fr;
-          if (col < Nout) crow[col] = f32_to_bf16(acc[i][j][r]);
-        }
-      }
-    }
-  }
-}
-
-#ifndef MOE_GEMM_RP
-#define MOE_GEMM_RP 0
-#endif
-#if MOE_GEMM_RP
-#define MOE_GEMM_BODY gemm_bf16_body_rp
-#else
-#define MOE_GEMM_BODY gemm_bf16_body
-#endif
 
 template <bool GATED, class C>
 __device__ __forceinline__ void gemm_bf16_item(const GemmArgs& g, int item, unsigned char* lds) {
   const WorkItem it = g.items[item];
   const int msub = (it.nrows + 31) >> 5;  // live 32-row sub-tiles
-  switch ((msub + C::RG - 1) / C::RG) {   // sub-tiles of the busiest wave
-    case 1: MOE_GEMM_BODY<GATED, C, 1>(g, it, lds, msub); break;
-    case 2: MOE_GEMM_BODY<GATED, C, 2>(g, it, lds, msub); break;
-    case 3: MOE_GEMM_BODY<GATED, C, 3>(g, it, lds, msub); break;
-    default: MOE_GEMM_BODY<GATED, C, 4>(g, it, lds, msub); break;
-  }
+  const int ms = (msub + C::RG - 1) / C::RG;  // sub-tiles of the busiest wave
+  constexpr int M2 = C::MSW < 2 ? C::MSW : 2, M3 = C::MSW < 3 ? C::MSW : 3;
+  if (ms <= 1) gemm_bf16_body<GATED, C, 1>(g, it, lds, msub);
+  else if (ms <= 2) gemm_bf16_body<GATED, C, M2>(g, it, lds, msub);
+  else if (ms <= 3) gemm_bf16_body<GATED, C, M3>(g, it, lds, msub);
+  else gemm_bf16_body<GATED, C, C::MSW>(g, it, lds, msub);
 }
 
 template <bool GATED, class C>
-__global__ __launch_bounds__(C::THREADS) void gemm_bf16_kernel(GemmArgs g) {
+__global__ __launch_bounds__(C::THREADS)
+__attribute__((amdgpu_waves_per_eu(C::WAVES * C::BLOCKS_PER_CU / 4))) void gemm_bf16_kernel(
+    GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds[C::LDS_BYTES];
 #if MOE_PERSISTENT
   int& s_item = *reinterpret_cast<int*>(lds);  // LDS is idle between items
@@ -765,8 +618,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgsF g) {
 
 inline int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 
-// one persistent block per compute unit, a multiple of the 8 XCDs
-int persistent_grid() {
+// persistent blocks: per compute unit, a multiple of the 8 XCDs
+int persistent_grid(int per_cu) {
   static int cached[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
@@ -777,7 +630,18 @@ int persistent_grid() {
       cus = 256;
     cached[dev] = (cus + 7) / 8 * 8;
   }
-  return cached[dev];
+  return cached[dev] * per_cu;
+}
+
+template <bool GATED, class C>
+void launch_bf16(const GemmArgs& g, int64_t cap, hipStream_t st) {
+  const int grid = MOE_PERSISTENT ? persistent_grid(C::BLOCKS_PER_CU) : (int)((cap + 7) / 8 * 8);
+  gemm_bf16_kernel<GATED, C><<<grid, C::THREADS, 0, st>>>(g);
+}
+
+bool narrow_tiles(const moe_shape& s) {
+  return s.dtype == MOE_DTYPE_BF16 && s.T * s.top_k <= (long long)kNarrowRows * s.n_experts &&
+         s.d_ff_shared == 0;
 }
 
 struct PlanGeom {
@@ -787,8 +651,11 @@ struct PlanGeom {
 // row-block size and column-tile counts of the two work lists
 PlanGeom plan_geom(const moe_shape& s) {
   const bool bf = s.dtype == MOE_DTYPE_BF16;
-  const int bm1 = bf ? Cfg1::BM : kBMf, bm2 = bf ? Cfg2::BM : kBMf;
-  const int bn1 = bf ? Cfg1::BNW / 2 : kBNf, bn2 = bf ? Cfg2::BNW : kBNf;
+  const bool nar = narrow_tiles(s);
+  const int bm1 = bf ? (nar ? Cfg1n::BM : Cfg1::BM) : kBMf;
+  const int bm2 = bf ? (nar ? Cfg2n::BM : Cfg2::BM) : kBMf;
+  const int bn1 = bf ? (nar ? Cfg1n::BNW : Cfg1::BNW) / 2 : kBNf;
+  const int bn2 = bf ? (nar ? Cfg2n::BNW : Cfg2::BNW) : kBNf;
   const bool sh = s.d_ff_shared > 0;
   return PlanGeom{bm1, bm2, cdiv(s.d_ff, bn1), sh ? cdiv(s.d_ff_shared, bn1) : 0,
                   cdiv(s.d_model, bn2), sh ? cdiv(s.d_model, bn2) : 0};
@@ -817,8 +684,10 @@ hipError_t launch_gemm1(const moe_shape& s, const void* x, const int32_t* perm, 
                 static_cast<const bf16_t*>(w1), static_cast<const bf16_t*>(w1s),
                 static_cast<bf16_t*>(h), static_cast<bf16_t*>(hs), d, d, f, fs,
                 (long long)2 * f * d, N, w.plan1, w.plan1_hdr};
-    const int grid = MOE_PERSISTENT ? persistent_grid() : (int)((w.plan1_cap + 7) / 8 * 8);
-    gemm_bf16_kernel<true, Cfg1><<<grid, Cfg1::THREADS, 0, st>>>(g1);
+    if (narrow_tiles(s))
+      launch_bf16<true, Cfg1n>(g1, w.plan1_cap, st);
+    else
+      launch_bf16<true, Cfg1>(g1, w.plan1_cap, st);
   } else {
     GemmArgsF g1{static_cast<const float*>(x), static_cast<const float*>(x), perm, s.top_k,
                  static_cast<const float*>(w1), static_cast<const float*>(w1s),
@@ -839,8 +708,10 @@ hipError_t launch_gemm2(const moe_shape& s, const void* h, const void* hs, const
                 s.top_k, static_cast<const bf16_t*>(w2), static_cast<const bf16_t*>(w2s),
                 static_cast<bf16_t*>(y_perm), static_cast<bf16_t*>(y_shared), f, fs, d, d,
                 (long long)d * f, N, w.plan2, w.plan2_hdr};
-    const int grid = MOE_PERSISTENT ? persistent_grid() : (int)((w.plan2_cap + 7) / 8 * 8);
-    gemm_bf16_kernel<false, Cfg2><<<grid, Cfg2::THREADS, 0, st>>>(g2);
+    if (narrow_tiles(s))
+      launch_bf16<false, Cfg2n>(g2, w.plan2_cap, st);
+    else
+      launch_bf16<false, Cfg2>(g2, w.plan2_cap, st);
   } else {
     GemmArgsF g2{static_cast<const float*>(h), static_cast<const float*>(hs), nullptr,
                  s.top_k, static_cast<const float*>(w2), static_cast<const float*>(w2s),

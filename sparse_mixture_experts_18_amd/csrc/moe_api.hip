@@ -147,13 +147,16 @@ moe_status moe_route(const moe_shape* shape, const void* x, const float* w_route
   if ((st = check_ws(shape, ws, ws_bytes, w)) != MOE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (scores_in)
-    return hip_status(
-        launch_topk(*shape, scores_in, nullptr, true, bias, scores_out, topk_idx, topk_w, s));
+    return hip_status(launch_topk(*shape, scores_in, 1, nullptr, nullptr, true, bias, scores_out,
+                                  topk_idx, topk_w, s));
   float* logits = logits_out ? logits_out : w.logits;
-  hipError_t e = launch_router_gemm(*shape, x, w_router, logits, w, s);
+  int np = 1;
+  hipError_t e = launch_router_gemm(*shape, x, w_router, logits, w, s, &np);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  return hip_status(
-      launch_topk(*shape, logits, logit_add, false, bias, scores_out, topk_idx, topk_w, s));
+  // a k-split router leaves partial sums; top-k adds them and fills logits_out
+  return hip_status(launch_topk(*shape, np > 1 ? w.router_part : logits, np,
+                                np > 1 ? logits_out : nullptr, logit_add, false, bias,
+                                scores_out, topk_idx, topk_w, s));
 }
 
 moe_status moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, int32_t* counts,
@@ -265,8 +268,10 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_rou
   int32_t* sl = slot ? slot : w.slot;
   int32_t* nk = n_kept_dropped ? n_kept_dropped : w.nkd;
   const bool shared = sh.d_ff_shared > 0;
-  if (launch_router_gemm(sh, x, w_router, w.logits, w, s) != hipSuccess) return MOE_ERR_HIP;
-  if (launch_topk(sh, w.logits, logit_add, false, bias, sc, ti, tw, s) != hipSuccess)
+  int np = 1;
+  if (launch_router_gemm(sh, x, w_router, w.logits, w, s, &np) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_topk(sh, np > 1 ? w.router_part : w.logits, np, nullptr, logit_add, false, bias, sc,
+                  ti, tw, s) != hipSuccess)
     return MOE_ERR_HIP;
   if (launch_dispatch(sh, ti, cn, of, sl, w.perm, nk, w, s) != hipSuccess) return MOE_ERR_HIP;
   if (launch_plan(sh, of, w, s) != hipSuccess) return MOE_ERR_HIP;

@@ -74,10 +74,12 @@ int64_t capacity_of(const moe_shape& s);  // -1 = dropless
 
 // ---- launchers (validated arguments; return hipError_t of the launch) ----
 hipError_t launch_router_gemm(const moe_shape& s, const void* x, const float* w_router,
-                              float* logits, const Workspace& w, hipStream_t st);
-hipError_t launch_topk(const moe_shape& s, const float* logits, const float* logit_add,
-                       bool logits_are_scores, const float* bias, float* scores_out,
-                       int32_t* topk_idx, float* topk_w, hipStream_t st);
+                              float* logits, const Workspace& w, hipStream_t st, int* nparts);
+// logits: x W_r^T (nparts == 1) or nparts k-chunk partial-sum planes [nparts][T][N]
+// to be added in chunk order; logits_out (optional) receives the summed x W_r^T
+hipError_t launch_topk(const moe_shape& s, const float* logits, int nparts, float* logits_out,
+                       const float* logit_add, bool logits_are_scores, const float* bias,
+                       float* scores_out, int32_t* topk_idx, float* topk_w, hipStream_t st);
 hipError_t launch_dispatch(const moe_shape& s, const int32_t* topk_idx, int32_t* counts,
                            int32_t* offsets, int32_t* slot, int32_t* perm, int32_t* nkd,
                            const Workspace& w, hipStream_t st);

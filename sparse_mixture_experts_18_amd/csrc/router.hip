@@ -122,7 +122,7 @@ __device__ __forceinline__ int rswz(int r) { return (r >> 1) & 7; }
 // start from zero, are summed smallest first, and the chunk results are added
 // in chunk order.  A block either walks all chunks (out = logits) or, for
 // small batches, one chunk (out = partials [chunk][T][N], summed in chunk order
-// by router_reduce_kernel): the same fp32 operations in the same order either
+// by the top-k kernel as it reads them): the same fp32 operations in the same order either
 // way, so the logits of a token never depend on the batch size.
 constexpr int RM_KC = 512;
 
@@ -207,16 +207,6 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const bf16_t* __restri
   }
 }
 
-__global__ __launch_bounds__(256) void router_reduce_kernel(const float* __restrict__ part,
-                                                            float* __restrict__ logits,
-                                                            long long n, int nkc) {
-  for (long long i = blockIdx.x * 256LL + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
-    float v = part[i];
-    for (int c = 1; c < nkc; ++c) v += part[(size_t)c * n + i];
-    logits[i] = v;
-  }
-}
-
 // ---------------------------------------------------------------------------
 // K2: one wavefront per token.  Lane l holds experts [l*P, l*P+P).
 // ---------------------------------------------------------------------------
@@ -256,7 +246,8 @@ constexpr int TK_WAVES = 4;
 
 template <int P>
 __global__ __launch_bounds__(256) void topk_kernel(
-    const float* __restrict__ logits, const float* __restrict__ logit_add,
+    const float* __restrict__ logits, int nparts, float* __restrict__ logits_out,
+    const float* __restrict__ logit_add,
     int logits_are_scores, const float* __restrict__ bias, float* __restrict__ scores_out,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int T, int N, int k,
     int score_fn, int renorm, int n_groups, int topk_groups) {
@@ -276,6 +267,10 @@ __global__ __launch_bounds__(256) void topk_kernel(
     float v = -INFINITY;
     if (e < N) {
       v = lrow[e];
+      // partial sums of a k-split router GEMM: added in chunk order, the
+      // order a single pass over the chunks uses
+      for (int c = 1; c < nparts; ++c) v += lrow[(size_t)c * T * N + e];
+      if (logits_out && valid) logits_out[(size_t)t * N + e] = v;
       if (logit_add && !logits_are_scores) v += logit_add[(size_t)t * N + e];
     }
     s[p] = v;
@@ -405,9 +400,13 @@ int router_split_chunks(const moe_shape& s) {
   return (blocks < 128 && nkc > 1) ? nkc : 0;
 }
 
+// writes x W_r^T to `logits`, or, when the k-split is taken, its per-chunk
+// partial sums to the workspace (launch_topk adds them up); returns the number
+// of partial-sum planes that launch_topk must read (1: `logits` holds sums)
 hipError_t launch_router_gemm(const moe_shape& s, const void* x, const float* w_router,
-                              float* logits, const Workspace& w, hipStream_t st) {
+                              float* logits, const Workspace& w, hipStream_t st, int* nparts) {
   const int T = (int)s.T, N = s.n_experts, d = s.d_model;
+  *nparts = 1;
   if (s.dtype == MOE_DTYPE_BF16) {
     const long long n = (long long)N * d;
     split3_kernel<<<(int)min((n + 255) / 256, 2048LL), 256, 0, st>>>(w_router, w.wsplit, n);
@@ -416,9 +415,7 @@ hipError_t launch_router_gemm(const moe_shape& s, const void* x, const float* w_
       dim3 grid((T + RM_BM - 1) / RM_BM, (N + RM_BN - 1) / RM_BN, nkc);
       router_mfma_kernel<<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(x), w.wsplit,
                                                w.router_part, T, N, d, 1);
-      const long long tn = (long long)T * N;
-      router_reduce_kernel<<<(int)min((tn + 255) / 256, 4096LL), 256, 0, st>>>(
-          w.router_part, logits, tn, nkc);
+      *nparts = nkc;
     } else {
       dim3 grid((T + RM_BM - 1) / RM_BM, (N + RM_BN - 1) / RM_BN, 1);
       router_mfma_kernel<<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(x), w.wsplit, logits,
@@ -432,14 +429,15 @@ hipError_t launch_router_gemm(const moe_shape& s, const void* x, const float* w_
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const moe_shape& s, const float* logits, const float* logit_add,
-                       bool logits_are_scores, const float* bias, float* scores_out,
-                       int32_t* topk_idx, float* topk_w, hipStream_t st) {
+hipError_t launch_topk(const moe_shape& s, const float* logits, int nparts, float* logits_out,
+                       const float* logit_add, bool logits_are_scores, const float* bias,
+                       float* scores_out, int32_t* topk_idx, float* topk_w, hipStream_t st) {
   const int T = (int)s.T, N = s.n_experts;
   dim3 grid((T + TK_WAVES - 1) / TK_WAVES);
   const int P = (N + 63) / 64;
 #define MOE_TOPK(PP)                                                                        \
-  topk_kernel<PP><<<grid, 256, 0, st>>>(logits, logit_add, logits_are_scores ? 1 : 0, bias, \
+  topk_kernel<PP><<<grid, 256, 0, st>>>(logits, nparts, logits_out, logit_add,             \
+                                        logits_are_scores ? 1 : 0, bias,                   \
                                         scores_out, topk_idx, topk_w, T, N, s.top_k,       \
                                         s.score_fn, s.renormalize, s.n_groups, s.topk_groups)
   if (P <= 1) MOE_TOPK(1);

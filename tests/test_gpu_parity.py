@@ -232,16 +232,19 @@ def test_determinism_bitwise():
         assert torch.equal(a[k], b[k]), k
 
 
-def test_batch_invariance_dropless():
-    """A token's scores, choice and gates do not depend on the batch it is in
-    (batch of 1, of 64 and a batch of 4096, which runs the router GEMM without
-    the small-batch k split)."""
-    cfg = W.CONFIGS["dsv3"]
+@pytest.mark.parametrize("name", ["dsv3", "decode"])
+def test_batch_invariance_dropless(name):
+    """A token's scores, choice, gates and output do not depend on the batch it
+    is in (batch of 1, of 64 and of 4096: the large batch runs the router GEMM
+    without the small-batch k split, and for the decode layer the expert GEMMs
+    with the wide tiles instead of the small-row tiles)."""
+    cfg = W.CONFIGS[name]
     inp = W.make_inputs(cfg, seed=4, device="cuda", T=4096)
     full = run_forward(inp)
     for lo, hi in [(0, 1), (100, 164), (4095, 4096)]:
+        la = None if inp.logit_add is None else inp.logit_add[lo:hi].contiguous()
         sub = W.LayerInputs(cfg, inp.x[lo:hi].contiguous(), inp.w_router, inp.w1, inp.w2,
-                            inp.w1_shared, inp.w2_shared, inp.bias, None)
+                            inp.w1_shared, inp.w2_shared, inp.bias, la)
         o = run_forward(sub, moe.MoeShape.from_config(cfg, T=hi - lo))
         for key in ["scores", "topk_idx", "topk_w"]:
             assert torch.equal(o[key], full[key][lo:hi]), (key, lo, hi)
