@@ -40,6 +40,11 @@
  *     256-byte aligned.  Entry points that take a workspace use disjoint
  *     regions of the same layout, so one workspace serves every call of one
  *     shape; two calls sharing a workspace must not overlap in time.
+ *   - Activation and weight pointers (x, w_router, w1, w2, w1_shared,
+ *     w2_shared, h, h_shared, y_perm, y_shared, y) must be 16-byte aligned,
+ *     the fp32/int32 arrays 4-byte aligned (any fresh hipMalloc or PyTorch
+ *     allocation is); a misaligned pointer is rejected with MOE_ERR_INVALID
+ *     before anything is enqueued.
  *   - `stream` is a hipStream_t (NULL = default stream).  Every call only
  *     enqueues work; it returns before the GPU finishes.  Outputs are valid
  *     once the stream is synchronised.  No call synchronises the host.
@@ -159,8 +164,20 @@ moe_status moe_dispatch(const moe_shape* shape, const int32_t* topk_idx,
                         int32_t* perm, int32_t* n_kept_dropped, void* ws,
                         size_t ws_bytes, void* stream);
 
+/* Work lists of the two expert projections for the segments in `offsets`
+ * (from moe_dispatch), written to the workspace: each expert segment is cut
+ * into near-equal row blocks, each row block into weight-column tiles, and
+ * the list into eight ranges of equal estimated cost, one per XCD.  The
+ * moe_expert_* calls build these lists themselves when given offsets; given
+ * offsets = NULL they reuse the lists already in `ws`, which must then come
+ * from an earlier moe_expert_plan or moe_expert_* call with the same shape,
+ * workspace and segments, ordered before it on the stream. */
+moe_status moe_expert_plan(const moe_shape* shape, const int32_t* offsets,
+                           void* ws, size_t ws_bytes, void* stream);
+
 /* Expert FFNs over the dispatched rows (one grouped launch per projection).
- * x [T,d]; perm, offsets from moe_dispatch; w1, w2 routed weights;
+ * x [T,d]; perm, offsets from moe_dispatch (offsets NULL: reuse the work
+ * lists in ws, see moe_expert_plan); w1, w2 routed weights;
  * w1_shared/w2_shared required iff d_ff_shared > 0.  Outputs: y_perm
  * [T*k, d] dtype, row s = E_e(x_t) for the kept assignment perm[s]
  * (rows >= R untouched); y_shared [T,d] dtype = S(x_t) (required iff
@@ -177,7 +194,8 @@ moe_status moe_expert_ffn(const moe_shape* shape, const void* x,
  * (t = perm[s] / k, e its expert), h [T*k, d_ff] dtype (rows >= R untouched),
  * and h_shared [T, d_ff_shared] for the shared expert (required iff
  * d_ff_shared > 0).  down: y_perm[s] = h[s] W2_e^T, y_shared = h_shared
- * W2s^T.  offsets as produced by moe_dispatch; all pointers device memory.
+ * W2s^T.  offsets as produced by moe_dispatch, or NULL to reuse the work
+ * lists in ws (see moe_expert_plan); all pointers device memory.
  * Source: "MoE architecture in practice", expert-parallelism section (one
  * grouped GEMM over the contiguous expert segments); the SwiGLU expert. */
 moe_status moe_expert_gate_up(const moe_shape* shape, const void* x,

@@ -8,7 +8,7 @@ fallback: if the library is missing or fails to load, every call raises.
 The functions mirror the C ABI in include/moe.h one to one (same names, same
 argument order, tensors in place of pointers):
 
-    moe_route, moe_dispatch, moe_expert_ffn, moe_expert_gate_up,
+    moe_route, moe_dispatch, moe_expert_plan, moe_expert_ffn, moe_expert_gate_up,
     moe_expert_down, moe_combine, moe_bias_update, moe_forward,
     moe_workspace_bytes, moe_check_shape, moe_capacity, moe_status_string,
     moe_abi_version
@@ -101,6 +101,7 @@ _SIGS = {
     "moe_workspace_bytes": (ctypes.c_size_t, [_S]),
     "moe_route": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_dispatch": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_expert_plan": (ctypes.c_int, [_S, _P, _P, ctypes.c_size_t, _P]),
     "moe_expert_ffn": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                       ctypes.c_size_t, _P]),
     "moe_expert_gate_up": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -229,6 +230,14 @@ def moe_dispatch(shape, topk_idx, counts, offsets, slot, perm, n_kept_dropped, w
         _ptr(slot, "slot", torch.int32, T * k), _ptr(perm, "perm", torch.int32, T * k),
         _ptr(n_kept_dropped, "n_kept_dropped", torch.int32, 2), p, n, _stream(stream))
     _check(st, "moe_dispatch")
+
+
+def moe_expert_plan(shape, offsets, ws, stream=None):
+    p, n = _ws(ws)
+    st = lib().moe_expert_plan(ctypes.byref(shape),
+                               _ptr(offsets, "offsets", torch.int32, shape.n_experts + 1),
+                               p, n, _stream(stream))
+    _check(st, "moe_expert_plan")
 
 
 def moe_expert_ffn(shape, x, perm, offsets, w1, w2, w1_shared, w2_shared, y_perm, y_shared,

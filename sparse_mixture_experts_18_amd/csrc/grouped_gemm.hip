@@ -58,7 +58,7 @@ __device__ __forceinline__ void block_exclusive_scan2(int* sh0, int* sh1, int v0
 
 // Work-list header (int32): [0] item count, [1..9] XCD range starts
 // (xcd x owns items [hdr[1+x], hdr[2+x])), [16..23] per-XCD item counters.
-constexpr int kHdrStart = 1, kHdrCtr = 16;  // header: 32 ints
+constexpr int kHdrStart = 1, kHdrCtr = 16, kHdrDone = 24;  // header: 32 ints
 
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int N,
                                                     int T, int has_shared, int bm1, int bm2,
@@ -160,6 +160,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
       hdr[kHdrStart] = 0;
       hdr[kHdrStart + 8] = tot;
       for (int x = 0; x < 8; ++x) hdr[kHdrCtr + x] = 0;
+      hdr[kHdrDone] = 0;
       if (total == 0)
         for (int x = 1; x < 8; ++x) hdr[kHdrStart + x] = 0;
     }
@@ -426,8 +427,6 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& g, const WorkItem
     // every wave's part of slice kt is now in LDS, and every wave is done
     // with slice kt-1, whose buffers the next loads overwrite
     __builtin_amdgcn_s_barrier();
-    if (kt + SA - 1 < nk) issue_a(kt + SA - 1);
-    if (kt + SB - 1 < nk) issue_b(kt + SB - 1);
     const unsigned char* As = Abuf + (kt % SA) * A_SL;
     const unsigned char* Bs = Bbuf + (kt % SB) * C::B_BYTES;
     // fragments of k-step ks+1 are read while the MFMAs of k-step ks run
@@ -436,6 +435,11 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& g, const WorkItem
 #pragma unroll
     for (int ks = 0; ks < C::BK / 16; ++ks) {
       const int cur = ks & 1;
+      // refill the buffers of slice kt-1: A behind the first fragment reads,
+      // B one k-step later, so the reads of k-step 0 are not queued behind
+      // a burst of loads
+      if (ks == 0 && kt + SA - 1 < nk) issue_a(kt + SA - 1);
+      if (ks == 1 && kt + SB - 1 < nk) issue_b(kt + SB - 1);
       if (ks + 1 < C::BK / 16)
         load_frags<C, MS>(As, Bs, a_row, b_row, fh, ks + 1, af[cur ^ 1], bf[cur ^ 1]);
       // weight fragment first: the accumulator holds the tile transposed
@@ -531,6 +535,13 @@ __attribute__((amdgpu_waves_per_eu(C::WAVES * C::BLOCKS_PER_CU / 4))) void gemm_
     __syncthreads();
     if (item >= end) break;
     gemm_bf16_item<GATED, C>(g, item, lds);
+  }
+  // the last block out re-arms the item counters, so the same work list can
+  // be launched again without rebuilding it (every other block has already
+  // drawn its final item)
+  if (threadIdx.x == 0 && atomicAdd(&g.hdr[kHdrDone], 1) == (int)gridDim.x - 1) {
+    for (int i = 0; i < 8; ++i) atomicExch(&g.hdr[kHdrCtr + i], 0);
+    atomicExch(&g.hdr[kHdrDone], 0);
   }
 #else
   const int item = xcd_item(g.hdr[0]);

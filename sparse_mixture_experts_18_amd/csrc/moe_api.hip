@@ -1,6 +1,8 @@
 // C ABI entry points: argument validation, workspace layout, launch order.
 #include <math.h>
 
+#include <initializer_list>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -42,6 +44,16 @@ moe_status check_shape(const moe_shape* s) {
 }
 
 inline moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// every pointer given (non-NULL) is aligned to `a` bytes: activation and
+// weight rows move in 16-byte vectors, the fp32/int32 arrays element-wise
+inline bool aligned(uintptr_t a, std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p && (reinterpret_cast<uintptr_t>(p) & (a - 1))) return false;
+  return true;
+}
+inline bool aligned16(std::initializer_list<const void*> ps) { return aligned(16, ps); }
+inline bool aligned4(std::initializer_list<const void*> ps) { return aligned(4, ps); }
 
 }  // namespace
 
@@ -143,6 +155,9 @@ moe_status moe_route(const moe_shape* shape, const void* x, const float* w_route
   if (st != MOE_OK) return st;
   if (!topk_idx || !topk_w) return MOE_ERR_INVALID;
   if (!scores_in && (!x || !w_router)) return MOE_ERR_INVALID;
+  if (!aligned16({x, w_router}) ||
+      !aligned4({logit_add, scores_in, bias, logits_out, scores_out, topk_idx, topk_w}))
+    return MOE_ERR_INVALID;
   Workspace w;
   if ((st = check_ws(shape, ws, ws_bytes, w)) != MOE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -166,10 +181,22 @@ moe_status moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, int32_t
   if (st != MOE_OK) return st;
   if (!topk_idx || !counts || !offsets || !slot || !perm || !n_kept_dropped)
     return MOE_ERR_INVALID;
+  if (!aligned4({topk_idx, counts, offsets, slot, perm, n_kept_dropped})) return MOE_ERR_INVALID;
   Workspace w;
   if ((st = check_ws(shape, ws, ws_bytes, w)) != MOE_OK) return st;
   return hip_status(launch_dispatch(*shape, topk_idx, counts, offsets, slot, perm,
                                     n_kept_dropped, w, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_expert_plan(const moe_shape* shape, const int32_t* offsets, void* ws,
+                           size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!offsets) return MOE_ERR_INVALID;
+  if (!aligned4({offsets})) return MOE_ERR_INVALID;
+  Workspace w;
+  if ((st = check_ws(shape, ws, ws_bytes, w)) != MOE_OK) return st;
+  return hip_status(launch_plan(*shape, offsets, w, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_expert_ffn(const moe_shape* shape, const void* x, const int32_t* perm,
@@ -178,13 +205,16 @@ moe_status moe_expert_ffn(const moe_shape* shape, const void* x, const int32_t* 
                           void* y_shared, void* ws, size_t ws_bytes, void* stream) {
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
-  if (!x || !perm || !offsets || !w1 || !w2 || !y_perm) return MOE_ERR_INVALID;
+  if (!x || !perm || !w1 || !w2 || !y_perm) return MOE_ERR_INVALID;
   if (shape->d_ff_shared > 0 && (!w1_shared || !w2_shared || !y_shared)) return MOE_ERR_INVALID;
+  if (!aligned16({x, w1, w2, w1_shared, w2_shared, y_perm, y_shared}) ||
+      !aligned4({perm, offsets}))
+    return MOE_ERR_INVALID;
   Workspace w;
   if ((st = check_ws(shape, ws, ws_bytes, w)) != MOE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool sh = shape->d_ff_shared > 0;
-  if (launch_plan(*shape, offsets, w, s) != hipSuccess) return MOE_ERR_HIP;
+  if (offsets && launch_plan(*shape, offsets, w, s) != hipSuccess) return MOE_ERR_HIP;
   if (launch_gemm1(*shape, x, perm, w1, w1_shared, w.h, w.h_shared, w, s) != hipSuccess)
     return MOE_ERR_HIP;
   return hip_status(launch_gemm2(*shape, w.h, w.h_shared, w2, w2_shared, y_perm,
@@ -197,12 +227,14 @@ moe_status moe_expert_gate_up(const moe_shape* shape, const void* x, const int32
                               void* stream) {
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
-  if (!x || !perm || !offsets || !w1 || !h) return MOE_ERR_INVALID;
+  if (!x || !perm || !w1 || !h) return MOE_ERR_INVALID;
   if (shape->d_ff_shared > 0 && (!w1_shared || !h_shared)) return MOE_ERR_INVALID;
+  if (!aligned16({x, w1, w1_shared, h, h_shared}) || !aligned4({perm, offsets}))
+    return MOE_ERR_INVALID;
   Workspace w;
   if ((st = check_ws(shape, ws, ws_bytes, w)) != MOE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (launch_plan(*shape, offsets, w, s) != hipSuccess) return MOE_ERR_HIP;
+  if (offsets && launch_plan(*shape, offsets, w, s) != hipSuccess) return MOE_ERR_HIP;
   return hip_status(launch_gemm1(*shape, x, perm, w1, w1_shared, h,
                                  shape->d_ff_shared > 0 ? h_shared : nullptr, w, s));
 }
@@ -213,12 +245,14 @@ moe_status moe_expert_down(const moe_shape* shape, const void* h, const void* h_
                            void* stream) {
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
-  if (!h || !offsets || !w2 || !y_perm) return MOE_ERR_INVALID;
+  if (!h || !w2 || !y_perm) return MOE_ERR_INVALID;
   if (shape->d_ff_shared > 0 && (!h_shared || !w2_shared || !y_shared)) return MOE_ERR_INVALID;
+  if (!aligned16({h, h_shared, w2, w2_shared, y_perm, y_shared}) || !aligned4({offsets}))
+    return MOE_ERR_INVALID;
   Workspace w;
   if ((st = check_ws(shape, ws, ws_bytes, w)) != MOE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (launch_plan(*shape, offsets, w, s) != hipSuccess) return MOE_ERR_HIP;
+  if (offsets && launch_plan(*shape, offsets, w, s) != hipSuccess) return MOE_ERR_HIP;
   const bool sh = shape->d_ff_shared > 0;
   return hip_status(launch_gemm2(*shape, h, sh ? h_shared : nullptr, w2, w2_shared, y_perm,
                                  sh ? y_shared : nullptr, w, s));
@@ -230,6 +264,7 @@ moe_status moe_combine(const moe_shape* shape, const void* y_perm, const void* y
   if (st != MOE_OK) return st;
   if (!y_perm || !slot || !topk_w || !y) return MOE_ERR_INVALID;
   if (shape->d_ff_shared > 0 && !y_shared) return MOE_ERR_INVALID;
+  if (!aligned16({y_perm, y_shared, y}) || !aligned4({slot, topk_w})) return MOE_ERR_INVALID;
   return hip_status(launch_combine(*shape, y_perm, shape->d_ff_shared > 0 ? y_shared : nullptr,
                                    slot, topk_w, y, static_cast<hipStream_t>(stream)));
 }
@@ -240,6 +275,7 @@ moe_status moe_bias_update(const moe_shape* shape, const int32_t* counts, const 
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
   if (!counts || !bias || !isfinite(step) || isnan(clamp)) return MOE_ERR_INVALID;
+  if (!aligned4({counts, scores, bias, aux_out})) return MOE_ERR_INVALID;
   Workspace w;
   if ((st = check_ws(shape, ws, ws_bytes, w)) != MOE_OK) return st;
   return hip_status(launch_bias_update(*shape, counts, scores, step, clamp, bias, aux_out,
@@ -256,6 +292,10 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_rou
   if (st != MOE_OK) return st;
   if (!x || !w_router || !w1 || !w2 || !y) return MOE_ERR_INVALID;
   if (shape->d_ff_shared > 0 && (!w1_shared || !w2_shared)) return MOE_ERR_INVALID;
+  if (!aligned16({x, w_router, w1, w2, w1_shared, w2_shared, y}) ||
+      !aligned4({logit_add, bias, scores_out, topk_idx, topk_w, counts, offsets, slot,
+                 n_kept_dropped}))
+    return MOE_ERR_INVALID;
   Workspace w;
   if ((st = check_ws(shape, ws, ws_bytes, w)) != MOE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -160,6 +160,15 @@ def test_invalid_arguments_fail_before_launch(m):
     assert L.moe_bias_update(ctypes.byref(s), None, None, ctypes.c_float(1e-3), 0.0, fake,
                              None, ws_ok, big, None) == m.MOE_ERR_INVALID
     assert L.moe_forward(None, *([fake] * 16), ws_ok, big, None) == m.MOE_ERR_INVALID
+    # misaligned pointers: activation rows need 16 bytes, int32/fp32 arrays 4
+    assert L.moe_combine(ctypes.byref(s), fake, None, fake, fake, P(4096 + 8), None) == \
+        m.MOE_ERR_INVALID
+    assert L.moe_combine(ctypes.byref(s), fake, None, P(4096 + 2), fake, fake, None) == \
+        m.MOE_ERR_INVALID
+    assert L.moe_expert_gate_up(ctypes.byref(s), P(4096 + 4), fake, None, fake, None, fake,
+                                None, ws_ok, big, None) == m.MOE_ERR_INVALID
+    # the work-list builder needs the segment offsets
+    assert L.moe_expert_plan(ctypes.byref(s), None, ws_ok, big, None) == m.MOE_ERR_INVALID
 
 
 def test_binding_rejects_cpu_tensors(m):

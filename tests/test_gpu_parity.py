@@ -100,7 +100,7 @@ def test_steps_compose_to_forward_and_expert_rows(name):
         assert err <= tol_for(cfg)
 
 
-@pytest.mark.parametrize("name", ["tiny", "dsv3"])
+@pytest.mark.parametrize("name", ["tiny", "dsv3", "decode"])
 def test_gate_up_then_down_equals_expert_ffn(name):
     """moe_expert_gate_up + moe_expert_down through caller buffers give
     moe_expert_ffn's rows bit for bit, and h matches the oracle's SwiGLU
@@ -125,6 +125,22 @@ def test_gate_up_then_down_equals_expert_ffn(name):
     assert torch.equal(yp[:R], st["y_perm"][:R])
     if fs:
         assert torch.equal(ysh, st["y_shared"])
+    # offsets = NULL: the work lists already in the workspace are launched
+    # again (twice, so the re-armed item counters are exercised), and once
+    # more after an explicit moe_expert_plan
+    for replan in (False, False, True):
+        if replan:
+            moe.moe_expert_plan(shape, st["offsets"], ws)
+        h2, yp2 = torch.zeros_like(h), torch.zeros_like(yp)
+        hs2 = torch.zeros_like(hs) if fs else None
+        ysh2 = torch.zeros_like(ysh) if fs else None
+        moe.moe_expert_gate_up(shape, inp.x, st["perm"], None, inp.w1, inp.w1_shared, h2, hs2,
+                               ws)
+        moe.moe_expert_down(shape, h2, hs2, None, inp.w2, inp.w2_shared, yp2, ysh2, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(h2[:R], h[:R]) and torch.equal(yp2[:R], yp[:R])
+        if fs:
+            assert torch.equal(hs2, hs) and torch.equal(ysh2, ysh)
     # h rows of the first kept assignments vs the oracle's silu(x Wg) * (x Wu)
     perm = host(st["perm"])[:R]
     offs = host(st["offsets"])
