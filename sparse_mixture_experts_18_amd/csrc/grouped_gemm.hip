@@ -226,7 +226,8 @@ struct GemmArgs {
 // lane -> LDS position map is fixed, so each lane fetches the chunk that
 // belongs at its position.
 // ---------------------------------------------------------------------------
-template <int RG_, int CG_, int NTW_, int BK_, int SA_, int SB_, int MSW_ = 4, int LDS_KIB_ = 160>
+template <int RG_, int CG_, int NTW_, int BK_, int SA_, int SB_, int MSW_ = 4, int LDS_KIB_ = 160,
+          int MAXS_ = 4>
 struct GCfg {
   static constexpr int RG = RG_, CG = CG_, NTW = NTW_, BK = BK_;
   static constexpr int SA = SA_, SB = SB_;      // LDS ring depth of A and of B
@@ -244,6 +245,7 @@ struct GCfg {
   // the whole CU (one block per CU); 80 KiB lets two blocks share a CU.
   static constexpr int LDS_BYTES = LDS_KIB_ * 1024;
   static constexpr int BLOCKS_PER_CU = 160 / LDS_KIB_;
+  static constexpr int MAXS = MAXS_;  // deepest ring that items with few rows get
   static_assert(A_LOADS * 1024 * WAVES == A_BYTES && B_LOADS * 1024 * WAVES == B_BYTES, "");
   static_assert(SA * A_BYTES + SB * B_BYTES <= LDS_BYTES, "LDS");
   static_assert(SB >= SA && SA >= 2 && SB <= SA + 1, "B runs at most one slice ahead of A");
@@ -259,16 +261,16 @@ struct GCfg {
 using Cfg1 = GCfg<MOE_GEMM1_CFG>;
 using Cfg2 = GCfg<MOE_GEMM2_CFG>;
 // Layers with few rows per expert (decode batches) stream the weights with
-// short items: one 32-row sub-tile per wave, half the LDS, two blocks per CU.
-// The weight slabs of the touched experts then spread over every CU instead
-// of leaving most CUs idle behind the few that hold a second item.  The k
-// order of every output is the same as with the wide tiles, so the choice
-// never changes a result.
+// short items: 64 rows x 128 weight rows, four waves, and the LDS spent on a
+// four-deep ring.  Twice as many items as weight slabs of 256 rows spread
+// the touched experts' weights over every CU, and the deeper ring keeps more
+// bytes in flight per CU.  The k order of every output is the same as with
+// the wide tiles, so the choice never changes a result.
 #ifndef MOE_GEMM1_SMALL_CFG
-#define MOE_GEMM1_SMALL_CFG 2, 4, 2, 64, 2, 2, 1, 80
+#define MOE_GEMM1_SMALL_CFG 2, 2, 2, 64, 2, 2, 1, 160, 4
 #endif
 #ifndef MOE_GEMM2_SMALL_CFG
-#define MOE_GEMM2_SMALL_CFG 2, 4, 2, 64, 2, 2, 1, 80
+#define MOE_GEMM2_SMALL_CFG 2, 2, 2, 64, 2, 2, 1, 160, 4
 #endif
 using Cfg1n = GCfg<MOE_GEMM1_SMALL_CFG>;
 using Cfg2n = GCfg<MOE_GEMM2_SMALL_CFG>;
@@ -363,8 +365,8 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& g, const WorkItem
   // the B slice.  Items with fewer rows have smaller A slices and get deeper
   // rings (their short MFMA phase hides less latency per slice).
   constexpr int A_SL = C::RG * MS * 32 * C::ROWB;  // bytes of one A slice
-  constexpr int SDEEP = (C::LDS_BYTES / (A_SL + C::B_BYTES)) < 4
-                            ? (C::LDS_BYTES / (A_SL + C::B_BYTES)) : 4;
+  constexpr int SDEEP = (C::LDS_BYTES / (A_SL + C::B_BYTES)) < C::MAXS
+                            ? (C::LDS_BYTES / (A_SL + C::B_BYTES)) : C::MAXS;
   constexpr int SA = SDEEP > C::SA ? SDEEP : C::SA;
   constexpr int SB = SDEEP > C::SB ? SDEEP : C::SB;
   static_assert(SA * A_SL + SB * C::B_BYTES <= C::LDS_BYTES, "LDS");
