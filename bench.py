@@ -39,7 +39,8 @@ def parse():
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", default="dsv3")
-    p.add_argument("--cpu-sample-tokens", type=int, default=8)
+    p.add_argument("--cpu-sample-tokens", type=int, default=48,
+                   help="tokens of the batch the oracle runs on (about 10 s on the host)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--stage-iters", type=int, default=10)
     return p.parse_args()
@@ -89,6 +90,7 @@ def cpu_baseline(cfg, inp, n_tokens: int) -> dict:
 
     import oracle
 
+    n_tokens = min(n_tokens, cfg.T)
     x = inp.x[:n_tokens].float().cpu().numpy()
     wr = inp.w_router.cpu().numpy()
     la = None if inp.logit_add is None else inp.logit_add[:n_tokens].cpu().numpy()
@@ -103,15 +105,17 @@ def cpu_baseline(cfg, inp, n_tokens: int) -> dict:
         cand = oracle.group_candidates(keys, cfg.n_groups, cfg.topk_groups,
                                        cfg.top_k // cfg.topk_groups)
     touched = sorted(set(oracle.topk_select(keys, cfg.top_k, cand).reshape(-1).tolist()))
-    wcache = {e: (inp.w1[e].float().cpu().numpy(), inp.w2[e].float().cpu().numpy())
-              for e in touched}
+    # host copies in the layer's own dtype; each expert is widened when the
+    # oracle asks for it (exact: bf16 -> fp32 is lossless)
+    wcache = {e: (inp.w1[e].cpu(), inp.w2[e].cpu()) for e in touched}
     w1s = None if inp.w1_shared is None else inp.w1_shared.float().cpu().numpy()
     w2s = None if inp.w2_shared is None else inp.w2_shared.float().cpu().numpy()
     torch.cuda.synchronize()
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
     t0 = time.perf_counter()
-    oracle.moe_layer(x, wr, lambda e: wcache[e], None, top_k=cfg.top_k,
+    oracle.moe_layer(x, wr, lambda e: (wcache[e][0].float().numpy(),
+                                       wcache[e][1].float().numpy()), None, top_k=cfg.top_k,
                      score_fn=cfg.score_fn, renormalize=cfg.renormalize,
                      n_groups=cfg.n_groups, topk_groups=cfg.topk_groups,
                      capacity_factor=cfg.capacity_factor, capacity_rule=cfg.capacity_rule,
