@@ -29,25 +29,49 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 // ---------------------------------------------------------------------------
 // work-list construction
 // ---------------------------------------------------------------------------
+// exclusive prefix sums of two values over the block (blockDim.x a multiple
+// of 64, at most 1024): scans inside each wave with lane shuffles, then one
+// wave scans the wave totals; integer, so exact
 __device__ __forceinline__ void block_exclusive_scan2(int* sh0, int* sh1, int v0, int v1,
                                                       int& ex0, int& ex1, int& tot0,
                                                       int& tot1) {
-  const int i = threadIdx.x, n = blockDim.x;
-  sh0[i] = v0;
-  sh1[i] = v1;
-  __syncthreads();
-  for (int o = 1; o < n; o <<= 1) {
-    int a = i >= o ? sh0[i - o] : 0;
-    int b = i >= o ? sh1[i - o] : 0;
-    __syncthreads();
-    sh0[i] += a;
-    sh1[i] += b;
-    __syncthreads();
+  const int i = threadIdx.x, lane = i & 63, w = i >> 6, nw = blockDim.x >> 6;
+  int a = v0, b = v1;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int ta = __shfl_up(a, o, 64), tb = __shfl_up(b, o, 64);
+    if (lane >= o) {
+      a += ta;
+      b += tb;
+    }
   }
-  ex0 = sh0[i] - v0;
-  ex1 = sh1[i] - v1;
-  tot0 = sh0[n - 1];
-  tot1 = sh1[n - 1];
+  __syncthreads();  // the scratch may still be read by a previous call
+  if (lane == 63) {
+    sh0[w] = a;
+    sh1[w] = b;
+  }
+  __syncthreads();
+  if (w == 0) {
+    int ca = lane < nw ? sh0[lane] : 0, cb = lane < nw ? sh1[lane] : 0;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const int ta = __shfl_up(ca, o, 64), tb = __shfl_up(cb, o, 64);
+      if (lane >= o) {
+        ca += ta;
+        cb += tb;
+      }
+    }
+    if (lane < nw) {
+      sh0[32 + lane] = ca;  // inclusive wave prefixes
+      sh1[32 + lane] = cb;
+    }
+  }
+  __syncthreads();
+  const int pa = w ? sh0[32 + w - 1] : 0, pb = w ? sh1[32 + w - 1] : 0;
+  ex0 = pa + a - v0;
+  ex1 = pb + b - v1;
+  tot0 = sh0[32 + nw - 1];
+  tot1 = sh1[32 + nw - 1];
 }
 
 // Cost of an item for the XCD split: (live 32-row sub-tiles + a fixed part for
@@ -68,7 +92,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
                                                     int32_t* __restrict__ hdr1,
                                                     WorkItem* __restrict__ plan2,
                                                     int32_t* __restrict__ hdr2) {
-  __shared__ int sh0[1024], sh1[1024];
+  __shared__ int sh0[64], sh1[64];
   __shared__ int st1s[1025], st2s[1025], mt1s[1024], mt2s[1024], rbases[1024], rowss[1024];
   const int s = threadIdx.x;
   const int S = N + has_shared;
