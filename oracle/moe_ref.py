@@ -34,6 +34,16 @@ in the sources):
   [NL]  "MoE industrial evolution" (alishangtian.com), section 4
         (DeepSeek route): node-limited routing, each token's experts lie in
         at most M groups.
+  [OBS] "MoE architecture in practice", section on scale drift between
+        experts (its closing summary of the minimum MoE observability: drop
+        ratio, per-expert load, per-expert output scale as mean / std / max,
+        bias magnitude, gate entropy) and its implementation checklist (drop
+        ratio logged per expert); "MoE landscape" (paper-daily-site topic
+        page), TL;DR and recommendations: dead-expert count, usage CV, token
+        drop and router bias norm as first-class indicators.
+  [SEQ] "MoE architecture in practice", section "load-balancing loss"
+        (update_bias from per-sequence loads, so that long sequences do not
+        dominate), and its long-context section (sequence-level balancing).
 
 Readings taken where the pages are silent or garbled are listed in the
 repository's design notes; the ones that change arithmetic are restated at
@@ -372,6 +382,140 @@ def bias_update(bias: np.ndarray, counts: np.ndarray, T: int, k: int,
     c = np.asarray(counts, np.int64)
     sg = np.sign(N * c - T * k).astype(f32)
     nb = (b - (f32(step) * sg).astype(f32)).astype(f32)
+    if clamp > 0:
+        nb = np.clip(nb, f32(-clamp), f32(clamp)).astype(f32)
+    return nb
+
+
+# ---------------------------------------------------------------------------
+# router telemetry
+# ---------------------------------------------------------------------------
+
+
+def _entropy(p: np.ndarray) -> float:
+    """-sum p ln p of a non-negative vector normalised to sum 1 (0 ln 0 = 0)."""
+    p = np.asarray(p, np.float64)
+    tot = p.sum()
+    if not tot > 0:
+        return 0.0
+    q = p / tot
+    nz = q > 0
+    return float(-np.sum(q[nz] * np.log(q[nz])))
+
+
+def router_stats(counts: np.ndarray, offsets: np.ndarray, topk_w: np.ndarray,
+                 scores: Optional[np.ndarray], bias: Optional[np.ndarray],
+                 y_perm: Optional[np.ndarray], y_shared: Optional[np.ndarray] = None
+                 ) -> Dict[str, np.ndarray]:
+    """The indicators [OBS] names, from what one forward already produced.
+
+    Global:
+      dropped       total dropped assignments, sum_e (load_e - kept_e)
+      drop_fraction dropped / (T*k)
+      usage_cv      population std / mean of the per-expert loads (pre-drop)
+      dead          number of experts no token chose
+      bias_norm     ||b||_2;  bias_absmax  max_i |b_i|   (0 without a bias)
+      gate_entropy  mean over tokens of -sum_j p ln p, p = the k gates of the
+                    token normalised to sum 1
+      score_entropy mean over tokens of the entropy of the N scores normalised
+                    to sum 1 (0 when no scores are given)
+    Per expert e (rows 0..N-1; row N = shared expert when y_shared is given):
+      load, kept, dropped, drop_ratio (dropped / load, 0 for an unused expert),
+      and the mean, population std, max and max |.| of the expert's output
+      rows (y_perm rows of its segment; all d columns), 0 for an empty one.
+    """
+    c = np.asarray(counts, np.int64)
+    off = np.asarray(offsets, np.int64)
+    N = c.size
+    g = np.asarray(topk_w, np.float64)
+    T, k = g.shape
+    kept = off[1:] - off[:-1]
+    dropped = c - kept
+    load = c.astype(np.float64)
+    mean = load.mean()
+    cv = float(np.sqrt(np.mean((load - mean) ** 2)) / mean) if mean > 0 else 0.0
+    glob = dict(dropped=int(dropped.sum()),
+                drop_fraction=float(dropped.sum()) / float(T * k),
+                usage_cv=cv, dead=int(np.sum(c == 0)))
+    if bias is not None:
+        b = np.asarray(bias, np.float64)
+        glob["bias_norm"] = float(np.sqrt(np.sum(b * b)))
+        glob["bias_absmax"] = float(np.max(np.abs(b)))
+    else:
+        glob["bias_norm"] = glob["bias_absmax"] = 0.0
+    glob["gate_entropy"] = float(np.mean([_entropy(g[t]) for t in range(T)]))
+    if scores is not None:
+        s = np.asarray(scores, np.float64)
+        glob["score_entropy"] = float(np.mean([_entropy(s[t]) for t in range(T)]))
+    else:
+        glob["score_entropy"] = 0.0
+    rows = N + (1 if y_shared is not None else 0)
+    per = np.zeros((rows, 8))
+    per[:N, 0] = c
+    per[:N, 1] = kept
+    per[:N, 2] = dropped
+    per[:N, 3] = np.where(c > 0, dropped / np.maximum(c, 1), 0.0)
+    segs = [(int(off[e]), int(off[e + 1])) for e in range(N)]
+    for e in range(rows):
+        if e < N:
+            if y_perm is None:
+                continue
+            blk = np.asarray(y_perm[segs[e][0]:segs[e][1]], np.float64)
+        else:
+            blk = np.asarray(y_shared, np.float64)
+        if blk.size == 0:
+            continue
+        per[e, 4] = blk.mean()
+        per[e, 5] = blk.std()
+        per[e, 6] = blk.max()
+        per[e, 7] = np.abs(blk).max()
+    if y_shared is not None:
+        T_ = np.asarray(y_shared).shape[0]
+        per[N, 0] = per[N, 1] = T_
+    glob["per_expert"] = per
+    return glob
+
+
+def bias_update_seq(bias: np.ndarray, topk_idx: np.ndarray, seq_lens: Sequence[int],
+                    step: float = 1e-3, clamp: float = 0.0) -> np.ndarray:
+    """Per-sequence balancing step ([SEQ]).  The article's update averages
+    per-sequence loads over the sequences so that long sequences do not
+    dominate; its code averages raw counts, which long sequences still
+    dominate, so the load of expert i in sequence s is read as its share
+    f_si = c_si / (k * L_s) (reading stated in the design notes).  Then
+    score_i = sum_s f_si / S, mean = sum_i score_i / N, and
+    b_i <- fl32(b_i + fl32(step * sign(mean - score_i))), clamped to
+    [-clamp, clamp] when clamp > 0.
+
+    The sign decides an integer, so the sums are taken in fp64 in a fixed
+    order (s ascending, then i ascending), one IEEE operation at a time --
+    the order the kernel uses."""
+    b = np.asarray(bias, f32)
+    N = b.size
+    idx = np.asarray(topk_idx, np.int64)
+    T, k = idx.shape
+    L = [int(v) for v in seq_lens]
+    assert sum(L) == T and all(v > 0 for v in L)
+    S = len(L)
+    score = [0.0] * N
+    t0 = 0
+    for s_ in range(S):
+        cnt = [0] * N
+        for t in range(t0, t0 + L[s_]):
+            for j in range(k):
+                cnt[int(idx[t, j])] += 1
+        den = float(k * L[s_])
+        for i in range(N):
+            score[i] = score[i] + cnt[i] / den
+        t0 += L[s_]
+    for i in range(N):
+        score[i] = score[i] / S
+    tot = 0.0
+    for i in range(N):
+        tot = tot + score[i]
+    mean = tot / N
+    sg = np.array([(mean > score[i]) - (mean < score[i]) for i in range(N)], f32)
+    nb = (b + (f32(step) * sg).astype(f32)).astype(f32)
     if clamp > 0:
         nb = np.clip(nb, f32(-clamp), f32(clamp)).astype(f32)
     return nb

@@ -410,3 +410,104 @@ def test_bias_update_closed_form():
     # non-integer mean load: sign taken exactly, no rounding of T*k/N
     nb2 = R.bias_update(np.zeros(3, f32), np.array([3, 3, 4]), 5, 2, 1e-3)
     assert nb2.tolist() == [np.float32(1e-3), np.float32(1e-3), np.float32(-1e-3)]
+
+
+# ------------------------------------------------------------- telemetry ---
+
+def _segs(counts, C=None):
+    """offsets of kept rows for per-expert loads under capacity C."""
+    kept = np.minimum(counts, C) if C is not None else np.asarray(counts)
+    return np.concatenate([[0], np.cumsum(kept)])
+
+
+def test_stats_uniform_and_collapsed_loads():
+    N, T, k = 8, 64, 2
+    g = np.full((T, k), 0.5)
+    st = R.router_stats(np.full(N, T * k // N), _segs(np.full(N, T * k // N)), g, None, None,
+                        None)
+    assert st["usage_cv"] == 0.0 and st["dead"] == 0 and st["dropped"] == 0
+    # every assignment on expert 0 (k = 1): loads [T, 0, ...]: cv = sqrt(N-1)
+    c = np.zeros(N, np.int64)
+    c[0] = T
+    st = R.router_stats(c, _segs(c), np.ones((T, 1)), None, None, None)
+    assert abs(st["usage_cv"] - math.sqrt(N - 1)) < 1e-12 and st["dead"] == N - 1
+
+
+def test_stats_drops_match_dispatch():
+    r = rng(31)
+    T, N, k = 64, 8, 2
+    idx = np.stack([r.choice(N, k, replace=False) for _ in range(T)])
+    C = R.capacity(1.25, T, N, k)
+    d = R.dispatch(idx, N, C)
+    st = R.router_stats(d["counts"], d["offsets"], np.full((T, k), 0.5), None, None, None)
+    assert st["dropped"] == d["n_dropped"]
+    assert abs(st["drop_fraction"] - d["n_dropped"] / (T * k)) < 1e-15
+    per = st["per_expert"]
+    for e in range(N):
+        over = max(0, int(d["counts"][e]) - C)
+        assert per[e, 2] == over
+        assert abs(per[e, 3] - (over / d["counts"][e] if d["counts"][e] else 0.0)) < 1e-15
+
+
+def test_stats_entropies_closed_forms():
+    T, N, k = 5, 6, 4
+    g = np.full((T, k), 0.25)
+    st = R.router_stats(np.full(N, 1), _segs(np.full(N, 1)), g, np.full((T, N), 0.3), None,
+                        None)
+    assert abs(st["gate_entropy"] - math.log(k)) < 1e-12
+    assert abs(st["score_entropy"] - math.log(N)) < 1e-12
+    g1 = np.zeros((T, k))
+    g1[:, 0] = 1.0
+    s1 = np.zeros((T, N))
+    s1[:, 2] = 0.9
+    st = R.router_stats(np.full(N, 1), _segs(np.full(N, 1)), g1, s1, None, None)
+    assert st["gate_entropy"] == 0.0 and st["score_entropy"] == 0.0
+    # two gates p, 1-p
+    p = 0.3
+    g2 = np.tile([p, 1 - p], (T, 1))
+    st = R.router_stats(np.full(N, 1), _segs(np.full(N, 1)), g2, None, None, None)
+    assert abs(st["gate_entropy"] + p * math.log(p) + (1 - p) * math.log(1 - p)) < 1e-12
+
+
+def test_stats_output_scale_and_bias_norm():
+    N, d = 3, 4
+    counts = np.array([2, 0, 3])
+    off = _segs(counts)
+    y = np.zeros((5, d))
+    y[0:2] = 1.5                         # expert 0: constant rows
+    y[2:5] = np.array([[2.0, -2.0, 2.0, -2.0]] * 3)   # expert 2: +-2
+    b = np.array([3.0, 4.0, 0.0])
+    st = R.router_stats(counts, off, np.full((5, 1), 1.0), None, b, y, y_shared=np.full((2, d), -1.0))
+    per = st["per_expert"]
+    assert per[0, 4:].tolist() == [1.5, 0.0, 1.5, 1.5]
+    assert per[1, 4:].tolist() == [0.0, 0.0, 0.0, 0.0]  # no rows
+    assert per[2, 4:].tolist() == [0.0, 2.0, 2.0, 2.0]
+    assert per[3, 4:].tolist() == [-1.0, 0.0, -1.0, 1.0]  # shared expert row
+    assert st["bias_norm"] == 5.0 and st["bias_absmax"] == 4.0
+
+
+def test_seq_bias_update_equal_lengths_is_the_batch_rule():
+    r = rng(32)
+    N, k, L, S = 8, 2, 16, 4
+    T = L * S
+    idx = np.stack([r.choice(N, k, replace=False) for _ in range(T)])
+    counts = np.bincount(idx.reshape(-1), minlength=N)
+    b = r.uniform(-0.01, 0.01, N).astype(f32)
+    # dyadic lengths: every fp64 share and sum is exact, ties stay ties
+    assert np.array_equal(R.bias_update_seq(b, idx, [L] * S, 1e-3),
+                          R.bias_update(b, counts, T, k, 1e-3))
+
+
+def test_seq_bias_update_weights_sequences_equally():
+    b = np.zeros(2, f32)
+    # sequence 0: one token on expert 0; sequence 1: three tokens on expert 1.
+    idx = np.array([[0], [1], [1], [1]])
+    # per-sequence shares [1, 0] and [0, 1]: balanced, no change ...
+    assert np.array_equal(R.bias_update_seq(b, idx, [1, 3], 1e-3), b)
+    # ... while the batch rule (loads 1 vs 3) moves both
+    assert R.bias_update(b, np.array([1, 3]), 4, 1, 1e-3).tolist() == \
+        [np.float32(1e-3), np.float32(-1e-3)]
+    # shares [1, 0] and [1/2, 1/2]: expert 0 overloaded
+    idx2 = np.array([[0], [0], [0], [1]])
+    nb = R.bias_update_seq(b, idx2, [2, 2], 1e-3, clamp=5e-4)
+    assert nb.tolist() == [np.float32(-5e-4), np.float32(5e-4)]
