@@ -228,6 +228,53 @@ moe_status moe_bias_update(const moe_shape* shape, const int32_t* counts,
                            float* bias, float* aux_out, void* ws,
                            size_t ws_bytes, void* stream);
 
+/* Router telemetry: the indicators that "MoE architecture in practice"
+ * (section on scale drift between experts, and its implementation
+ * checklist) and the "MoE landscape" page (first-class training indicators)
+ * name, from what one forward produced.  All reductions in fp64, fixed
+ * order (bitwise reproducible).
+ *   counts [N] (pre-drop), offsets [N+1] from moe_dispatch; topk_w [T,k];
+ *   scores [T,N] (NULL: score entropy 0); bias [N] (NULL: norms 0);
+ *   y_perm [T*k, d] dtype from the expert FFNs (NULL: output moments 0);
+ *   y_shared [T, d] (NULL, or given iff d_ff_shared > 0).
+ * Output `stats`: moe_router_stats_count(shape) = 16 + 8*(N+1) doubles,
+ * device memory, 8-byte aligned:
+ *   [0] T  [1] T*k  [2] dropped assignments  [3] dropped / (T*k)
+ *   [4] usage CV = population std / mean of counts  [5] experts with count 0
+ *   [6] ||bias||_2  [7] max |bias|  [8] mean over tokens of the entropy of
+ *   its k gates (normalised to sum 1)  [9] mean entropy of its N scores
+ *   (normalised to sum 1)  [10..15] 0
+ *   then per expert e = 0..N-1 and e = N (the shared expert; zeros without
+ *   one), 8 doubles: load, kept, dropped, dropped/load (0 if load is 0),
+ *   mean, population std, max and max |.| of the expert's output rows
+ *   (y_perm rows [offsets[e], offsets[e+1]); all d columns; zeros if empty). */
+size_t moe_router_stats_count(const moe_shape* shape);
+moe_status moe_router_stats(const moe_shape* shape, const int32_t* counts,
+                            const int32_t* offsets, const float* topk_w,
+                            const float* scores, const float* bias,
+                            const void* y_perm, const void* y_shared,
+                            double* stats, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/* Per-sequence balancing step ("MoE architecture in practice", section
+ * "load-balancing loss": update_bias averages loads over sequences so that
+ * long sequences do not dominate).  The batch holds n_seq sequences of
+ * tokens [seq_offsets[s], seq_offsets[s+1]) (device int32 [n_seq+1],
+ * seq_offsets[0] = 0, strictly increasing, seq_offsets[n_seq] = T).  With
+ * c_si the pre-drop count of expert i among sequence s's k*L_s assignments:
+ *   score_i = (sum_s c_si / (k L_s)) / n_seq,  mean = sum_i score_i / N,
+ *   bias_i <- fl32(bias_i + step * sign(mean - score_i)), then clamped to
+ *   [-clamp, clamp] when clamp > 0.
+ * The sums are fp64, one IEEE operation at a time in s then i order.
+ * topk_idx [T,k] from moe_route.  If the device offsets are malformed the
+ * bias is left unchanged and *err_out (optional, device int32) is set to 1,
+ * else 0.  1 <= n_seq <= T, step finite. */
+moe_status moe_bias_update_seq(const moe_shape* shape, const int32_t* topk_idx,
+                               const int32_t* seq_offsets, int32_t n_seq,
+                               float step, float clamp, float* bias,
+                               int32_t* err_out, void* ws, size_t ws_bytes,
+                               void* stream);
+
 /* The whole layer: route -> dispatch -> expert FFNs -> combine on `stream`.
  * Required: x, w_router, w1, w2, y (and the shared weights iff
  * d_ff_shared > 0).  Optional inputs logit_add, bias; optional outputs

@@ -9,7 +9,8 @@ The functions mirror the C ABI in include/moe.h one to one (same names, same
 argument order, tensors in place of pointers):
 
     moe_route, moe_dispatch, moe_expert_plan, moe_expert_ffn, moe_expert_gate_up,
-    moe_expert_down, moe_combine, moe_bias_update, moe_forward,
+    moe_expert_down, moe_combine, moe_bias_update, moe_bias_update_seq,
+    moe_router_stats, moe_router_stats_count, moe_forward,
     moe_workspace_bytes, moe_check_shape, moe_capacity, moe_status_string,
     moe_abi_version
 
@@ -111,6 +112,11 @@ _SIGS = {
     "moe_combine": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P]),
     "moe_bias_update": (ctypes.c_int, [_S, _P, _P, ctypes.c_float, ctypes.c_float, _P, _P, _P,
                                        ctypes.c_size_t, _P]),
+    "moe_router_stats_count": (ctypes.c_size_t, [_S]),
+    "moe_router_stats": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                        _P]),
+    "moe_bias_update_seq": (ctypes.c_int, [_S, _P, _P, ctypes.c_int32, ctypes.c_float,
+                                           ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_forward": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                    _P, _P, _P, _P, ctypes.c_size_t, _P]),
 }
@@ -280,6 +286,37 @@ def moe_expert_down(shape, h, h_shared, offsets, w2, w2_shared, y_perm, y_shared
         _ptr(w2_shared, "w2_shared", dt, d * fs), _ptr(y_perm, "y_perm", dt, T * k * d),
         _ptr(y_shared, "y_shared", dt, T * d), p, n, _stream(stream))
     _check(st, "moe_expert_down")
+
+
+def moe_router_stats_count(shape: MoeShape) -> int:
+    return lib().moe_router_stats_count(ctypes.byref(shape))
+
+
+def moe_router_stats(shape, counts, offsets, topk_w, scores, bias, y_perm, y_shared, stats, ws,
+                     stream=None):
+    T, N, k, d = shape.T, shape.n_experts, shape.top_k, shape.d_model
+    dt = _dt(shape)
+    p, n = _ws(ws)
+    st = lib().moe_router_stats(
+        ctypes.byref(shape), _ptr(counts, "counts", torch.int32, N),
+        _ptr(offsets, "offsets", torch.int32, N + 1), _ptr(topk_w, "topk_w", torch.float32, T * k),
+        _ptr(scores, "scores", torch.float32, T * N), _ptr(bias, "bias", torch.float32, N),
+        _ptr(y_perm, "y_perm", dt, T * k * d), _ptr(y_shared, "y_shared", dt, T * d),
+        _ptr(stats, "stats", torch.float64, moe_router_stats_count(shape)), p, n, _stream(stream))
+    _check(st, "moe_router_stats")
+
+
+def moe_bias_update_seq(shape, topk_idx, seq_offsets, step, clamp, bias, err_out, ws,
+                        stream=None):
+    T, N, k = shape.T, shape.n_experts, shape.top_k
+    p, n = _ws(ws)
+    n_seq = seq_offsets.numel() - 1
+    st = lib().moe_bias_update_seq(
+        ctypes.byref(shape), _ptr(topk_idx, "topk_idx", torch.int32, T * k),
+        _ptr(seq_offsets, "seq_offsets", torch.int32), n_seq, float(step), float(clamp),
+        _ptr(bias, "bias", torch.float32, N), _ptr(err_out, "err_out", torch.int32, 1), p, n,
+        _stream(stream))
+    _check(st, "moe_bias_update_seq")
 
 
 def moe_combine(shape, y_perm, y_shared, slot, topk_w, y, stream=None):

@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["moe_api.hip", "router.hip", "dispatch.hip", "grouped_gemm.hip", "combine.hip"]
+SOURCES = ["moe_api.hip", "router.hip", "dispatch.hip", "grouped_gemm.hip", "combine.hip",
+           "telemetry.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

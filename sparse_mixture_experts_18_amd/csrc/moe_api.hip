@@ -103,6 +103,8 @@ Workspace layout_workspace(const moe_shape& s, void* ws) {
   w.pmean = static_cast<double*>(take(N * 8));
   w.wsplit = static_cast<bf16_t*>(take(s.dtype == MOE_DTYPE_BF16 ? 3 * N * d * 2 : 0));
   w.router_part = static_cast<float*>(take((size_t)router_split_chunks(s) * T * N * 4));
+  w.stats_rows = static_cast<double*>(take((A + T) * 4 * 8));
+  w.stats_ent = static_cast<double*>(take(T * 2 * 8));
   w.total = off;
   return w;
 }
@@ -280,6 +282,44 @@ moe_status moe_bias_update(const moe_shape* shape, const int32_t* counts, const 
   if ((st = check_ws(shape, ws, ws_bytes, w)) != MOE_OK) return st;
   return hip_status(launch_bias_update(*shape, counts, scores, step, clamp, bias, aux_out,
                                        w.pmean, static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_router_stats_count(const moe_shape* shape) {
+  if (check_shape(shape) != MOE_OK) return 0;
+  return (size_t)kStatsGlobal + (size_t)kStatsPerExpert * (shape->n_experts + 1);
+}
+
+moe_status moe_router_stats(const moe_shape* shape, const int32_t* counts,
+                            const int32_t* offsets, const float* topk_w, const float* scores,
+                            const float* bias, const void* y_perm, const void* y_shared,
+                            double* stats, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!counts || !offsets || !topk_w || !stats) return MOE_ERR_INVALID;
+  if (y_shared && shape->d_ff_shared == 0) return MOE_ERR_INVALID;
+  if (!aligned16({y_perm, y_shared}) || !aligned4({counts, offsets, topk_w, scores, bias}) ||
+      !aligned(8, {stats}))
+    return MOE_ERR_INVALID;
+  Workspace w;
+  if ((st = check_ws(shape, ws, ws_bytes, w)) != MOE_OK) return st;
+  return hip_status(launch_router_stats(*shape, counts, offsets, topk_w, scores, bias, y_perm,
+                                        y_shared, stats, w, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_bias_update_seq(const moe_shape* shape, const int32_t* topk_idx,
+                               const int32_t* seq_offsets, int32_t n_seq, float step,
+                               float clamp, float* bias, int32_t* err_out, void* ws,
+                               size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!topk_idx || !seq_offsets || !bias || !isfinite(step) || isnan(clamp))
+    return MOE_ERR_INVALID;
+  if (n_seq < 1 || n_seq > shape->T) return MOE_ERR_INVALID;
+  if (!aligned4({topk_idx, seq_offsets, bias, err_out})) return MOE_ERR_INVALID;
+  Workspace w;
+  if ((st = check_ws(shape, ws, ws_bytes, w)) != MOE_OK) return st;
+  return hip_status(launch_bias_update_seq(*shape, topk_idx, seq_offsets, n_seq, step, clamp,
+                                           bias, err_out, w, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_router,

@@ -63,6 +63,8 @@ struct Workspace {
   double* pmean;   // [N] mean score per expert (balancing step)
   bf16_t* wsplit;  // [3][N][d] bf16 terms of the fp32 router weight (bf16 layers)
   float* router_part;  // [chunks][T][N] partial logits of the split router GEMM
+  double* stats_rows;  // [T*k + T][4] per-row output moments (telemetry)
+  double* stats_ent;   // [T][2] per-token gate / score entropy (telemetry)
   size_t total;
   int64_t plan1_cap, plan2_cap;
 };
@@ -71,6 +73,9 @@ struct Workspace {
 Workspace layout_workspace(const moe_shape& s, void* ws);
 
 int64_t capacity_of(const moe_shape& s);  // -1 = dropless
+
+constexpr int kStatsGlobal = 16;   // doubles of global indicators
+constexpr int kStatsPerExpert = 8; // doubles per expert row (N routed + 1 shared)
 
 // ---- launchers (validated arguments; return hipError_t of the launch) ----
 hipError_t launch_router_gemm(const moe_shape& s, const void* x, const float* w_router,
@@ -98,5 +103,13 @@ hipError_t launch_bias_update(const moe_shape& s, const int32_t* counts, const f
                               double* p_scratch, hipStream_t st);
 void plan_caps(const moe_shape& s, int64_t& cap1, int64_t& cap2);
 int router_split_chunks(const moe_shape& s);  // 0: router GEMM not split
+
+hipError_t launch_router_stats(const moe_shape& s, const int32_t* counts, const int32_t* offsets,
+                               const float* topk_w, const float* scores, const float* bias,
+                               const void* y_perm, const void* y_shared, double* stats,
+                               const Workspace& w, hipStream_t st);
+hipError_t launch_bias_update_seq(const moe_shape& s, const int32_t* topk_idx,
+                                  const int32_t* seq_off, int n_seq, float step, float clamp,
+                                  float* bias, int32_t* err, const Workspace& w, hipStream_t st);
 
 }  // namespace moe
