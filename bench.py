@@ -260,6 +260,17 @@ def main():
     gemm2 = {"kernel": "gemm_bf16_kernel<false> (down projection)", "avg_ms": round(g2_ms, 4),
              "tflops": round(g2_flops / (g2_ms * 1e-3) / 1e12, 2)}
 
+    # router telemetry over this forward's outputs (HBM-bound: it reads the
+    # kept expert rows, the shared rows, the scores and the gates once)
+    stats = torch.empty(moe.moe_router_stats_count(shape), dtype=torch.float64, device=dev)
+    tl_ms = timed(lambda: moe.moe_router_stats(shape, cn, of, tw, sc, inp.bias, yp, ysh, stats,
+                                               ws), args.stage_iters)
+    tl_bytes = esz * (n_kept + (T if cfg.d_ff_shared else 0)) * d + 4 * T * (N + k) + 8 * N
+    tl_gbs = tl_bytes / (tl_ms * 1e-3) / 1e9
+    telemetry = {"kernels": "row_stats, expert_stats, entropy, stats_final (moe_router_stats)",
+                 "avg_ms": round(tl_ms, 4), "algorithmic_bytes": tl_bytes,
+                 "GB/s": round(tl_gbs, 1), "hbm_frac": round(tl_gbs / PEAK_HBM_GBS, 4)}
+
     res = {
         "metric": METRIC,
         "value": round(T / (ms * 1e-3), 1),
@@ -283,6 +294,7 @@ def main():
         "n_kept": n_kept,
         "roofline": roofline,
         "gemm2": gemm2,
+        "telemetry": telemetry,
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

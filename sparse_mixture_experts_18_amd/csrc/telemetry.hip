@@ -29,16 +29,30 @@ __device__ __forceinline__ double wave_max_d(double v) {
   return v;
 }
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// the values of one 16-byte chunk of a row
 template <typename XT>
-__device__ __forceinline__ float load_elem(const XT* p, size_t i);
+struct Chunk;
 template <>
-__device__ __forceinline__ float load_elem<float>(const float* p, size_t i) {
-  return p[i];
-}
+struct Chunk<float> {
+  static constexpr int n = 4;
+  __device__ static __forceinline__ void get(const u32x4_t& v, float* o) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = __uint_as_float(v[i]);
+  }
+};
 template <>
-__device__ __forceinline__ float load_elem<bf16_t>(const bf16_t* p, size_t i) {
-  return bf16_to_f32(p[i]);
-}
+struct Chunk<bf16_t> {
+  static constexpr int n = 8;
+  __device__ static __forceinline__ void get(const u32x4_t& v, float* o) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = __uint_as_float(v[i] << 16);
+      o[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+    }
+  }
+};
 
 // one wave per output row: fp64 sum, sum of squares, max and max |.| of the
 // row's d values -> part[row][4]; rows from *nrows_dev on (dropped slots of
@@ -50,14 +64,22 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const XT* __restrict__ y
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows || (nrows_dev && row >= *nrows_dev)) return;
-  const XT* p = y + (size_t)row * d;
+  // 16-byte chunks (d is a multiple of 32 elements, rows 16-byte aligned)
+  const u32x4_t* p = reinterpret_cast<const u32x4_t*>(y + (size_t)row * d);
+  constexpr int E = Chunk<XT>::n;
+  const int nch = d / E;
   double s = 0.0, q = 0.0, mx = -INFINITY, ma = 0.0;
-  for (int c = lane; c < d; c += kWave) {
-    const double v = (double)load_elem<XT>(p, c);
-    s += v;
-    q += v * v;
-    mx = fmax(mx, v);
-    ma = fmax(ma, fabs(v));
+  for (int c = lane; c < nch; c += kWave) {
+    float f[E];
+    Chunk<XT>::get(p[c], f);
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const double v = (double)f[i];
+      s += v;
+      q += v * v;
+      mx = fmax(mx, v);
+      ma = fmax(ma, fabs(v));
+    }
   }
   s = wave_sum_d(s);
   q = wave_sum_d(q);
