@@ -10,13 +10,15 @@
 // GEMM1: h[s, c] = silu(x_t . Wg_e[c]) * (x_t . Wu_e[c])   t = perm[s] / k
 // GEMM2: y_perm[s, n] = h[s] . W2_e[n]
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16, fp32 accumulation, 128-row work items,
-// both operands K-contiguous (weights in nn.Linear [out, in] layout), staged
-// through LDS with an XOR swizzle of the 16-byte chunks.  The work list
-// (segment, row block, column tile) is built on the device from the dispatch
-// offsets, so no host synchronisation is needed; blocks are mapped so that
-// each XCD walks a contiguous run of the list (same expert, same weight
-// slab), which keeps that slab in the XCD's L2 across the row blocks.
+// bf16 path: v_mfma_f32_32x32x16_bf16, fp32 accumulation, work items of up
+// to 256 rows x 256 weight rows (64 x 128 for layers with few rows per
+// expert), both operands K-contiguous (weights in nn.Linear [out, in]
+// layout), staged through LDS by direct DMA with an XOR swizzle of the
+// 16-byte chunks.  The work list (segment, row block, column tile) is built
+// on the device from the dispatch offsets, so no host synchronisation is
+// needed.  Persistent blocks, one per CU: each XCD walks its own contiguous,
+// cost-balanced run of the list (same expert, same weight slab), which keeps
+// that slab in the XCD's L2 across the row blocks.
 #include "moe_internal.h"
 
 namespace moe {
@@ -298,7 +300,8 @@ using Cfg2 = GCfg<MOE_GEMM2_CFG>;
 #endif
 using Cfg1n = GCfg<MOE_GEMM1_SMALL_CFG>;
 using Cfg2n = GCfg<MOE_GEMM2_SMALL_CFG>;
-static_assert(Cfg1n::BK == Cfg1::BK && Cfg2n::BK == Cfg2::BK, "same k slicing");
+// (the MFMAs walk k in 16-wide steps in ascending order whatever the slice
+// width BK, so tile families with different BK give the same bits)
 
 // mean rows per expert at or below which the small-row tiles are used
 #ifndef MOE_SMALL_ROWS

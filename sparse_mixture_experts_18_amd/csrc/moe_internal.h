@@ -26,11 +26,9 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
 constexpr int kWave = 64;
 constexpr int kDispatchChunk = 512;  // assignments ranked by one block
 
-// Grouped-GEMM tile geometry.  bf16 path: MFMA tiles; fp32 path: VALU tiles.
-constexpr int kBM = 128;       // rows (assignments) per work item, bf16
-constexpr int kBN1 = 128;      // h columns per GEMM1 work item (256 W1 rows)
-constexpr int kBN2 = 128;      // output columns per GEMM2 work item
-constexpr int kBMf = 32;       // fp32 path
+// Grouped-GEMM tile geometry of the fp32 path (VALU tiles); the bf16 tile
+// families are defined with their kernel.
+constexpr int kBMf = 32;
 constexpr int kBNf = 32;
 
 // one unit of grouped-GEMM work: rows [row0, row0+nrows) of segment `seg`

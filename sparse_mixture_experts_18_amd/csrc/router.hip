@@ -14,30 +14,18 @@ namespace moe {
 namespace {
 
 // ---------------------------------------------------------------------------
-// K1: logits[T,N] = x[T,d] . W_r[N,d]^T, fp32 FMA.  Each output is a single
+// K1 (fp32 layers): logits[T,N] = x[T,d] . W_r[N,d]^T, fp32 FMA.  Each output is a single
 // FMA chain over k = 0..d-1 in order, so a token's logits do not depend on
 // the batch it is in.
 // ---------------------------------------------------------------------------
 constexpr int RT_BM = 64, RT_BN = 64, RT_BK = 16;
 
-template <typename XT>
-__device__ __forceinline__ void load4(const XT* p, float* o);
-template <>
-__device__ __forceinline__ void load4<float>(const float* p, float* o) {
+__device__ __forceinline__ void load4(const float* p, float* o) {
   float4 v = *reinterpret_cast<const float4*>(p);
   o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
 }
-template <>
-__device__ __forceinline__ void load4<bf16_t>(const bf16_t* p, float* o) {
-  uint2 v = *reinterpret_cast<const uint2*>(p);
-  o[0] = __uint_as_float(v.x << 16);
-  o[1] = __uint_as_float(v.x & 0xffff0000u);
-  o[2] = __uint_as_float(v.y << 16);
-  o[3] = __uint_as_float(v.y & 0xffff0000u);
-}
 
-template <typename XT>
-__global__ __launch_bounds__(256) void router_gemm_kernel(const XT* __restrict__ x,
+__global__ __launch_bounds__(256) void router_gemm_kernel(const float* __restrict__ x,
                                                           const float* __restrict__ w,
                                                           float* __restrict__ logits,
                                                           int T, int N, int d) {
@@ -48,13 +36,13 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const XT* __restrict__
   const int lr = tid >> 2, lk = (tid & 3) * 4;  // loader: row, k quad
   const int ty = tid >> 4, tx = tid & 15;       // compute: 4x4 outputs
   const int am = min(m0 + lr, T - 1), bn = min(n0 + lr, N - 1);
-  const XT* xa = x + (size_t)am * d + lk;
+  const float* xa = x + (size_t)am * d + lk;
   const float* wb = w + (size_t)bn * d + lk;
   float acc[4][4] = {};
   for (int k0 = 0; k0 < d; k0 += RT_BK) {
     float a4[4], b4[4];
-    load4<XT>(xa + k0, a4);
-    load4<float>(wb + k0, b4);
+    load4(xa + k0, a4);
+    load4(wb + k0, b4);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       As[lk + i][lr] = a4[i];
@@ -423,7 +411,7 @@ hipError_t launch_router_gemm(const moe_shape& s, const void* x, const float* w_
     }
   } else {
     dim3 grid((T + RT_BM - 1) / RT_BM, (N + RT_BN - 1) / RT_BN);
-    router_gemm_kernel<float><<<grid, 256, 0, st>>>(static_cast<const float*>(x), w_router,
+    router_gemm_kernel<<<grid, 256, 0, st>>>(static_cast<const float*>(x), w_router,
                                                      logits, T, N, d);
   }
   return hipGetLastError();
