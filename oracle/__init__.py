@@ -4,7 +4,8 @@ TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
 benchmark's CPU-baseline leg, never by the product path.
 """
 from .moe_ref import (  # noqa: F401
-    aux_statistic, bias_update, bias_update_seq, capacity, dispatch, gate_weights,
+    aux_statistic, bias_update, bias_update_seq, capacity, dispatch,
+    expert_choice_dispatch, expert_choice_select, gate_weights, moe_layer_ec,
     group_candidates, moe_layer, router_logits, scores_from_logits,
     router_stats, selection_keys, silu, swiglu_ffn, topk_select,
 )

@@ -41,6 +41,11 @@ in the sources):
         ratio logged per expert); "MoE landscape" (paper-daily-site topic
         page), TL;DR and recommendations: dead-expert count, usage CV, token
         drop and router bias norm as first-class indicators.
+  [EC]  "MoE architecture in practice", routing-math section (expert
+        choice routing: each expert takes its top-C tokens by its own
+        capacity; perfectly balanced, no overflow, not causal); "MoE
+        landscape" page (expert choice folds the capacity constraint into the
+        routing).
   [SEQ] "MoE architecture in practice", section "load-balancing loss"
         (update_bias from per-sequence loads, so that long sequences do not
         dominate), and its long-context section (sequence-level balancing).
@@ -519,3 +524,83 @@ def bias_update_seq(bias: np.ndarray, topk_idx: np.ndarray, seq_lens: Sequence[i
     if clamp > 0:
         nb = np.clip(nb, f32(-clamp), f32(clamp)).astype(f32)
     return nb
+
+
+# ---------------------------------------------------------------------------
+# expert-choice routing
+# ---------------------------------------------------------------------------
+
+
+def expert_choice_select(s32: np.ndarray, C: int) -> np.ndarray:
+    """[EC]: every expert e takes the min(C, T) tokens with the largest score
+    s[t, e] (ties to the lower token index, NaN lowest, -0 == +0): the same
+    total order as token choice, read down an expert's column.  Returns the
+    [T, N] boolean choice matrix."""
+    key = np.asarray(s32, f32).copy()
+    key[key == 0] = f32(0.0)
+    T = key.shape[0]
+    r = _ranks(np.ascontiguousarray(key.T))          # [N, T]: rank of t in column e
+    return (r < min(int(C), T)).T
+
+
+def expert_choice_dispatch(chosen: np.ndarray, k: int) -> Dict[str, np.ndarray]:
+    """Segments of the chosen tokens, expert by expert, tokens ascending in a
+    segment (the stable grouping of [EP], one row per (token, expert) pair).
+    perm holds t*k (the flat assignment id of slot 0 of the token, so the
+    expert GEMMs find the token as perm // k); row_of[t, e] is the row of the
+    pair or -1."""
+    T, N = chosen.shape
+    counts = chosen.sum(axis=0).astype(np.int64)
+    offsets = np.zeros(N + 1, np.int64)
+    offsets[1:] = np.cumsum(counts)
+    perm = np.zeros(int(offsets[-1]), np.int64)
+    row_of = np.full((T, N), -1, np.int64)
+    for e in range(N):
+        r = int(offsets[e])
+        for t in range(T):
+            if chosen[t, e]:
+                perm[r] = t * k
+                row_of[t, e] = r
+                r += 1
+    return dict(counts=counts, offsets=offsets, perm=perm, row_of=row_of)
+
+
+def moe_layer_ec(x: np.ndarray, w_router: np.ndarray, w1, w2, *, C: int, k: int,
+                 score_fn: str = "softmax", logit_add: Optional[np.ndarray] = None,
+                 w1_shared: Optional[np.ndarray] = None,
+                 w2_shared: Optional[np.ndarray] = None,
+                 scores_fp32: Optional[np.ndarray] = None,
+                 compute_outputs: bool = True) -> Dict[str, np.ndarray]:
+    """One expert-choice MoE layer forward ([EC]): scores as in token choice,
+    each expert takes its top-C tokens, y_t = sum over the experts that took
+    t of s[t, e] * E_e(x_t) (the raw score is the gate), plus the shared
+    expert; a token no expert took gets only the shared term.  The sum over
+    experts runs in ascending e."""
+    x = np.asarray(x)
+    T = x.shape[0]
+    N = w_router.shape[0]
+    out: Dict[str, np.ndarray] = {}
+    if scores_fp32 is None:
+        l = router_logits(x, w_router, logit_add)
+        s = scores_from_logits(l, score_fn)
+        out["scores"] = s
+        s32 = s.astype(f32)
+    else:
+        s32 = np.asarray(scores_fp32, f32)
+    chosen = expert_choice_select(s32, C)
+    out.update(chosen=chosen, **expert_choice_dispatch(chosen, k))
+    if not compute_outputs:
+        return out
+    d = x.shape[1]
+    y = np.zeros((T, d), np.float64)
+    for e in range(N):
+        t = np.nonzero(chosen[:, e])[0]
+        if t.size == 0:
+            continue
+        w1e, w2e = _expert_weights(w1, w2, e)
+        o = swiglu_ffn(x[t], w1e, w2e)
+        y[t] += s32[t, e].astype(np.float64)[:, None] * o
+    if w1_shared is not None:
+        y += swiglu_ffn(x, w1_shared, w2_shared)
+    out["y"] = y
+    return out

@@ -511,3 +511,82 @@ def test_seq_bias_update_weights_sequences_equally():
     idx2 = np.array([[0], [0], [0], [1]])
     nb = R.bias_update_seq(b, idx2, [2, 2], 1e-3, clamp=5e-4)
     assert nb.tolist() == [np.float32(-5e-4), np.float32(5e-4)]
+
+
+# --------------------------------------------------------- expert choice ---
+
+def test_expert_choice_bruteforce_and_balance():
+    r = rng(41)
+    T, N, C = 9, 5, 3
+    for trial in range(20):
+        s = r.integers(0, 4, size=(T, N)).astype(f32) / 4  # many ties
+        ch = R.expert_choice_select(s, C)
+        assert (ch.sum(axis=0) == C).all()          # perfectly balanced
+        for e in range(N):
+            # brute force: the chosen set is the lexicographically best C-subset
+            # under (score desc, token asc)
+            best = sorted(range(T), key=lambda t: (-float(s[t, e]), t))[:C]
+            assert set(np.nonzero(ch[:, e])[0]) == set(best)
+
+
+def test_expert_choice_nan_and_large_capacity():
+    s = np.array([[np.nan, 0.1], [0.5, np.nan], [-0.0, 0.0]], f32)
+    ch = R.expert_choice_select(s, 2)
+    assert ch[:, 0].tolist() == [False, True, True]     # NaN lowest; -0 == +0 kept by index
+    assert ch[:, 1].tolist() == [True, False, True]
+    assert R.expert_choice_select(s, 10).all()           # C >= T: every token
+
+
+def test_expert_choice_dispatch_segments():
+    r = rng(42)
+    T, N, C, k = 12, 4, 5, 2
+    ch = R.expert_choice_select(r.random((T, N)).astype(f32), C)
+    dsp = R.expert_choice_dispatch(ch, k)
+    assert dsp["offsets"].tolist() == [0, 5, 10, 15, 20]
+    for e in range(N):
+        seg = dsp["perm"][dsp["offsets"][e]:dsp["offsets"][e + 1]] // k
+        assert (np.diff(seg) > 0).all()                   # tokens ascending
+        assert set(seg) == set(np.nonzero(ch[:, e])[0])
+        for t in seg:
+            assert dsp["perm"][dsp["row_of"][t, e]] == t * k
+    assert (dsp["row_of"][~ch] == -1).all()
+
+
+def test_expert_choice_full_capacity_identical_experts_is_dense():
+    """C >= T with softmax scores: every expert takes every token and the
+    gates of a token sum to 1, so identical experts give the dense FFN."""
+    r = rng(43)
+    T, d, N, f = 7, 12, 3, 10
+    x = r.standard_normal((T, d))
+    wr = r.standard_normal((N, d)) / math.sqrt(d)
+    w1 = r.standard_normal((2 * f, d)) / math.sqrt(d)
+    w2 = r.standard_normal((d, f)) / math.sqrt(f)
+    out = R.moe_layer_ec(x, wr, np.stack([w1] * N), np.stack([w2] * N), C=T, k=1)
+    dense = np.zeros((T, d))
+    for t in range(T):
+        for j in range(d):
+            acc = 0.0
+            for c in range(f):
+                g = sum(x[t, i] * w1[c, i] for i in range(d))
+                u = sum(x[t, i] * w1[f + c, i] for i in range(d))
+                acc += w2[j, c] * g / (1.0 + math.exp(-g)) * u
+            dense[t, j] = acc
+    # the gates are fp32 scores: their sum is 1 to within a few fp32 ulps
+    assert np.max(np.abs(out["y"] - dense)) <= 1e-6 * np.max(np.abs(dense))
+
+
+def test_expert_choice_unchosen_token_gets_shared_only():
+    T, d, N, f = 4, 8, 2, 6
+    r = rng(44)
+    x = r.standard_normal((T, d))
+    wr = np.zeros((N, d))
+    w1 = r.standard_normal((N, 2 * f, d))
+    w2 = r.standard_normal((N, d, f))
+    w1s = r.standard_normal((2 * f, d))
+    w2s = r.standard_normal((d, f))
+    # equal scores everywhere: each expert takes the first C tokens by index
+    out = R.moe_layer_ec(x, wr, w1, w2, C=2, k=1, w1_shared=w1s, w2_shared=w2s)
+    assert out["chosen"][:, 0].tolist() == [True, True, False, False]
+    shared = R.swiglu_ffn(x, w1s, w2s)
+    assert np.allclose(out["y"][2:], shared[2:], rtol=0, atol=1e-12)
+    assert not np.allclose(out["y"][:2], shared[:2])
