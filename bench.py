@@ -292,6 +292,29 @@ def main():
                  "avg_ms": round(tl_ms, 4), "algorithmic_bytes": tl_bytes,
                  "GB/s": round(tl_gbs, 1), "hbm_frac": round(tl_gbs / PEAK_HBM_GBS, 4)}
 
+    # expert-choice routing on the same layer: every expert takes its
+    # C = k*T/N tokens (the same number of expert rows as token choice)
+    ec_shape = shape.replace(capacity_factor=1.0, capacity_rule=moe.MOE_CAP_ASSIGNMENTS)
+    expert_choice = None
+    if moe.moe_ec_capacity(ec_shape) * N <= T * k:
+        y_ec = torch.empty_like(out["y"])
+        ws_ec = moe.workspace(ec_shape, dev)
+
+        def ec_step():
+            moe.moe_forward_ec(ec_shape, inp.x, inp.w_router, inp.logit_add, inp.w1, inp.w2,
+                               inp.w1_shared, inp.w2_shared, y_ec, None, None, None, ws_ec)
+        for _ in range(2):
+            ec_step()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.stage_iters):
+            ec_step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ec_ms = e0.elapsed_time(e1) / args.stage_iters
+        expert_choice = {"ms_per_step": round(ec_ms, 4), "tokens/s": round(T / (ec_ms * 1e-3), 1),
+                         "capacity_per_expert": moe.moe_ec_capacity(ec_shape)}
+
     res = {
         "metric": METRIC,
         "value": round(T / (ms * 1e-3), 1),
@@ -319,6 +342,7 @@ def main():
         "roofline": roofline,
         "gemm2": gemm2,
         "telemetry": telemetry,
+        "expert_choice": expert_choice,
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

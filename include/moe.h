@@ -275,6 +275,45 @@ moe_status moe_bias_update_seq(const moe_shape* shape, const int32_t* topk_idx,
                                int32_t* err_out, void* ws, size_t ws_bytes,
                                void* stream);
 
+/* Expert-choice routing ("MoE architecture in practice", routing-math
+ * section: each expert takes the top-C tokens its capacity allows, perfectly
+ * balanced, no overflow, not causal; "MoE landscape" page).  Scores as in
+ * token choice (score_fn; logit_add), then every expert e takes the
+ * Cp = min(C, T) tokens with the largest s[t, e] -- ties to the lower token,
+ * NaN lowest, -0 == +0 -- where C = moe_capacity(shape) (capacity_factor > 0
+ * required).  The raw score is the gate; a token no expert took gets only the
+ * shared expert.  top_k only sizes the buffers (N*Cp <= T*top_k required,
+ * else MOE_ERR_UNSUPPORTED); the selection bias and the group limit do not
+ * apply.
+ * moe_ec_capacity: Cp, or -1 for an invalid shape or no capacity.
+ * moe_route_ec outputs (all required): counts [N] (= Cp each), offsets [N+1]
+ *   (e*Cp), perm [T*top_k] (rows [0, N*Cp): t*top_k for the token of the
+ *   row, segment by segment, tokens ascending -- the layout moe_expert_ffn
+ *   reads), row_of [T, N] int32 (row of the pair, -1 if e did not take t);
+ *   scores_out [T, N] optional; scores_in replaces the router (as in
+ *   moe_route).
+ * moe_combine_ec: y_t = sum over e ascending with row_of[t,e] >= 0 of
+ *   scores[t,e] * y_perm[row_of[t,e]] (+ y_shared_t), fp32 accumulation.
+ * moe_forward_ec: route_ec -> expert FFNs -> combine_ec on `stream`;
+ *   scores_out, offsets, row_of optional outputs. */
+int64_t moe_ec_capacity(const moe_shape* shape);
+moe_status moe_route_ec(const moe_shape* shape, const void* x,
+                        const float* w_router, const float* logit_add,
+                        const float* scores_in, float* scores_out,
+                        int32_t* counts, int32_t* offsets, int32_t* perm,
+                        int32_t* row_of, void* ws, size_t ws_bytes,
+                        void* stream);
+moe_status moe_combine_ec(const moe_shape* shape, const void* y_perm,
+                          const void* y_shared, const int32_t* row_of,
+                          const float* scores, void* y, void* stream);
+moe_status moe_forward_ec(const moe_shape* shape, const void* x,
+                          const float* w_router, const float* logit_add,
+                          const void* w1, const void* w2,
+                          const void* w1_shared, const void* w2_shared,
+                          void* y, float* scores_out, int32_t* offsets,
+                          int32_t* row_of, void* ws, size_t ws_bytes,
+                          void* stream);
+
 /* The whole layer: route -> dispatch -> expert FFNs -> combine on `stream`.
  * Required: x, w_router, w1, w2, y (and the shared weights iff
  * d_ff_shared > 0).  Optional inputs logit_add, bias; optional outputs

@@ -10,7 +10,8 @@ argument order, tensors in place of pointers):
 
     moe_route, moe_dispatch, moe_expert_plan, moe_expert_ffn, moe_expert_gate_up,
     moe_expert_down, moe_combine, moe_bias_update, moe_bias_update_seq,
-    moe_router_stats, moe_router_stats_count, moe_forward,
+    moe_router_stats, moe_router_stats_count, moe_route_ec, moe_combine_ec,
+    moe_forward_ec, moe_ec_capacity, moe_forward,
     moe_workspace_bytes, moe_check_shape, moe_capacity, moe_status_string,
     moe_abi_version
 
@@ -117,6 +118,12 @@ _SIGS = {
                                         _P]),
     "moe_bias_update_seq": (ctypes.c_int, [_S, _P, _P, ctypes.c_int32, ctypes.c_float,
                                            ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_ec_capacity": (ctypes.c_int64, [_S]),
+    "moe_route_ec": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                    _P]),
+    "moe_combine_ec": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P]),
+    "moe_forward_ec": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                      ctypes.c_size_t, _P]),
     "moe_forward": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                    _P, _P, _P, _P, ctypes.c_size_t, _P]),
 }
@@ -317,6 +324,54 @@ def moe_bias_update_seq(shape, topk_idx, seq_offsets, step, clamp, bias, err_out
         _ptr(bias, "bias", torch.float32, N), _ptr(err_out, "err_out", torch.int32, 1), p, n,
         _stream(stream))
     _check(st, "moe_bias_update_seq")
+
+
+def moe_ec_capacity(shape: MoeShape) -> int:
+    return lib().moe_ec_capacity(ctypes.byref(shape))
+
+
+def moe_route_ec(shape, x, w_router, logit_add, scores_in, scores_out, counts, offsets, perm,
+                 row_of, ws, stream=None):
+    T, N, k = shape.T, shape.n_experts, shape.top_k
+    p, n = _ws(ws)
+    st = lib().moe_route_ec(
+        ctypes.byref(shape), _ptr(x, "x", _dt(shape), T * shape.d_model),
+        _ptr(w_router, "w_router", torch.float32, N * shape.d_model),
+        _ptr(logit_add, "logit_add", torch.float32, T * N),
+        _ptr(scores_in, "scores_in", torch.float32, T * N),
+        _ptr(scores_out, "scores_out", torch.float32, T * N),
+        _ptr(counts, "counts", torch.int32, N), _ptr(offsets, "offsets", torch.int32, N + 1),
+        _ptr(perm, "perm", torch.int32, T * k), _ptr(row_of, "row_of", torch.int32, T * N),
+        p, n, _stream(stream))
+    _check(st, "moe_route_ec")
+
+
+def moe_combine_ec(shape, y_perm, y_shared, row_of, scores, y, stream=None):
+    T, N, k, d = shape.T, shape.n_experts, shape.top_k, shape.d_model
+    dt = _dt(shape)
+    st = lib().moe_combine_ec(
+        ctypes.byref(shape), _ptr(y_perm, "y_perm", dt, T * k * d),
+        _ptr(y_shared, "y_shared", dt, T * d), _ptr(row_of, "row_of", torch.int32, T * N),
+        _ptr(scores, "scores", torch.float32, T * N), _ptr(y, "y", dt, T * d), _stream(stream))
+    _check(st, "moe_combine_ec")
+
+
+def moe_forward_ec(shape, x, w_router, logit_add, w1, w2, w1_shared, w2_shared, y, scores_out,
+                   offsets, row_of, ws, stream=None):
+    T, N, k, d, f, fs = (shape.T, shape.n_experts, shape.top_k, shape.d_model, shape.d_ff,
+                         shape.d_ff_shared)
+    dt = _dt(shape)
+    p, n = _ws(ws)
+    st = lib().moe_forward_ec(
+        ctypes.byref(shape), _ptr(x, "x", dt, T * d),
+        _ptr(w_router, "w_router", torch.float32, N * d),
+        _ptr(logit_add, "logit_add", torch.float32, T * N), _ptr(w1, "w1", dt, N * 2 * f * d),
+        _ptr(w2, "w2", dt, N * d * f), _ptr(w1_shared, "w1_shared", dt, 2 * fs * d),
+        _ptr(w2_shared, "w2_shared", dt, d * fs), _ptr(y, "y", dt, T * d),
+        _ptr(scores_out, "scores_out", torch.float32, T * N),
+        _ptr(offsets, "offsets", torch.int32, N + 1), _ptr(row_of, "row_of", torch.int32, T * N),
+        p, n, _stream(stream))
+    _check(st, "moe_forward_ec")
 
 
 def moe_combine(shape, y_perm, y_shared, slot, topk_w, y, stream=None):

@@ -105,6 +105,7 @@ Workspace layout_workspace(const moe_shape& s, void* ws) {
   w.router_part = static_cast<float*>(take((size_t)router_split_chunks(s) * T * N * 4));
   w.stats_rows = static_cast<double*>(take((A + T) * 4 * 8));
   w.stats_ent = static_cast<double*>(take(T * 2 * 8));
+  w.ec_row = static_cast<int32_t*>(take(T * N * 4));
   w.total = off;
   return w;
 }
@@ -320,6 +321,109 @@ moe_status moe_bias_update_seq(const moe_shape* shape, const int32_t* topk_idx,
   if ((st = check_ws(shape, ws, ws_bytes, w)) != MOE_OK) return st;
   return hip_status(launch_bias_update_seq(*shape, topk_idx, seq_offsets, n_seq, step, clamp,
                                            bias, err_out, w, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+namespace {
+// expert choice needs a capacity, and its N*min(C,T) rows must fit the T*k
+// rows the buffers hold
+moe_status check_ec(const moe_shape* shape) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const int64_t Cp = ec_capacity(*shape);
+  if (Cp <= 0) return MOE_ERR_INVALID;
+  if (Cp * shape->n_experts > shape->T * (int64_t)shape->top_k) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// scores of every (token, expert) pair: the token-choice scores, without a
+// selection (a top-1 pass whose picks are discarded)
+hipError_t ec_scores(const moe_shape& sh, const void* x, const float* w_router,
+                     const float* logit_add, float* scores, const Workspace& w, hipStream_t s) {
+  moe_shape s1 = sh;
+  s1.top_k = 1;
+  s1.n_groups = 1;
+  s1.topk_groups = 1;
+  s1.renormalize = 1;
+  int np = 1;
+  hipError_t e = launch_router_gemm(s1, x, w_router, w.logits, w, s, &np);
+  if (e != hipSuccess) return e;
+  return launch_topk(s1, np > 1 ? w.router_part : w.logits, np, nullptr, logit_add, false,
+                     nullptr, scores, w.topk_idx, w.topk_w, s);
+}
+}  // namespace
+
+extern "C" {
+
+int64_t moe_ec_capacity(const moe_shape* shape) {
+  if (check_shape(shape) != MOE_OK) return -1;
+  return ec_capacity(*shape);
+}
+
+moe_status moe_route_ec(const moe_shape* shape, const void* x, const float* w_router,
+                        const float* logit_add, const float* scores_in, float* scores_out,
+                        int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* row_of,
+                        void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_ec(shape);
+  if (st != MOE_OK) return st;
+  if (!counts || !offsets || !perm || !row_of) return MOE_ERR_INVALID;
+  if (!scores_in && (!x || !w_router)) return MOE_ERR_INVALID;
+  if (!aligned16({x, w_router}) ||
+      !aligned4({logit_add, scores_in, scores_out, counts, offsets, perm, row_of}))
+    return MOE_ERR_INVALID;
+  Workspace w;
+  if ((st = check_ws(shape, ws, ws_bytes, w)) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float* sc = scores_in;
+  if (!sc) {
+    float* so = scores_out ? scores_out : w.scores;
+    if (ec_scores(*shape, x, w_router, logit_add, so, w, s) != hipSuccess) return MOE_ERR_HIP;
+    sc = so;
+  }
+  return hip_status(launch_ec_select(*shape, sc, counts, offsets, perm, row_of, w, s));
+}
+
+moe_status moe_combine_ec(const moe_shape* shape, const void* y_perm, const void* y_shared,
+                          const int32_t* row_of, const float* scores, void* y, void* stream) {
+  moe_status st = check_ec(shape);
+  if (st != MOE_OK) return st;
+  if (!y_perm || !row_of || !scores || !y) return MOE_ERR_INVALID;
+  if (shape->d_ff_shared > 0 && !y_shared) return MOE_ERR_INVALID;
+  if (!aligned16({y_perm, y_shared, y}) || !aligned4({row_of, scores})) return MOE_ERR_INVALID;
+  return hip_status(launch_ec_combine(*shape, y_perm, shape->d_ff_shared > 0 ? y_shared : nullptr,
+                                      row_of, scores, y, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_forward_ec(const moe_shape* shape, const void* x, const float* w_router,
+                          const float* logit_add, const void* w1, const void* w2,
+                          const void* w1_shared, const void* w2_shared, void* y,
+                          float* scores_out, int32_t* offsets, int32_t* row_of, void* ws,
+                          size_t ws_bytes, void* stream) {
+  moe_status st = check_ec(shape);
+  if (st != MOE_OK) return st;
+  if (!x || !w_router || !w1 || !w2 || !y) return MOE_ERR_INVALID;
+  if (shape->d_ff_shared > 0 && (!w1_shared || !w2_shared)) return MOE_ERR_INVALID;
+  if (!aligned16({x, w_router, w1, w2, w1_shared, w2_shared, y}) ||
+      !aligned4({logit_add, scores_out, offsets, row_of}))
+    return MOE_ERR_INVALID;
+  Workspace w;
+  if ((st = check_ws(shape, ws, ws_bytes, w)) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const moe_shape& sh = *shape;
+  float* sc = scores_out ? scores_out : w.scores;
+  int32_t* of = offsets ? offsets : w.offsets;
+  int32_t* ro = row_of ? row_of : w.ec_row;
+  const bool shared = sh.d_ff_shared > 0;
+  if (ec_scores(sh, x, w_router, logit_add, sc, w, s) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_ec_select(sh, sc, w.counts, of, w.perm, ro, w, s) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_plan(sh, of, w, s) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_gemm1(sh, x, w.perm, w1, w1_shared, w.h, w.h_shared, w, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (launch_gemm2(sh, w.h, w.h_shared, w2, w2_shared, w.y_perm, shared ? w.y_shared : nullptr,
+                   w, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  return hip_status(launch_ec_combine(sh, w.y_perm, shared ? w.y_shared : nullptr, ro, sc, y, s));
 }
 
 moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_router,

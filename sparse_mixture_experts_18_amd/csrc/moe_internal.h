@@ -63,6 +63,7 @@ struct Workspace {
   float* router_part;  // [chunks][T][N] partial logits of the split router GEMM
   double* stats_rows;  // [T*k + T][4] per-row output moments (telemetry)
   double* stats_ent;   // [T][2] per-token gate / score entropy (telemetry)
+  int32_t* ec_row;     // [T][N] row of each (token, expert) pair, expert choice
   size_t total;
   int64_t plan1_cap, plan2_cap;
 };
@@ -109,5 +110,14 @@ hipError_t launch_router_stats(const moe_shape& s, const int32_t* counts, const 
 hipError_t launch_bias_update_seq(const moe_shape& s, const int32_t* topk_idx,
                                   const int32_t* seq_off, int n_seq, float step, float clamp,
                                   float* bias, int32_t* err, const Workspace& w, hipStream_t st);
+
+// expert choice: per-expert capacity min(C, T) (-1 without a capacity)
+int64_t ec_capacity(const moe_shape& s);
+hipError_t launch_ec_select(const moe_shape& s, const float* scores, int32_t* counts,
+                            int32_t* offsets, int32_t* perm, int32_t* row_of, const Workspace& w,
+                            hipStream_t st);
+hipError_t launch_ec_combine(const moe_shape& s, const void* y_perm, const void* y_shared,
+                             const int32_t* row_of, const float* scores, void* y,
+                             hipStream_t st);
 
 }  // namespace moe
