@@ -8,4 +8,6 @@ from .moe_ref import (  # noqa: F401
     expert_choice_dispatch, expert_choice_select, gate_weights, moe_layer_ec,
     group_candidates, moe_layer, router_logits, scores_from_logits,
     router_stats, selection_keys, silu, swiglu_ffn, topk_select,
+    MX_BLOCK, E4M3_MAX, e4m3_decode, e4m3_encode, mx_quantize, mx_dequantize,
+    mx_round, swiglu_ffn_mx,
 )

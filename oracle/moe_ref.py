@@ -46,6 +46,15 @@ in the sources):
         capacity; perfectly balanced, no overflow, not causal); "MoE
         landscape" page (expert choice folds the capacity constraint into the
         routing).
+  [FP8] "MoE common taste of open models", section 2 (FP8/MXFP8 expert
+        compute listed as a strong candidate) and its closing recipe table
+        (router kept in FP32, or at least protected, when the rest is
+        quantised); "MoE architecture in practice", precision section (FP8
+        for the forward matrix products with the gate GEMM kept at higher
+        precision).  The number format is the one the name refers to: the
+        OCP Microscaling Formats (MX) v1.0 specification, MXFP8 = E4M3
+        elements sharing one E8M0 power-of-two scale per 32 consecutive
+        values.
   [SEQ] "MoE architecture in practice", section "load-balancing loss"
         (update_bias from per-sequence loads, so that long sequences do not
         dominate), and its long-context section (sequence-level balancing).
@@ -269,6 +278,106 @@ def swiglu_ffn(x_rows: np.ndarray, w1: np.ndarray, w2: np.ndarray) -> np.ndarray
     return (silu(a) * u) @ w2.T
 
 
+# ---------------------------------------------------------------------------
+# MXFP8 ([FP8]): E4M3 elements, one E8M0 scale per 32 consecutive values
+# ---------------------------------------------------------------------------
+MX_BLOCK = 32
+E4M3_MAX = 448.0     # 1.75 * 2^8, the largest finite E4M3 magnitude
+E4M3_EMAX = 8        # exponent of the largest normal binade
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Value of each E4M3 code: sign bit, 4 exponent bits with bias 7, 3
+    mantissa bits; exponent field 0 holds subnormals m * 2^-9; the two codes
+    with all exponent and mantissa bits set are NaN (there is no infinity)."""
+    c = np.asarray(codes, np.uint8).astype(np.int64)
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    v = np.where(c & 0x80, -mag, mag)
+    return np.where((c & 0x7F) == 0x7F, np.nan, v)
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """Nearest E4M3 code of each value, ties to the even mantissa; magnitudes
+    beyond 448 saturate to 448; NaN gives the NaN code; the sign bit is kept
+    (so -0 and negative values that round to zero give 0x80)."""
+    v = np.asarray(v, np.float64)
+    neg = np.signbit(v)
+    nan = np.isnan(v)
+    a = np.where(nan, 0.0, np.abs(v))
+    # binade of a (subnormals share the lowest normal binade, 2^-6): the
+    # spacing of E4M3 numbers there is 2^(binade - 3)
+    _, e = np.frexp(a)                      # a = m 2^e, m in [0.5, 1)
+    b = np.maximum(e - 1, -6)
+    q = np.ldexp(np.rint(np.ldexp(a, 3 - b)), b - 3)   # exact scalings, RNE
+    q = np.minimum(q, E4M3_MAX)
+    # code of the rounded magnitude q (a rounding carry may have moved it up
+    # one binade, so its binade is taken again)
+    _, e2 = np.frexp(q)
+    b2 = e2 - 1
+    sub = q < 2.0 ** -6
+    mant = np.where(sub, 0.0, np.ldexp(q, -b2) - 1.0) * 8.0
+    code = np.where(sub, np.ldexp(q, 9), (b2 + 7) * 8 + mant)
+    code = code.astype(np.int64)
+    code = np.where(nan, 0x7F, code)
+    return (code | np.where(neg, 0x80, 0)).astype(np.uint8)
+
+
+def mx_quantize(v) -> Tuple[np.ndarray, np.ndarray]:
+    """MXFP8 quantisation along the last axis (length a multiple of 32), the
+    OCP MX v1.0 conversion: each block of 32 gets the shared exponent
+    X = floor(log2(max |v|)) - 8 (8 = exponent of the largest E4M3 binade),
+    clamped to the E8M0 range [-127, 127]; each element becomes the E4M3
+    code of v / 2^X (e4m3_encode: nearest, ties to even, saturating).
+    Readings for the cases the definition leaves open: an all-zero block
+    takes X = -127; NaN elements do not enter the maximum and give the NaN
+    code; a block holding an infinity takes X = 127.  Returns (codes
+    [..., K] uint8, scales [..., K/32] uint8 holding X + 127)."""
+    v = np.asarray(v, np.float64)
+    K = v.shape[-1]
+    if K % MX_BLOCK:
+        raise ValueError("MX blocks need a multiple of 32 values")
+    blk = v.reshape(v.shape[:-1] + (K // MX_BLOCK, MX_BLOCK))
+    a = np.abs(blk)
+    amax = np.max(np.where(np.isnan(a), 0.0, a), axis=-1)
+    _, e = np.frexp(np.where(np.isfinite(amax), amax, 1.0))
+    X = np.where(amax > 0, e - 1 - E4M3_EMAX, -127)
+    X = np.where(np.isinf(amax), 127, X)
+    X = np.clip(X, -127, 127).astype(np.int64)
+    codes = e4m3_encode(np.ldexp(blk, -X[..., None]))
+    return codes.reshape(v.shape), (X + 127).astype(np.uint8)
+
+
+def mx_dequantize(codes, scales) -> np.ndarray:
+    """Value of an MXFP8 tensor: code value * 2^(scale - 127), blocks of 32
+    along the last axis."""
+    c = np.asarray(codes, np.uint8)
+    X = np.asarray(scales, np.int64) - 127
+    K = c.shape[-1]
+    vals = e4m3_decode(c).reshape(c.shape[:-1] + (K // MX_BLOCK, MX_BLOCK))
+    return np.ldexp(vals, X[..., None]).reshape(c.shape)
+
+
+def mx_round(v) -> np.ndarray:
+    """v rounded through MXFP8 (quantise, then dequantise)."""
+    return mx_dequantize(*mx_quantize(v))
+
+
+def swiglu_ffn_mx(x_rows: np.ndarray, w1: np.ndarray, w2: np.ndarray) -> np.ndarray:
+    """An MXFP8 expert ([FP8]): both operands of each matrix product are MXFP8
+    with blocks along the reduction axis.  The weights arrive already rounded
+    through MXFP8 (w1 [2*d_ff, d], w2 [d, d_ff]); the token rows are rounded
+    here along d, the SwiGLU intermediate along d_ff; products, SiLU and sums
+    in fp64."""
+    x = mx_round(np.asarray(x_rows, np.float64))
+    w1 = np.asarray(w1, np.float64)
+    w2 = np.asarray(w2, np.float64)
+    f = w1.shape[0] // 2
+    h = silu(x @ w1[:f].T) * (x @ w1[f:].T)
+    return mx_round(h) @ w2.T
+
+
 WeightSource = Union[Tuple[np.ndarray, np.ndarray],
                      Callable[[int], Tuple[np.ndarray, np.ndarray]]]
 
@@ -289,9 +398,12 @@ def moe_layer(x: np.ndarray, w_router: np.ndarray, w1, w2, *, top_k: int,
               w2_shared: Optional[np.ndarray] = None,
               scores_fp32: Optional[np.ndarray] = None,
               tokens: Optional[Sequence[int]] = None,
-              compute_outputs: bool = True) -> Dict[str, np.ndarray]:
+              compute_outputs: bool = True,
+              ffn: Callable = swiglu_ffn) -> Dict[str, np.ndarray]:
     """One MoE FFN layer forward ([G] y = sum_i g_i E_i(x), [SE] plus the
-    shared expert).
+    shared expert).  ``ffn`` is the expert function of the routed and shared
+    experts: swiglu_ffn, or swiglu_ffn_mx for MXFP8 experts (with the router
+    unchanged: fp32 scores from the unquantised x, [FP8]).
 
     x [T, d]; w_router [N, d]; w1 [N, 2*d_ff, d] and w2 [N, d, d_ff], or w1 a
     callable e -> (w1_e, w2_e) (w2 ignored) so that weights can be streamed one
@@ -344,14 +456,14 @@ def moe_layer(x: np.ndarray, w_router: np.ndarray, w1, w2, *, top_k: int,
         t = a // top_k
         j = a % top_k
         w1e, w2e = _expert_weights(w1, w2, e)
-        o = swiglu_ffn(x[t], w1e, w2e)
+        o = ffn(x[t], w1e, w2e)
         # accumulate in ascending-j order per token: add the j-th term of each
         # token one j at a time
         for jj in range(top_k):
             m = j == jj
             y[t[m]] += g[t[m], jj][:, None] * o[m]
     if w1_shared is not None:
-        y[rows] += swiglu_ffn(x[rows], w1_shared, w2_shared)
+        y[rows] += ffn(x[rows], w1_shared, w2_shared)
     out["y"] = y[rows]
     out["rows"] = rows
     out["keep2d"] = keep

@@ -590,3 +590,163 @@ def test_expert_choice_unchosen_token_gets_shared_only():
     shared = R.swiglu_ffn(x, w1s, w2s)
     assert np.allclose(out["y"][2:], shared[2:], rtol=0, atol=1e-12)
     assert not np.allclose(out["y"][:2], shared[:2])
+
+
+# ------------------------------------------------------------------ MXFP8 ---
+
+def _torch():
+    return pytest.importorskip("torch")
+
+
+def test_e4m3_decode_matches_library_type():
+    """All 256 codes against the library's float8 E4M3 (OCP 'fn') type."""
+    torch = _torch()
+    c = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(c).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(R.e4m3_decode(c), ref, equal_nan=True)
+    assert R.e4m3_decode(np.uint8(0x7E)) == 448.0 and R.e4m3_decode(np.uint8(0x01)) == 2.0 ** -9
+
+
+def test_e4m3_encode_matches_library_cast_in_range():
+    """Round to nearest, ties to even, against the library's cast, on random
+    values of every binade and on every midpoint between neighbouring codes."""
+    torch = _torch()
+    r = rng(50)
+    v = (r.standard_normal(100000) * np.exp2(r.integers(-14, 9, 100000))).astype(f32)
+    vals = np.unique(R.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8)))
+    mids = ((vals[1:] + vals[:-1]) / 2).astype(f32)
+    assert np.array_equal(mids.astype(np.float64), (vals[1:] + vals[:-1]) / 2)
+    v = np.concatenate([v, mids, -mids, vals.astype(f32)])
+    v = v[np.abs(v) <= 448]
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(R.e4m3_encode(v), ref)
+
+
+def test_e4m3_encode_saturation_and_specials():
+    v = np.array([1000.0, -449.0, 464.0, 479.0, np.nan, -np.nan, -0.0, 0.0, -1e-30,
+                  2.0 ** -10, 3 * 2.0 ** -10])
+    assert R.e4m3_encode(v).tolist() == [0x7E, 0xFE, 0x7E, 0x7E, 0x7F, 0xFF, 0x80, 0x00,
+                                         0x80, 0x00, 0x02]
+
+
+def test_mx_quantize_is_nearest_by_brute_force():
+    """Every element's code is a nearest of the 254 finite codes times the
+    block scale 2^X (ties to the even mantissa), or 448 when it lies beyond;
+    X = floor(log2 max|v|) - 8 per block of 32 consecutive values."""
+    r = rng(51)
+    v = r.standard_normal((6, 128)) * np.exp2(r.integers(-20, 20, (6, 1)))
+    v[0, :32] *= np.exp2(r.integers(-30, 0, 32))      # a block with a wide spread
+    codes, scales = R.mx_quantize(v)
+    fin = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    grid = R.e4m3_decode(fin)
+    for i in range(v.shape[0]):
+        for b in range(v.shape[1] // 32):
+            blk = v[i, 32 * b:32 * b + 32]
+            m, e = math.frexp(float(np.max(np.abs(blk))))
+            X = e - 1 - 8
+            assert int(scales[i, b]) == X + 127
+            for j in range(32):
+                s = blk[j] / 2.0 ** X
+                got = R.e4m3_decode(codes[i, 32 * b + j])
+                if abs(s) > 448:
+                    assert got == math.copysign(448.0, s)
+                    continue
+                dist = np.abs(grid - s)
+                best = dist.min()
+                assert abs(got - s) == best
+                ties = fin[dist == best]
+                if len(set(R.e4m3_decode(ties).tolist())) > 1:  # a true tie: even mantissa
+                    assert codes[i, 32 * b + j] % 2 == 0
+
+
+def test_mx_quantize_closed_forms():
+    # a power-of-two maximum 2^k: X = k - 8 and that element is 1.0 * 2^8
+    blk = np.full(32, 0.001)
+    blk[7] = 2.0 ** 5
+    c, s = R.mx_quantize(blk)
+    assert int(s[0]) == 127 + 5 - 8 and c[7] == 0x78
+    # 448 * 2^j is exact; 480 * 2^j exceeds the top code after scaling and saturates
+    blk[7] = 448.0 * 2.0 ** -3
+    c, s = R.mx_quantize(blk)
+    assert int(s[0]) == 127 - 3 and c[7] == 0x7E
+    blk[7] = -480.0 * 2.0 ** -3
+    c, s = R.mx_quantize(blk)
+    assert int(s[0]) == 127 - 3 and c[7] == 0xFE
+    # all zero (and negative zero): X = -127, codes keep the sign
+    c, s = R.mx_quantize(np.array([0.0, -0.0] * 16))
+    assert int(s[0]) == 0 and c.tolist() == [0x00, 0x80] * 16
+    # NaN is left out of the maximum and keeps the NaN code; an infinity gives X = 127
+    blk = np.linspace(-1, 1, 32)
+    blk[3] = np.nan
+    c, s = R.mx_quantize(blk)
+    assert c[3] == 0x7F and int(s[0]) == 127 + 0 - 8
+    blk[3] = -np.inf
+    c, s = R.mx_quantize(blk)
+    assert int(s[0]) == 254 and c[3] == 0xFE and (c[np.arange(32) != 3] & 0x7F == 0).all()
+
+
+def test_mx_round_trip_of_representable_blocks():
+    """Codes times 2^X, with one element in the top binade, quantise back to
+    the same codes and scale."""
+    r = rng(52)
+    fin = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    for _ in range(50):
+        c = r.choice(fin, 64)
+        c[r.integers(0, 32)] = 0x78 | r.integers(0, 7)
+        c[32 + r.integers(0, 32)] = 0xF8 | r.integers(0, 7)
+        s = r.integers(1, 254, 2).astype(np.uint8)
+        v = R.mx_dequantize(c, s)
+        c2, s2 = R.mx_quantize(v)
+        assert np.array_equal(s2, s)
+        assert np.array_equal(R.e4m3_decode(c2), R.e4m3_decode(c))
+
+
+def test_mx_error_bound():
+    """|q - v| <= 2^-4 |v| in the normal range of the block, <= 2^(X-10) below."""
+    r = rng(53)
+    v = r.standard_normal((64, 256)) * np.exp2(r.integers(-8, 8, (64, 256)))
+    c, s = R.mx_quantize(v)
+    q = R.mx_dequantize(c, s)
+    X = np.repeat(s.astype(np.int64) - 127, 32, axis=1)
+    sc = np.abs(v) / np.exp2(X)
+    normal = (sc >= 2.0 ** -6) & (sc <= 448)
+    assert (np.abs(q - v)[normal] <= 2.0 ** -4 * np.abs(v)[normal]).all()
+    assert (np.abs(q - v)[~normal & (sc < 1)] <= np.exp2(X - 10)[~normal & (sc < 1)]).all()
+
+
+def test_swiglu_ffn_mx_explicit_loops():
+    """The MXFP8 expert: token rows rounded along d, h along d_ff (each row
+    quantised on its own here, in blocks of 32), products in loops."""
+    r = rng(54)
+    d, f, n = 64, 96, 3
+    x = r.standard_normal((n, d))
+    w1 = R.mx_round(r.standard_normal((2 * f, d)) / 8)
+    w2 = R.mx_round(r.standard_normal((d, f)) / 8)
+    got = R.swiglu_ffn_mx(x, w1, w2)
+    for t in range(n):
+        xq = R.mx_dequantize(*R.mx_quantize(x[t]))
+        h = np.zeros(f)
+        for c in range(f):
+            a = sum(xq[i] * w1[c, i] for i in range(d))
+            u = sum(xq[i] * w1[f + c, i] for i in range(d))
+            h[c] = a / (1 + math.exp(-a)) * u
+        hq = R.mx_dequantize(*R.mx_quantize(h))
+        for j in range(d):
+            ref = sum(hq[c] * w2[j, c] for c in range(f))
+            assert abs(got[t, j] - ref) <= 1e-12 * (1 + abs(ref))
+
+
+def test_moe_layer_mx_close_to_unquantised_layer():
+    """MXFP8 experts change the output by the format's rounding only (a few
+    per cent), and the routing not at all (the router stays fp32)."""
+    r = rng(55)
+    T, d, N, f, k = 40, 64, 6, 64, 2
+    x = r.standard_normal((T, d))
+    wr = r.standard_normal((N, d)) / 8
+    w1 = R.mx_round(r.standard_normal((N, 2 * f, d)) / 8)
+    w2 = R.mx_round(r.standard_normal((N, d, f)) / 8)
+    a = R.moe_layer(x, wr, w1, w2, top_k=k)
+    b = R.moe_layer(x, wr, w1, w2, top_k=k, ffn=R.swiglu_ffn_mx)
+    assert np.array_equal(a["topk_idx"], b["topk_idx"])
+    err = np.linalg.norm(a["y"] - b["y"]) / np.linalg.norm(a["y"])
+    assert 1e-3 < err < 0.08
