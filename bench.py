@@ -18,6 +18,10 @@ Extra fields beside the contract's:
                 8 TB/s HBM peak, or FLOPs at the dense bf16 MFMA peak.
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload,
                 timed on this host's cores
+  mxfp8         the same layer with MXFP8 experts (weights quantised once,
+                router unchanged): forward rate and the expert projections
+                against the fp8 MFMA and HBM peaks
+  expert_choice the same layer routed by expert choice at C = k*T/N
 """
 from __future__ import annotations
 
@@ -31,6 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 METRIC = "MoE layer fwd tokens/s + TFLOP/s (% bf16 MFMA peak), DeepSeek-V3 shape"
@@ -270,7 +275,7 @@ def main():
                     "unit": "TFLOP/s", "frac": round(tfs / peak_fl, 4), "traffic": traffic,
                     "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
     roofline.update({
-        "kernel": "gemm_bf16_kernel<true> (gate/up projection + SwiGLU over every expert "
+        "kernel": "gemm_mfma_kernel<true, false, .> (bf16 gate/up projection + SwiGLU over every expert "
                   "segment and the shared expert; one launch per call, work list prebuilt)",
         "avg_ms": round(g1_ms, 4),
         "flops_per_launch": g1_flops,
@@ -278,7 +283,7 @@ def main():
         "touched_experts": touched,
         "min_ms_at_peaks": round(max(t_hbm, t_mfma) * 1e3, 4),
     })
-    gemm2 = {"kernel": "gemm_bf16_kernel<false> (down projection)", "avg_ms": round(g2_ms, 4),
+    gemm2 = {"kernel": "gemm_mfma_kernel<false, false, .> (bf16 down projection)", "avg_ms": round(g2_ms, 4),
              "tflops": round(g2_flops / (g2_ms * 1e-3) / 1e12, 2)}
 
     # router telemetry over this forward's outputs (HBM-bound: it reads the
@@ -315,6 +320,65 @@ def main():
         expert_choice = {"ms_per_step": round(ec_ms, 4), "tokens/s": round(T / (ec_ms * 1e-3), 1),
                          "capacity_per_expert": moe.moe_ec_capacity(ec_shape)}
 
+    # MXFP8 experts on the same layer (router unchanged): the bf16 weights
+    # quantised once by moe_quantize_mx, then the same forward and the two
+    # expert projections timed as above
+    mxfp8 = None
+    if cfg.dtype == "bf16" and d % 128 == 0 and cfg.d_ff % 128 == 0 and \
+            cfg.d_ff_shared % 128 == 0:
+        mx_shape = shape.replace(dtype=moe.MOE_DTYPE_MXFP8)
+        ws_mx = moe.workspace(mx_shape, dev)
+        w1q, w2q = moe.quantize_mx(inp.w1), moe.quantize_mx(inp.w2)
+        w1sq = moe.quantize_mx(inp.w1_shared) if cfg.d_ff_shared else None
+        w2sq = moe.quantize_mx(inp.w2_shared) if cfg.d_ff_shared else None
+        y_mx = torch.empty_like(out["y"])
+
+        def mx_step():
+            moe.moe_forward(mx_shape, inp.x, inp.w_router, inp.logit_add, inp.bias, w1q, w2q,
+                            w1sq, w2sq, y_mx, None, None, None, None, None, None, None, ws_mx)
+        for _ in range(2):
+            mx_step()
+        g_mx = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_mx):
+            mx_step()
+        for _ in range(2):
+            g_mx.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            g_mx.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        mx_ms = e0.elapsed_time(e1) / args.steps
+        del g_mx
+        hq = torch.empty(moe.mx_bytes(T * k * cfg.d_ff), dtype=torch.uint8, device=dev)
+        hsq = (torch.empty(moe.mx_bytes(T * cfg.d_ff_shared), dtype=torch.uint8, device=dev)
+               if cfg.d_ff_shared else None)
+        moe.moe_expert_plan(mx_shape, of, ws_mx)
+        m1_ms = timed(lambda: moe.moe_expert_gate_up(mx_shape, inp.x, pm, None, w1q, w1sq, hq,
+                                                     hsq, ws_mx), args.stage_iters)
+        m2_ms = timed(lambda: moe.moe_expert_down(mx_shape, hq, hsq, None, w2q, w2sq, yp, ysh,
+                                                  ws_mx), args.stage_iters)
+        mxb = 33.0 / 32.0  # bytes per MXFP8 value with its share of a scale
+        m1_bytes = mxb * (touched * 2 * cfg.d_ff * d + 2 * cfg.d_ff_shared * d + T * d
+                          + n_kept * cfg.d_ff + T * cfg.d_ff_shared)
+        m1_gbs = m1_bytes / (m1_ms * 1e-3) / 1e9
+        m1_tfs = g1_flops / (m1_ms * 1e-3) / 1e12
+        mxfp8 = {
+            "experts": "MXFP8 (E4M3 + E8M0 per 32), router fp32",
+            "ms_per_step": round(mx_ms, 4), "tokens/s": round(T / (mx_ms * 1e-3), 1),
+            "tflops": round(fl["total"] / (mx_ms * 1e-3) / 1e12, 2),
+            "gate_up_ms": round(m1_ms, 4), "gate_up_note": "x quantisation + grouped GEMM",
+            "gate_up_GB/s": round(m1_gbs, 1), "gate_up_hbm_frac": round(m1_gbs / PEAK_HBM_GBS, 4),
+            "gate_up_TFLOP/s": round(m1_tfs, 2),
+            "gate_up_fp8_frac": round(m1_tfs / PEAK_FP8_TFLOPS, 4),
+            "gate_up_min_ms_at_peaks": round(max(m1_bytes / (PEAK_HBM_GBS * 1e9),
+                                                 g1_flops / (PEAK_FP8_TFLOPS * 1e12)) * 1e3, 4),
+            "down_ms": round(m2_ms, 4),
+            "down_TFLOP/s": round(g2_flops / (m2_ms * 1e-3) / 1e12, 2),
+        }
+        del w1q, w2q, w1sq, w2sq, ws_mx, hq, hsq
+
     res = {
         "metric": METRIC,
         "value": round(T / (ms * 1e-3), 1),
@@ -343,6 +407,7 @@ def main():
         "gemm2": gemm2,
         "telemetry": telemetry,
         "expert_choice": expert_choice,
+        "mxfp8": mxfp8,
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

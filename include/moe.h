@@ -65,8 +65,22 @@
  *     segment; perm[R..T*k) is left unspecified.
  *   - dtype MOE_DTYPE_F32: activations and expert weights fp32 (all math
  *     fp32).  MOE_DTYPE_BF16: bf16 activations/weights, bf16 MFMA with fp32
- *     accumulation, SwiGLU intermediate rounded to bf16, fp32 combine.  The
- *     router (GEMM, scores, selection, gates) is fp32 in both.
+ *     accumulation, SwiGLU intermediate rounded to bf16, fp32 combine.
+ *     MOE_DTYPE_MXFP8 (MXFP8 experts: "MoE common taste of open models",
+ *     section 2 and its closing recipe table; "MoE architecture in
+ *     practice", precision section): x, y, y_perm, y_shared bf16; the expert
+ *     weights and the SwiGLU intermediate (w1, w2, w1_shared, w2_shared, h,
+ *     h_shared) are packed MX matrices (below); x is quantised to MXFP8
+ *     along d and h along d_ff inside the expert call; E4M3 x E4M3 MFMA with
+ *     the block scales applied, fp32 accumulation.  The router (GEMM,
+ *     scores, selection, gates) is fp32 in all three.
+ *   - Packed MX matrix of R rows and K values per row (OCP Microscaling
+ *     Formats v1.0, MXFP8 with E4M3 elements): R*K code bytes, row-major,
+ *     then R*K/32 scale bytes, row-major, scale byte = X + 127 for the block
+ *     value 2^X.  A stack of N such matrices (w1, w2) holds the N code
+ *     arrays first, then the N scale arrays; h [T*k, d_ff] and h_shared
+ *     [T, d_ff_shared] are packed over all T*k (T) rows.  moe_quantize_mx
+ *     writes this layout.
  *   - Errors: every argument is validated before anything is enqueued; on
  *     an error nothing is launched and the status says why.  No C++
  *     exception crosses this interface.  MOE_ERR_HIP reports a failed
@@ -96,7 +110,7 @@ typedef enum moe_status {
 } moe_status;
 
 enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
-enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 };
+enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1, MOE_DTYPE_MXFP8 = 2 };
 /* capacity rule: TOKENS  C = floor(cf*T/N)               (llm-compass page)
  *                ASSIGNMENTS C = max(int(cf*k*T/N), k)    (deepseekmodel.com
  *                                                          TopKRouter)      */
@@ -115,7 +129,7 @@ typedef struct moe_shape {
   int32_t topk_groups;    /* groups kept per token; divides k               */
   float capacity_factor;  /* <= 0: dropless                                 */
   int32_t capacity_rule;  /* MOE_CAP_*                                      */
-  int32_t dtype;          /* MOE_DTYPE_* of activations and expert weights  */
+  int32_t dtype;          /* MOE_DTYPE_*: activations and expert weights    */
 } moe_shape;
 
 /* Version of this interface (MOE_ABI_VERSION). */
@@ -129,8 +143,8 @@ const char* moe_status_string(moe_status status);
  * d_ff < 1, d_ff_shared < 0, unknown enum values, n_groups < 1 or not
  * dividing N, topk_groups < 1 or > n_groups, k % topk_groups != 0,
  * k/topk_groups > N/n_groups, NaN capacity_factor.  Unsupported: N > 512,
- * k > 16, n_groups > 64, d_model, d_ff, d_ff_shared not multiples of 64
- * (bf16) or 32 (fp32), T*k*max(d_model, d_ff, d_ff_shared) >= 2^31,
+ * k > 16, n_groups > 64, d_model, d_ff, d_ff_shared not multiples of 128
+ * (MXFP8), 64 (bf16) or 32 (fp32), T*k*max(d_model, d_ff, d_ff_shared) >= 2^31,
  * 2*d_ff*d_model >= 2^31. */
 moe_status moe_check_shape(const moe_shape* shape);
 
@@ -140,6 +154,21 @@ int64_t moe_capacity(const moe_shape* shape);
 /* Workspace bytes that every entry point below needs for this shape
  * (0 on an invalid shape). */
 size_t moe_workspace_bytes(const moe_shape* shape);
+
+/* MXFP8 quantisation (OCP MX v1.0) of a row-major [rows, cols] matrix `in`
+ * (in_dtype MOE_DTYPE_BF16 or MOE_DTYPE_F32; cols a multiple of 32) into the
+ * packed MX layout at `out` (rows*cols*33/32 bytes): each block of 32
+ * consecutive values of a row gets X = floor(log2 max|v|) - 8 (8 = the top
+ * E4M3 binade), clamped to [-127, 127] (an all-zero block: -127; a block
+ * holding an infinity: 127; NaN does not enter the maximum), and each value
+ * the E4M3 code of v / 2^X: nearest, ties to the even mantissa, magnitudes
+ * beyond 448 saturate, NaN gives the NaN code, the sign bit is kept.  For
+ * a stack of expert matrices call it once per stack with rows = N * rows
+ * per expert.  in, out 16-byte aligned device pointers.  Errors:
+ * MOE_ERR_INVALID (NULL or misaligned pointer, bad dtype, rows < 1, cols
+ * not a positive multiple of 32), MOE_ERR_UNSUPPORTED (rows*cols >= 2^40). */
+moe_status moe_quantize_mx(const void* in, int32_t in_dtype, int64_t rows,
+                           int64_t cols, void* out, void* stream);
 
 /* Router: logits, scores, selection and gates for all T tokens.
  * x [T,d] dtype; w_router [N,d] fp32; logit_add [T,N] or NULL (added to the

@@ -11,12 +11,13 @@ argument order, tensors in place of pointers):
     moe_route, moe_dispatch, moe_expert_plan, moe_expert_ffn, moe_expert_gate_up,
     moe_expert_down, moe_combine, moe_bias_update, moe_bias_update_seq,
     moe_router_stats, moe_router_stats_count, moe_route_ec, moe_combine_ec,
-    moe_forward_ec, moe_ec_capacity, moe_forward,
+    moe_forward_ec, moe_ec_capacity, moe_quantize_mx, moe_forward,
     moe_workspace_bytes, moe_check_shape, moe_capacity, moe_status_string,
     moe_abi_version
 
-plus ``MoeShape`` (the C struct), ``workspace(shape)`` and ``forward(...)``,
-a convenience wrapper that allocates the outputs of one layer forward.
+plus ``MoeShape`` (the C struct), ``workspace(shape)``, ``quantize_mx(t)``
+(allocates a packed MX matrix) and ``forward(...)``, a convenience wrapper
+that allocates the outputs of one layer forward.
 """
 from __future__ import annotations
 
@@ -31,7 +32,8 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
-MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
+MOE_DTYPE_F32, MOE_DTYPE_BF16, MOE_DTYPE_MXFP8 = 0, 1, 2
+MX_BLOCK = 32
 MOE_CAP_TOKENS, MOE_CAP_ASSIGNMENTS = 0, 1
 
 
@@ -68,7 +70,8 @@ class MoeShape(ctypes.Structure):
                    1 if renormalize else 0, int(n_groups), int(topk_groups),
                    float(capacity_factor),
                    MOE_CAP_ASSIGNMENTS if capacity_rule == "assignments" else MOE_CAP_TOKENS,
-                   MOE_DTYPE_F32 if dtype in ("f32", torch.float32) else MOE_DTYPE_BF16)
+                   MOE_DTYPE_F32 if dtype in ("f32", torch.float32)
+                   else MOE_DTYPE_MXFP8 if dtype == "mxfp8" else MOE_DTYPE_BF16)
 
     @classmethod
     def from_config(cls, cfg, T: Optional[int] = None) -> "MoeShape":
@@ -118,6 +121,8 @@ _SIGS = {
                                         _P]),
     "moe_bias_update_seq": (ctypes.c_int, [_S, _P, _P, ctypes.c_int32, ctypes.c_float,
                                            ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_quantize_mx": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, _P,
+                                       _P]),
     "moe_ec_capacity": (ctypes.c_int64, [_S]),
     "moe_route_ec": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                     _P]),
@@ -169,6 +174,20 @@ def _ptr(t: Optional[torch.Tensor], name: str, dtype=None, numel=None):
     return t.data_ptr()
 
 
+def mx_bytes(elems: int) -> int:
+    """Bytes of a packed MX matrix of `elems` values (codes, then one scale
+    byte per 32 values)."""
+    return elems + elems // MX_BLOCK
+
+
+def _wptr(t: Optional[torch.Tensor], name: str, shape: "MoeShape", elems: int):
+    """Expert weights and the SwiGLU intermediate: the layer dtype, or a
+    packed MX matrix (uint8) in an MXFP8 layer."""
+    if shape.dtype == MOE_DTYPE_MXFP8:
+        return _ptr(t, name, torch.uint8, mx_bytes(elems))
+    return _ptr(t, name, shape.torch_dtype, elems)
+
+
 def _stream(stream=None):
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -216,6 +235,26 @@ def _dt(shape):
     return shape.torch_dtype
 
 
+def moe_quantize_mx(x, out, stream=None):
+    """MXFP8-quantise x ([..., cols] bf16 or fp32, cols % 32 == 0) into the
+    packed MX layout `out` (uint8, mx_bytes(x.numel()) bytes)."""
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("moe_quantize_mx takes bf16 or fp32 input")
+    cols = x.shape[-1]
+    rows = x.numel() // max(cols, 1)
+    st = lib().moe_quantize_mx(
+        _ptr(x, "x"), MOE_DTYPE_F32 if x.dtype == torch.float32 else MOE_DTYPE_BF16,
+        int(rows), int(cols), _ptr(out, "out", torch.uint8, mx_bytes(x.numel())), _stream(stream))
+    _check(st, "moe_quantize_mx")
+
+
+def quantize_mx(x: torch.Tensor, stream=None) -> torch.Tensor:
+    """Allocate and fill the packed MX matrix of x (see moe_quantize_mx)."""
+    out = torch.empty(mx_bytes(x.numel()), dtype=torch.uint8, device=x.device)
+    moe_quantize_mx(x, out, stream)
+    return out
+
+
 def moe_route(shape, x, w_router, logit_add, scores_in, bias, logits_out, scores_out,
               topk_idx, topk_w, ws, stream=None):
     T, N, k = shape.T, shape.n_experts, shape.top_k
@@ -261,9 +300,9 @@ def moe_expert_ffn(shape, x, perm, offsets, w1, w2, w1_shared, w2_shared, y_perm
     p, n = _ws(ws)
     st = lib().moe_expert_ffn(
         ctypes.byref(shape), _ptr(x, "x", dt, T * d), _ptr(perm, "perm", torch.int32, T * k),
-        _ptr(offsets, "offsets", torch.int32, N + 1), _ptr(w1, "w1", dt, N * 2 * f * d),
-        _ptr(w2, "w2", dt, N * d * f), _ptr(w1_shared, "w1_shared", dt, 2 * fs * d),
-        _ptr(w2_shared, "w2_shared", dt, d * fs), _ptr(y_perm, "y_perm", dt, T * k * d),
+        _ptr(offsets, "offsets", torch.int32, N + 1), _wptr(w1, "w1", shape, N * 2 * f * d),
+        _wptr(w2, "w2", shape, N * d * f), _wptr(w1_shared, "w1_shared", shape, 2 * fs * d),
+        _wptr(w2_shared, "w2_shared", shape, d * fs), _ptr(y_perm, "y_perm", dt, T * k * d),
         _ptr(y_shared, "y_shared", dt, T * d), p, n, _stream(stream))
     _check(st, "moe_expert_ffn")
 
@@ -275,9 +314,9 @@ def moe_expert_gate_up(shape, x, perm, offsets, w1, w1_shared, h, h_shared, ws, 
     p, n = _ws(ws)
     st = lib().moe_expert_gate_up(
         ctypes.byref(shape), _ptr(x, "x", dt, T * d), _ptr(perm, "perm", torch.int32, T * k),
-        _ptr(offsets, "offsets", torch.int32, N + 1), _ptr(w1, "w1", dt, N * 2 * f * d),
-        _ptr(w1_shared, "w1_shared", dt, 2 * fs * d), _ptr(h, "h", dt, T * k * f),
-        _ptr(h_shared, "h_shared", dt, T * fs), p, n, _stream(stream))
+        _ptr(offsets, "offsets", torch.int32, N + 1), _wptr(w1, "w1", shape, N * 2 * f * d),
+        _wptr(w1_shared, "w1_shared", shape, 2 * fs * d), _wptr(h, "h", shape, T * k * f),
+        _wptr(h_shared, "h_shared", shape, T * fs), p, n, _stream(stream))
     _check(st, "moe_expert_gate_up")
 
 
@@ -288,9 +327,10 @@ def moe_expert_down(shape, h, h_shared, offsets, w2, w2_shared, y_perm, y_shared
     dt = _dt(shape)
     p, n = _ws(ws)
     st = lib().moe_expert_down(
-        ctypes.byref(shape), _ptr(h, "h", dt, T * k * f), _ptr(h_shared, "h_shared", dt, T * fs),
-        _ptr(offsets, "offsets", torch.int32, N + 1), _ptr(w2, "w2", dt, N * d * f),
-        _ptr(w2_shared, "w2_shared", dt, d * fs), _ptr(y_perm, "y_perm", dt, T * k * d),
+        ctypes.byref(shape), _wptr(h, "h", shape, T * k * f),
+        _wptr(h_shared, "h_shared", shape, T * fs),
+        _ptr(offsets, "offsets", torch.int32, N + 1), _wptr(w2, "w2", shape, N * d * f),
+        _wptr(w2_shared, "w2_shared", shape, d * fs), _ptr(y_perm, "y_perm", dt, T * k * d),
         _ptr(y_shared, "y_shared", dt, T * d), p, n, _stream(stream))
     _check(st, "moe_expert_down")
 
@@ -365,9 +405,9 @@ def moe_forward_ec(shape, x, w_router, logit_add, w1, w2, w1_shared, w2_shared, 
     st = lib().moe_forward_ec(
         ctypes.byref(shape), _ptr(x, "x", dt, T * d),
         _ptr(w_router, "w_router", torch.float32, N * d),
-        _ptr(logit_add, "logit_add", torch.float32, T * N), _ptr(w1, "w1", dt, N * 2 * f * d),
-        _ptr(w2, "w2", dt, N * d * f), _ptr(w1_shared, "w1_shared", dt, 2 * fs * d),
-        _ptr(w2_shared, "w2_shared", dt, d * fs), _ptr(y, "y", dt, T * d),
+        _ptr(logit_add, "logit_add", torch.float32, T * N), _wptr(w1, "w1", shape, N * 2 * f * d),
+        _wptr(w2, "w2", shape, N * d * f), _wptr(w1_shared, "w1_shared", shape, 2 * fs * d),
+        _wptr(w2_shared, "w2_shared", shape, d * fs), _ptr(y, "y", dt, T * d),
         _ptr(scores_out, "scores_out", torch.float32, T * N),
         _ptr(offsets, "offsets", torch.int32, N + 1), _ptr(row_of, "row_of", torch.int32, T * N),
         p, n, _stream(stream))
@@ -407,9 +447,9 @@ def moe_forward(shape, x, w_router, logit_add, bias, w1, w2, w1_shared, w2_share
         ctypes.byref(shape), _ptr(x, "x", dt, T * d),
         _ptr(w_router, "w_router", torch.float32, N * d),
         _ptr(logit_add, "logit_add", torch.float32, T * N),
-        _ptr(bias, "bias", torch.float32, N), _ptr(w1, "w1", dt, N * 2 * f * d),
-        _ptr(w2, "w2", dt, N * d * f), _ptr(w1_shared, "w1_shared", dt, 2 * fs * d),
-        _ptr(w2_shared, "w2_shared", dt, d * fs), _ptr(y, "y", dt, T * d),
+        _ptr(bias, "bias", torch.float32, N), _wptr(w1, "w1", shape, N * 2 * f * d),
+        _wptr(w2, "w2", shape, N * d * f), _wptr(w1_shared, "w1_shared", shape, 2 * fs * d),
+        _wptr(w2_shared, "w2_shared", shape, d * fs), _ptr(y, "y", dt, T * d),
         _ptr(scores_out, "scores_out", torch.float32, T * N),
         _ptr(topk_idx, "topk_idx", torch.int32, T * k),
         _ptr(topk_w, "topk_w", torch.float32, T * k), _ptr(counts, "counts", torch.int32, N),

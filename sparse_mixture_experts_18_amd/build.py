@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe.so")
 SOURCES = ["moe_api.hip", "router.hip", "dispatch.hip", "grouped_gemm.hip", "combine.hip",
-           "telemetry.hip", "expert_choice.hip"]
+           "telemetry.hip", "expert_choice.hip", "mx.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

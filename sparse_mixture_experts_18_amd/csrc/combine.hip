@@ -142,7 +142,7 @@ __global__ __launch_bounds__(512) void bias_step_kernel(const int32_t* __restric
 hipError_t launch_combine(const moe_shape& s, const void* y_perm, const void* y_shared,
                           const int32_t* slot, const float* topk_w, void* y, hipStream_t st) {
   const int T = (int)s.T, d = s.d_model, k = s.top_k;
-  if (s.dtype == MOE_DTYPE_BF16)
+  if (act_bf16(s))
     combine_bf16_kernel<<<T, CB_THREADS, 0, st>>>(
         static_cast<const bf16_t*>(y_perm), static_cast<const bf16_t*>(y_shared), slot, topk_w,
         static_cast<bf16_t*>(y), d, k);

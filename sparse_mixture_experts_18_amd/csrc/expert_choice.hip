@@ -264,7 +264,7 @@ hipError_t launch_ec_combine(const moe_shape& s, const void* y_perm, const void*
                              const int32_t* row_of, const float* scores, void* y,
                              hipStream_t st) {
   const int T = (int)s.T, N = s.n_experts, d = s.d_model;
-  if (s.dtype == MOE_DTYPE_BF16)
+  if (act_bf16(s))
     ec_combine_kernel<bf16_t><<<T, ECC_THREADS, 0, st>>>(
         static_cast<const bf16_t*>(y_perm), static_cast<const bf16_t*>(y_shared), row_of, scores,
         static_cast<bf16_t*>(y), N, d);

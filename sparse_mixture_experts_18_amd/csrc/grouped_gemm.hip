@@ -19,6 +19,8 @@
 // needed.  Persistent blocks, one per CU: each XCD walks its own contiguous,
 // cost-balanced run of the list (same expert, same weight slab), which keeps
 // that slab in the XCD's L2 across the row blocks.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -214,32 +216,43 @@ __device__ __forceinline__ int xcd_item(int count) {
   return item < count ? item : -1;
 }
 
+// Operands are addressed in bytes: bf16 elements are 2 bytes, MXFP8 codes 1.
+// MXFP8 operands carry their scales in separate arrays, one byte per row per
+// 32 values of the reduction axis.
 struct GemmArgs {
-  const bf16_t* a_routed;  // GEMM1: x [T, d]       GEMM2: h [T*k, d_ff]
-  const bf16_t* a_shared;  // GEMM1: x [T, d]       GEMM2: h_shared [T, d_ffs]
-  const int32_t* perm;     // GEMM1: row -> token via perm[row] / k; GEMM2: null
+  const unsigned char* a_routed;  // GEMM1: x [T, d]       GEMM2: h [T*k, d_ff]
+  const unsigned char* a_shared;  // GEMM1: x [T, d]       GEMM2: h_shared [T, d_ffs]
+  const int32_t* perm;            // GEMM1: row -> token via perm[row] / k; GEMM2: null
   int k;
-  const bf16_t* b_routed;  // GEMM1: w1 [N][2*d_ff][d]  GEMM2: w2 [N][d][d_ff]
-  const bf16_t* b_shared;
-  bf16_t* c_routed;        // GEMM1: h              GEMM2: y_perm
-  bf16_t* c_shared;        // GEMM1: h_shared       GEMM2: y_shared
-  int K_r, K_s;            // reduction length
-  int Nout_r, Nout_s;      // output columns (h columns for GEMM1)
-  long long b_stride;      // elements per routed expert weight matrix
+  const unsigned char* b_routed;  // GEMM1: w1 [N][2*d_ff][d]  GEMM2: w2 [N][d][d_ff]
+  const unsigned char* b_shared;
+  unsigned char* c_routed;        // GEMM1: h              GEMM2: y_perm (bf16)
+  unsigned char* c_shared;        // GEMM1: h_shared       GEMM2: y_shared (bf16)
+  // MXFP8 only: scale bytes [rows][K/32] of A and B, and of the GEMM1 output
+  const unsigned char* as_routed;
+  const unsigned char* as_shared;
+  const unsigned char* bs_routed;
+  const unsigned char* bs_shared;
+  unsigned char* cs_routed;
+  unsigned char* cs_shared;
+  int K_r, K_s;                   // reduction length (elements)
+  int Nout_r, Nout_s;             // output columns (h columns for GEMM1)
+  long long b_stride;             // elements per routed expert weight matrix
   int N;
   const WorkItem* items;
   int32_t* hdr;
 };
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA grouped GEMM.
+// MFMA grouped GEMM (bf16, or MXFP8 with per-32 block scales).
 //
-// Block tile: up to BM rows (assignments) x BNW weight rows, k-slices of BK.
-// RG x CG waves: wave (rg, cg) owns the weight rows of column group cg
-// (GATED: gate rows 32cg..32cg+31 and the matching up rows, i.e. 32 h columns,
-// so SwiGLU is applied in registers; plain: 64 output columns) and the 32-row
-// MFMA sub-tiles i with i % RG == rg.  An item with few rows costs MFMA work
-// in proportion to ceil(rows/32), not to the full tile.
+// Block tile: up to BM rows (assignments) x BNW weight rows, k-slices of 128
+// bytes per row (64 bf16 or 128 MXFP8 values).  RG x CG waves: wave (rg, cg)
+// owns the weight rows of column group cg (GATED: gate rows 32cg..32cg+31 and
+// the matching up rows, i.e. 32 h columns, so SwiGLU is applied in
+// registers; plain: 64 output columns) and the 32-row MFMA sub-tiles i with
+// i % RG == rg.  An item with few rows costs MFMA work in proportion to
+// ceil(rows/32), not to the full tile.
 //
 // Operands move global -> LDS with the direct DMA load (global_load_lds, 16
 // bytes per lane, one 1 KiB block of rows per wave instruction) into rings of
@@ -251,6 +264,13 @@ struct GemmArgs {
 // of an MFMA fragment read then hit 64 distinct banks per 16 lanes.  The DMA
 // lane -> LDS position map is fixed, so each lane fetches the chunk that
 // belongs at its position.
+//
+// MXFP8: v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, fp32 accumulation),
+// two 64-deep k-steps per slice.  Lane (r, h) of a fragment holds row r and
+// k 16h..16h+15 and 32+16h..32+16h+15 of the step, and gives the scale of
+// row r for the step's 32-value block h.  The scale bytes of a slice (four
+// per row) travel with the A slice: one 4-byte DMA per lane per wave, rows
+// of A first, then the weight rows.
 // ---------------------------------------------------------------------------
 template <int RG_, int CG_, int NTW_, int BK_, int SA_, int SB_, int MSW_ = 4, int LDS_KIB_ = 160,
           int MAXS_ = 4>
@@ -267,14 +287,17 @@ struct GCfg {
   static constexpr int DROWS = 1024 / ROWB;   // rows per wave DMA instruction
   static constexpr int A_BYTES = BM * ROWB, B_BYTES = BNW * ROWB;
   static constexpr int A_LOADS = A_BYTES / 1024 / WAVES, B_LOADS = B_BYTES / 1024 / WAVES;
+  static constexpr int SCL = WAVES * 64 * 4;  // MXFP8 scale bytes of one slice
   // LDS per block; items with few rows use it for deeper rings.  160 KiB is
   // the whole CU (one block per CU); 80 KiB lets two blocks share a CU.
   static constexpr int LDS_BYTES = LDS_KIB_ * 1024;
   static constexpr int BLOCKS_PER_CU = 160 / LDS_KIB_;
   static constexpr int MAXS = MAXS_;  // deepest ring that items with few rows get
   static_assert(A_LOADS * 1024 * WAVES == A_BYTES && B_LOADS * 1024 * WAVES == B_BYTES, "");
-  static_assert(SA * A_BYTES + SB * B_BYTES <= LDS_BYTES, "LDS");
+  static_assert(SA * (A_BYTES + SCL) + SB * B_BYTES <= LDS_BYTES, "LDS");
   static_assert(SB >= SA && SA >= 2 && SB <= SA + 1, "B runs at most one slice ahead of A");
+  static_assert(BM + BNW <= WAVES * 64, "one scale DMA per wave covers every row");
+  static_assert(ROWB == 128, "k-slices are 128 bytes per row");
   __device__ static __forceinline__ int swz(int r) { return (r / RP) % CPR; }
 };
 
@@ -300,8 +323,6 @@ using Cfg2 = GCfg<MOE_GEMM2_CFG>;
 #endif
 using Cfg1n = GCfg<MOE_GEMM1_SMALL_CFG>;
 using Cfg2n = GCfg<MOE_GEMM2_SMALL_CFG>;
-// (the MFMAs walk k in 16-wide steps in ascending order whatever the slice
-// width BK, so tile families with different BK give the same bits)
 
 // mean rows per expert at or below which the small-row tiles are used
 #ifndef MOE_SMALL_ROWS
@@ -311,9 +332,26 @@ constexpr int kNarrowRows = MOE_SMALL_ROWS;
 
 typedef __attribute__((address_space(1))) void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
-__device__ __forceinline__ void dma16(const bf16_t* src, unsigned char* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((gptr_t)(src), (lptr_t)(lds_wave_base), 16, 0, 0);
+// Direct global -> LDS loads through a buffer resource: the base address
+// sits in scalar registers, each lane supplies a 32-bit offset and the
+// k-slice offset is the scalar soffset, so a load costs one VGPR.  Lane i
+// of a wave writes its 16 (or 4) bytes to lds_wave_base + 16 i (4 i).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const unsigned char* base) {
+  // raw buffer (stride 0), every 32-bit offset in range; gfx9 dword 3
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(base), (short)0,
+                                           (int)0xFFFFFFFFu, 0x00020000);
+}
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff,
+                                      unsigned char* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lptr_t)(lds_wave_base), 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void dma4(rsrc_t r, uint32_t voff, uint32_t soff,
+                                     unsigned char* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lptr_t)(lds_wave_base), 4, voff, soff, 0, 0);
 }
 
 // wait until at most n vector-memory ops of this wave are outstanding
@@ -323,36 +361,71 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// MFMA operand fragments of k-step ks (16 k) from one LDS stage: this wave's
-// A sub-tiles (rows a_row[j]) and weight rows b_row[0..1]; 16-byte chunk
-// 2ks + lane/32 of each row
-template <class C, int MS>
+// Operand fragments of one k-step from an LDS stage: this wave's A sub-tiles
+// (rows a_row[j]) and weight rows b_row[0..NTW).  bf16 (16-k steps): 16-byte
+// chunk 2ks + h of each row.  MXFP8 (64-k steps): chunks 4ks + h and
+// 4ks + 2 + h.
+template <bool MX>
+struct Frag;
+template <>
+struct Frag<false> {
+  typedef bf16x8_t T;
+  static constexpr int STEPS = 4;
+  __device__ static __forceinline__ T read(const unsigned char* row, int ks, int fh, int sw) {
+    return *reinterpret_cast<const bf16x8_t*>(row + (((2 * ks + fh) ^ sw) << 4));
+  }
+};
+template <>
+struct Frag<true> {
+  typedef i32x8_t T;
+  static constexpr int STEPS = 2;
+  __device__ static __forceinline__ T read(const unsigned char* row, int ks, int fh, int sw) {
+    const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(row + (((4 * ks + fh) ^ sw) << 4));
+    const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(row + (((4 * ks + 2 + fh) ^ sw) << 4));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+};
+
+template <bool MX, class C, int MS>
 __device__ __forceinline__ void load_frags(const unsigned char* As, const unsigned char* Bs,
                                            const int (&a_row)[MS], const int (&b_row)[C::NTW],
-                                           int fh, int ks, bf16x8_t (&af)[MS],
-                                           bf16x8_t (&bf)[C::NTW]) {
-  const int ch = 2 * ks + fh;
+                                           int fh, int ks, typename Frag<MX>::T (&af)[MS],
+                                           typename Frag<MX>::T (&bf)[C::NTW]) {
 #pragma unroll
   for (int j = 0; j < C::NTW; ++j)
-    bf[j] = *reinterpret_cast<const bf16x8_t*>(Bs + b_row[j] * C::ROWB +
-                                               ((ch ^ C::swz(b_row[j])) << 4));
+    bf[j] = Frag<MX>::read(Bs + b_row[j] * C::ROWB, ks, fh, C::swz(b_row[j]));
 #pragma unroll
   for (int i = 0; i < MS; ++i)
-    af[i] = *reinterpret_cast<const bf16x8_t*>(As + a_row[i] * C::ROWB +
-                                               ((ch ^ C::swz(a_row[i])) << 4));
+    af[i] = Frag<MX>::read(As + a_row[i] * C::ROWB, ks, fh, C::swz(a_row[i]));
+}
+
+// acc += weight fragment x row fragment (the accumulator holds the tile
+// transposed); MXFP8 scales are E8M0 bytes in bits 0..7 of sb / sa
+__device__ __forceinline__ f32x16_t mma(const bf16x8_t& b, const bf16x8_t& a, const f32x16_t& c,
+                                        int, int) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16_t mma(const i32x8_t& b, const i32x8_t& a, const f32x16_t& c,
+                                        int sb, int sa) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 0, 0, 0, sb, 0, sa);
 }
 
 // main loop + epilogue for items whose waves hold MS row sub-tiles (the last
 // one only if `last` is set for this wave)
-template <bool GATED, class C, int MS>
-__device__ __forceinline__ void gemm_bf16_body(const GemmArgs& g, const WorkItem& it,
-                                               unsigned char* lds, int msub) {
+template <bool GATED, bool MX, class C, int MS>
+__device__ __forceinline__ void gemm_body(const GemmArgs& g, const WorkItem& it,
+                                          unsigned char* lds, int msub) {
+  typedef typename Frag<MX>::T FT;
+  constexpr int ES = MX ? 1 : 2;         // bytes per element
+  constexpr int KSTEPS = Frag<MX>::STEPS;
   const bool shared = it.seg == g.N;
   const int K = shared ? g.K_s : g.K_r;
+  const int Kb = K * ES;                 // bytes per operand row
   const int Nout = shared ? g.Nout_s : g.Nout_r;
-  const bf16_t* A = shared ? g.a_shared : g.a_routed;
-  const bf16_t* B = shared ? g.b_shared : g.b_routed + (long long)it.seg * g.b_stride;
-  bf16_t* Cm = shared ? g.c_shared : g.c_routed;
+  const unsigned char* A = shared ? g.a_shared : g.a_routed;
+  const unsigned char* B =
+      shared ? g.b_shared : g.b_routed + (long long)it.seg * g.b_stride * ES;
+  unsigned char* Cm = shared ? g.c_shared : g.c_routed;
   const int n0 = it.nt * (GATED ? C::BNW / 2 : C::BNW);
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -368,30 +441,52 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& g, const WorkItem
   // only the rows of the MS*RG live sub-tiles are fetched
   constexpr int AL = C::RG * MS * 32 * C::ROWB / 1024 / C::WAVES;
   static_assert(AL * 1024 * C::WAVES == C::RG * MS * 32 * C::ROWB, "A rows per wave load");
+  auto a_src = [&](int tr) {  // source row of tile row tr (clamped to the item)
+    int src = it.row0 + min(tr, it.nrows - 1);
+    if (g.perm && !shared) src = g.perm[src] / g.k;
+    return src;
+  };
+  auto b_src = [&](int r) {  // weight row of tile weight row r (clamped)
+    if (GATED)
+      return r < C::BNW / 2 ? min(n0 + r, Nout - 1) : Nout + min(n0 + r - C::BNW / 2, Nout - 1);
+    return min(n0 + r, Nout - 1);
+  };
   uint32_t a_off[AL], b_off[C::B_LOADS];
 #pragma unroll
   for (int j = 0; j < AL; ++j) {
     const int tr = (w * AL + j) * C::DROWS + drow;
-    const int r = min(tr, it.nrows - 1);
-    int src = it.row0 + r;
-    if (g.perm && !shared) src = g.perm[src] / g.k;
-    a_off[j] = (uint32_t)src * (uint32_t)K + (dpos ^ C::swz(tr)) * 8;
+    a_off[j] = (uint32_t)a_src(tr) * (uint32_t)Kb + (dpos ^ C::swz(tr)) * 16;
   }
 #pragma unroll
   for (int j = 0; j < C::B_LOADS; ++j) {
     const int r = (w * C::B_LOADS + j) * C::DROWS + drow;
-    int wrow;
-    if (GATED)
-      wrow = r < C::BNW / 2 ? min(n0 + r, Nout - 1) : Nout + min(n0 + r - C::BNW / 2, Nout - 1);
-    else
-      wrow = min(n0 + r, Nout - 1);
-    b_off[j] = (uint32_t)wrow * (uint32_t)K + (dpos ^ C::swz(r)) * 8;
+    b_off[j] = (uint32_t)b_src(r) * (uint32_t)Kb + (dpos ^ C::swz(r)) * 16;
+  }
+  // MXFP8 scales: lane gl = 64w + lane fetches the 4 scale bytes of a slice
+  // for tile row gl (gl < BM) or weight row gl - BM (gl < BM + BNW); the
+  // remaining lanes repeat weight row 0 into slots nobody reads.  BM is a
+  // multiple of 64, so each wave reads from one array (a uniform base).
+  const unsigned char* s_base = nullptr;
+  uint32_t s_off = 0;
+  if (MX) {
+    static_assert(C::BM % 64 == 0, "");
+    const int gl = w * 64 + lane;
+    const int kb = K / kMxBlock;  // scale bytes per row
+    if (w * 64 < C::BM) {
+      s_base = shared ? g.as_shared : g.as_routed;
+      s_off = (uint32_t)a_src(gl) * (uint32_t)kb;
+    } else {
+      const int r = gl - C::BM < C::BNW ? gl - C::BM : 0;
+      s_base = shared ? g.bs_shared : g.bs_routed + (long long)it.seg * (g.b_stride / kMxBlock);
+      s_off = (uint32_t)b_src(r) * (uint32_t)kb;
+    }
   }
 
-  // LDS: SA buffers of the A slice (only the live rows), then SB buffers of
-  // the B slice.  Items with fewer rows have smaller A slices and get deeper
-  // rings (their short MFMA phase hides less latency per slice).
-  constexpr int A_SL = C::RG * MS * 32 * C::ROWB;  // bytes of one A slice
+  // LDS: SA buffers of the A slice (only the live rows; MXFP8: then the
+  // slice's scale bytes), then SB buffers of the B slice.  Items with fewer
+  // rows have smaller A slices and get deeper rings (their short MFMA phase
+  // hides less latency per slice).
+  constexpr int A_SL = C::RG * MS * 32 * C::ROWB + (MX ? C::SCL : 0);  // bytes of one A stage
   constexpr int SDEEP = (C::LDS_BYTES / (A_SL + C::B_BYTES)) < C::MAXS
                             ? (C::LDS_BYTES / (A_SL + C::B_BYTES)) : C::MAXS;
   constexpr int SA = SDEEP > C::SA ? SDEEP : C::SA;
@@ -399,19 +494,23 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& g, const WorkItem
   static_assert(SA * A_SL + SB * C::B_BYTES <= C::LDS_BYTES, "LDS");
   unsigned char* const Abuf = lds;
   unsigned char* const Bbuf = lds + SA * A_SL;
-  const int nk = K / C::BK;
+  constexpr int SC_OFF = C::RG * MS * 32 * C::ROWB;  // scale bytes inside an A stage
+  const int nk = Kb / C::ROWB;
+  const rsrc_t ra = make_rsrc(A), rb = make_rsrc(B);
+  const rsrc_t rs = make_rsrc(MX ? s_base : A);
   auto issue_a = [&](int kt) {
     unsigned char* st = Abuf + (kt % SA) * A_SL;
-    const int k0 = kt * C::BK;
+    const uint32_t k0 = kt * C::ROWB;
 #pragma unroll
-    for (int j = 0; j < AL; ++j) dma16(A + a_off[j] + k0, st + (w * AL + j) * 1024);
+    for (int j = 0; j < AL; ++j) dma16(ra, a_off[j], k0, st + (w * AL + j) * 1024);
+    if (MX) dma4(rs, s_off, kt * 4, st + SC_OFF + w * 256);
   };
   auto issue_b = [&](int kt) {
     unsigned char* st = Bbuf + (kt % SB) * C::B_BYTES;
-    const int k0 = kt * C::BK;
+    const uint32_t k0 = kt * C::ROWB;
 #pragma unroll
     for (int j = 0; j < C::B_LOADS; ++j)
-      dma16(B + b_off[j] + k0, st + (w * C::B_LOADS + j) * 1024);
+      dma16(rb, b_off[j], k0, st + (w * C::B_LOADS + j) * 1024);
   };
 
   constexpr int NT = C::NTW, HT = NT / 2;  // weight tiles per wave; GATED: gate tiles
@@ -443,7 +542,8 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& g, const WorkItem
   // younger ones are outstanding: B(kt+1) .. B(kt+SB-2) and A(kt+1) ..
   // A(kt+SA-2) when B leads by one slice, A/B(kt+1 .. kt+SA-2) otherwise.
   constexpr int LEAD = SB - SA;
-  constexpr int YOUNGER = (SA - 2) * (AL + C::B_LOADS) + LEAD * C::B_LOADS;
+  constexpr int ALX = AL + (MX ? 1 : 0);  // loads per A issue
+  constexpr int YOUNGER = (SA - 2) * (ALX + C::B_LOADS) + LEAD * C::B_LOADS;
 #pragma unroll
   for (int j = -(SB - 1); j < 0; ++j) {
     if (j + SA - 1 >= 0 && j + SA - 1 < nk) issue_a(j + SA - 1);
@@ -458,31 +558,53 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& g, const WorkItem
     __builtin_amdgcn_s_barrier();
     const unsigned char* As = Abuf + (kt % SA) * A_SL;
     const unsigned char* Bs = Bbuf + (kt % SB) * C::B_BYTES;
-    // fragments of k-step ks+1 are read while the MFMAs of k-step ks run
-    bf16x8_t bf[2][NT], af[2][MS];
-    load_frags<C, MS>(As, Bs, a_row, b_row, fh, 0, af[0], bf[0]);
+    // MXFP8 scales of this slice: byte b of a row's word is its block b; the
+    // lane of half h takes block 2ks + h into bits 0..7
+    uint32_t sa_w[MS], sb_w[NT];
+    if (MX) {
+      const uint32_t* sc = reinterpret_cast<const uint32_t*>(As + SC_OFF);
 #pragma unroll
-    for (int ks = 0; ks < C::BK / 16; ++ks) {
-      const int cur = ks & 1;
+      for (int i = 0; i < MS; ++i) sa_w[i] = sc[a_row[i]] >> (8 * fh);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) sb_w[j] = sc[C::BM + b_row[j]] >> (8 * fh);
+    }
+    // bf16: fragments of k-step ks+1 are read while the MFMAs of k-step ks
+    // run (two register sets).  MXFP8 fragments are twice as wide and each
+    // MFMA four times as long, so one set is read per k-step and the MFMAs
+    // start as soon as their own fragments have arrived.
+    constexpr int NB = MX ? 1 : 2;
+    FT bf[NB][NT], af[NB][MS];
+    load_frags<MX, C, MS>(As, Bs, a_row, b_row, fh, 0, af[0], bf[0]);
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const int cur = MX ? 0 : (ks & 1);
+      if (MX && ks > 0) {
+        // keep the next step's fragment reads behind this point, so the two
+        // register sets are never live together
+        __builtin_amdgcn_sched_barrier(0);
+        load_frags<MX, C, MS>(As, Bs, a_row, b_row, fh, ks, af[0], bf[0]);
+      }
       // refill the buffers of slice kt-1: A behind the first fragment reads,
       // B one k-step later, so the reads of k-step 0 are not queued behind
       // a burst of loads
       if (ks == 0 && kt + SA - 1 < nk) issue_a(kt + SA - 1);
       if (ks == 1 && kt + SB - 1 < nk) issue_b(kt + SB - 1);
-      if (ks + 1 < C::BK / 16)
-        load_frags<C, MS>(As, Bs, a_row, b_row, fh, ks + 1, af[cur ^ 1], bf[cur ^ 1]);
-      // weight fragment first: the accumulator holds the tile transposed
+      if (!MX && ks + 1 < KSTEPS)
+        load_frags<MX, C, MS>(As, Bs, a_row, b_row, fh, ks + 1, af[(cur ^ 1) % NB],
+                              bf[(cur ^ 1) % NB]);
+      const int sh = 16 * ks;  // MXFP8: block 2ks + h sits 16 ks bits up
 #pragma unroll
       for (int i = 0; i < MS - 1; ++i)
 #pragma unroll
         for (int j = 0; j < NT; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[cur][j], af[cur][i], acc[i][j],
-                                                              0, 0, 0);
+          acc[i][j] = mma(bf[cur][j], af[cur][i], acc[i][j], MX ? (int)(sb_w[j] >> sh) : 0,
+                          MX ? (int)(sa_w[i] >> sh) : 0);
       if (last) {
 #pragma unroll
         for (int j = 0; j < NT; ++j)
-          acc[MS - 1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              bf[cur][j], af[cur][MS - 1], acc[MS - 1][j], 0, 0, 0);
+          acc[MS - 1][j] = mma(bf[cur][j], af[cur][MS - 1], acc[MS - 1][j],
+                               MX ? (int)(sb_w[j] >> sh) : 0,
+                               MX ? (int)(sa_w[MS - 1] >> sh) : 0);
       }
     }
   }
@@ -490,35 +612,64 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& g, const WorkItem
   // epilogue.  32x32 accumulator layout of the transposed tile: lane l holds
   // token row l & 31 of the sub-tile; register r holds output column
   // 8*(r/4) + 4*(l/32) + r%4 of the 32-column weight tile, so each group of
-  // four registers is four consecutive columns: one 8-byte store.
+  // four registers is four consecutive columns: one 8-byte bf16 store, or
+  // one 4-byte store of MXFP8 codes.  An MXFP8 output (GEMM1) is quantised
+  // per 32 columns: the two lanes l and l^32 hold the 32 columns of a row.
   constexpr int OT = GATED ? HT : NT;  // output tiles per wave
+  constexpr bool QOUT = MX && GATED;   // h is stored as MXFP8
 #pragma unroll
   for (int i = 0; i < MS; ++i) {
     if (i == MS - 1 && !last) continue;
     const int row = (i * C::RG + rg) * 32 + fr;
-    if (row >= it.nrows) continue;
-    bf16_t* crow = Cm + (size_t)(it.row0 + row) * Nout;
+    const bool live = row < it.nrows;
+    const size_t orow = (size_t)(it.row0 + row);
 #pragma unroll
     for (int j = 0; j < OT; ++j) {
       const int c0 = n0 + (cg * OT + j) * 32;  // Nout is a multiple of 32
       if (c0 >= Nout) continue;
+      float v[16];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float gv = acc[i][j][4 * q + e];
-          if (GATED) {
-            const float uv = acc[i][j + HT][4 * q + e];
-            v[e] = gv / (1.0f + expf(-gv)) * uv;
-          } else {
-            v[e] = gv;
-          }
+      for (int r = 0; r < 16; ++r) {
+        const float gv = acc[i][j][r];
+        if (GATED) {
+          const float uv = acc[i][j + HT][r];
+          v[r] = gv / (1.0f + expf(-gv)) * uv;
+        } else {
+          v[r] = gv;
         }
-        u32x2_t pk;
-        pk[0] = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-        pk[1] = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-        *reinterpret_cast<u32x2_t*>(crow + c0 + 8 * q + 4 * fh) = pk;
+      }
+      if (QOUT) {
+        float amax = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float a = fabsf(v[r]);
+          amax = a > amax ? a : amax;
+        }
+        const float o = __shfl_xor(amax, 32, 64);
+        amax = o > amax ? o : amax;
+        const int X = mx_shared_exp(amax);
+        if (live) {
+          unsigned char* crow = Cm + orow * Nout;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t pk = e4m3_code(v[4 * q], X) | (e4m3_code(v[4 * q + 1], X) << 8) |
+                                (e4m3_code(v[4 * q + 2], X) << 16) |
+                                (e4m3_code(v[4 * q + 3], X) << 24);
+            *reinterpret_cast<uint32_t*>(crow + c0 + 8 * q + 4 * fh) = pk;
+          }
+          if (fh == 0)
+            (shared ? g.cs_shared : g.cs_routed)[orow * (Nout / kMxBlock) + c0 / kMxBlock] =
+                (unsigned char)(X + 127);
+        }
+      } else if (live) {
+        bf16_t* crow = reinterpret_cast<bf16_t*>(Cm) + orow * Nout;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          u32x2_t pk;
+          pk[0] = (uint32_t)f32_to_bf16(v[4 * q]) | ((uint32_t)f32_to_bf16(v[4 * q + 1]) << 16);
+          pk[1] = (uint32_t)f32_to_bf16(v[4 * q + 2]) | ((uint32_t)f32_to_bf16(v[4 * q + 3]) << 16);
+          *reinterpret_cast<u32x2_t*>(crow + c0 + 8 * q + 4 * fh) = pk;
+        }
       }
     }
   }
@@ -536,21 +687,25 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmArgs& g, const WorkItem
 #endif
 
 
-template <bool GATED, class C>
-__device__ __forceinline__ void gemm_bf16_item(const GemmArgs& g, int item, unsigned char* lds) {
-  const WorkItem it = g.items[item];
+template <bool GATED, bool MX, class C>
+__device__ __forceinline__ void gemm_item(const GemmArgs& g, int item, unsigned char* lds) {
+  // the item is the same for the whole block: keep its fields (and every
+  // base pointer derived from them) in scalar registers
+  const WorkItem ld = g.items[item];
+  const WorkItem it{__builtin_amdgcn_readfirstlane(ld.seg), __builtin_amdgcn_readfirstlane(ld.row0),
+                    __builtin_amdgcn_readfirstlane(ld.nrows), __builtin_amdgcn_readfirstlane(ld.nt)};
   const int msub = (it.nrows + 31) >> 5;  // live 32-row sub-tiles
   const int ms = (msub + C::RG - 1) / C::RG;  // sub-tiles of the busiest wave
   constexpr int M2 = C::MSW < 2 ? C::MSW : 2, M3 = C::MSW < 3 ? C::MSW : 3;
-  if (ms <= 1) gemm_bf16_body<GATED, C, 1>(g, it, lds, msub);
-  else if (ms <= 2) gemm_bf16_body<GATED, C, M2>(g, it, lds, msub);
-  else if (ms <= 3) gemm_bf16_body<GATED, C, M3>(g, it, lds, msub);
-  else gemm_bf16_body<GATED, C, C::MSW>(g, it, lds, msub);
+  if (ms <= 1) gemm_body<GATED, MX, C, 1>(g, it, lds, msub);
+  else if (ms <= 2) gemm_body<GATED, MX, C, M2>(g, it, lds, msub);
+  else if (ms <= 3) gemm_body<GATED, MX, C, M3>(g, it, lds, msub);
+  else gemm_body<GATED, MX, C, C::MSW>(g, it, lds, msub);
 }
 
-template <bool GATED, class C>
+template <bool GATED, bool MX, class C>
 __global__ __launch_bounds__(C::THREADS)
-__attribute__((amdgpu_waves_per_eu(C::WAVES * C::BLOCKS_PER_CU / 4))) void gemm_bf16_kernel(
+__attribute__((amdgpu_waves_per_eu(C::WAVES * C::BLOCKS_PER_CU / 4))) void gemm_mfma_kernel(
     GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds[C::LDS_BYTES];
 #if MOE_PERSISTENT
@@ -560,10 +715,10 @@ __attribute__((amdgpu_waves_per_eu(C::WAVES * C::BLOCKS_PER_CU / 4))) void gemm_
   for (;;) {
     if (threadIdx.x == 0) s_item = beg + atomicAdd(&g.hdr[kHdrCtr + x], 1);
     __syncthreads();  // also: every wave is done with the previous item's LDS
-    const int item = s_item;
+    const int item = __builtin_amdgcn_readfirstlane(s_item);
     __syncthreads();
     if (item >= end) break;
-    gemm_bf16_item<GATED, C>(g, item, lds);
+    gemm_item<GATED, MX, C>(g, item, lds);
   }
   // the last block out re-arms the item counters, so the same work list can
   // be launched again without rebuilding it (every other block has already
@@ -575,7 +730,7 @@ __attribute__((amdgpu_waves_per_eu(C::WAVES * C::BLOCKS_PER_CU / 4))) void gemm_
 #else
   const int item = xcd_item(g.hdr[0]);
   if (item < 0) return;
-  gemm_bf16_item<GATED, C>(g, item, lds);
+  gemm_item<GATED, MX, C>(g, item, lds);
 #endif
 }
 
@@ -673,15 +828,31 @@ int persistent_grid(int per_cu) {
   return cached[dev] * per_cu;
 }
 
-template <bool GATED, class C>
-void launch_bf16(const GemmArgs& g, int64_t cap, hipStream_t st) {
+template <bool GATED, bool MX, class C>
+void launch_mfma(const GemmArgs& g, int64_t cap, hipStream_t st) {
   const int grid = MOE_PERSISTENT ? persistent_grid(C::BLOCKS_PER_CU) : (int)((cap + 7) / 8 * 8);
-  gemm_bf16_kernel<GATED, C><<<grid, C::THREADS, 0, st>>>(g);
+  gemm_mfma_kernel<GATED, MX, C><<<grid, C::THREADS, 0, st>>>(g);
 }
 
 bool narrow_tiles(const moe_shape& s) {
-  return s.dtype == MOE_DTYPE_BF16 && s.T * s.top_k <= (long long)kNarrowRows * s.n_experts &&
+  return s.dtype != MOE_DTYPE_F32 && s.T * s.top_k <= (long long)kNarrowRows * s.n_experts &&
          s.d_ff_shared == 0;
+}
+
+typedef const unsigned char* cbytes;
+typedef unsigned char* bytes;
+inline cbytes cb(const void* p) { return static_cast<cbytes>(p); }
+inline bytes mb(void* p) { return static_cast<bytes>(p); }
+// scale bytes of a packed MX matrix with `elems` codes (NULL stays NULL)
+inline cbytes mx_sc(const void* p, size_t elems) { return p ? cb(p) + elems : nullptr; }
+inline bytes mx_sc(void* p, size_t elems) { return p ? mb(p) + elems : nullptr; }
+
+template <bool GATED, bool MX>
+void launch_tiles(const moe_shape& s, const GemmArgs& g, int64_t cap, hipStream_t st) {
+  if (narrow_tiles(s))
+    launch_mfma<GATED, MX, typename std::conditional<GATED, Cfg1n, Cfg2n>::type>(g, cap, st);
+  else
+    launch_mfma<GATED, MX, typename std::conditional<GATED, Cfg1, Cfg2>::type>(g, cap, st);
 }
 
 struct PlanGeom {
@@ -690,7 +861,7 @@ struct PlanGeom {
 
 // row-block size and column-tile counts of the two work lists
 PlanGeom plan_geom(const moe_shape& s) {
-  const bool bf = s.dtype == MOE_DTYPE_BF16;
+  const bool bf = s.dtype != MOE_DTYPE_F32;  // bf16 or MXFP8 MFMA tiles
   const bool nar = narrow_tiles(s);
   const int bm1 = bf ? (nar ? Cfg1n::BM : Cfg1::BM) : kBMf;
   const int bm2 = bf ? (nar ? Cfg2n::BM : Cfg2::BM) : kBMf;
@@ -714,20 +885,28 @@ hipError_t launch_plan(const moe_shape& s, const int32_t* offsets, const Workspa
   return hipGetLastError();
 }
 
-// h = silu(x W_gate^T) * (x W_up^T) over the work list built by launch_plan
+// h = silu(x W_gate^T) * (x W_up^T) over the work list built by launch_plan.
+// MXFP8 layers: x is quantised into the workspace first, w1 / w1s / h / hs
+// are packed MX matrices (codes, then scales).
 hipError_t launch_gemm1(const moe_shape& s, const void* x, const int32_t* perm, const void* w1,
                         const void* w1s, void* h, void* hs, const Workspace& w,
                         hipStream_t st) {
   const int N = s.n_experts, d = s.d_model, f = s.d_ff, fs = s.d_ff_shared;
+  const size_t T = (size_t)s.T, A = T * s.top_k;
   if (s.dtype == MOE_DTYPE_BF16) {
-    GemmArgs g1{static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(x), perm, s.top_k,
-                static_cast<const bf16_t*>(w1), static_cast<const bf16_t*>(w1s),
-                static_cast<bf16_t*>(h), static_cast<bf16_t*>(hs), d, d, f, fs,
-                (long long)2 * f * d, N, w.plan1, w.plan1_hdr};
-    if (narrow_tiles(s))
-      launch_bf16<true, Cfg1n>(g1, w.plan1_cap, st);
-    else
-      launch_bf16<true, Cfg1>(g1, w.plan1_cap, st);
+    GemmArgs g1{cb(x), cb(x), perm, s.top_k, cb(w1), cb(w1s), mb(h), mb(hs),
+                nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                d, d, f, fs, (long long)2 * f * d, N, w.plan1, w.plan1_hdr};
+    launch_tiles<true, false>(s, g1, w.plan1_cap, st);
+  } else if (s.dtype == MOE_DTYPE_MXFP8) {
+    hipError_t e = launch_mx_quantize(x, MOE_DTYPE_BF16, s.T, d, w.xq, w.xq + T * d, st);
+    if (e != hipSuccess) return e;
+    const unsigned char* xs = w.xq + T * d;
+    GemmArgs g1{w.xq, w.xq, perm, s.top_k, cb(w1), cb(w1s), mb(h), mb(hs),
+                xs, xs, mx_sc(w1, (size_t)N * 2 * f * d), mx_sc(w1s, (size_t)2 * fs * d),
+                mx_sc(h, A * f), mx_sc(hs, T * fs),
+                d, d, f, fs, (long long)2 * f * d, N, w.plan1, w.plan1_hdr};
+    launch_tiles<true, true>(s, g1, w.plan1_cap, st);
   } else {
     GemmArgsF g1{static_cast<const float*>(x), static_cast<const float*>(x), perm, s.top_k,
                  static_cast<const float*>(w1), static_cast<const float*>(w1s),
@@ -743,15 +922,18 @@ hipError_t launch_gemm2(const moe_shape& s, const void* h, const void* hs, const
                         const void* w2s, void* y_perm, void* y_shared, const Workspace& w,
                         hipStream_t st) {
   const int N = s.n_experts, d = s.d_model, f = s.d_ff, fs = s.d_ff_shared;
-  if (s.dtype == MOE_DTYPE_BF16) {
-    GemmArgs g2{static_cast<const bf16_t*>(h), static_cast<const bf16_t*>(hs), nullptr,
-                s.top_k, static_cast<const bf16_t*>(w2), static_cast<const bf16_t*>(w2s),
-                static_cast<bf16_t*>(y_perm), static_cast<bf16_t*>(y_shared), f, fs, d, d,
-                (long long)d * f, N, w.plan2, w.plan2_hdr};
-    if (narrow_tiles(s))
-      launch_bf16<false, Cfg2n>(g2, w.plan2_cap, st);
+  const size_t T = (size_t)s.T, A = T * s.top_k;
+  if (s.dtype != MOE_DTYPE_F32) {
+    const bool mx = s.dtype == MOE_DTYPE_MXFP8;
+    GemmArgs g2{cb(h), cb(hs), nullptr, s.top_k, cb(w2), cb(w2s), mb(y_perm), mb(y_shared),
+                mx ? mx_sc(h, A * f) : nullptr, mx ? mx_sc(hs, T * fs) : nullptr,
+                mx ? mx_sc(w2, (size_t)N * d * f) : nullptr,
+                mx ? mx_sc(w2s, (size_t)d * fs) : nullptr, nullptr, nullptr,
+                f, fs, d, d, (long long)d * f, N, w.plan2, w.plan2_hdr};
+    if (mx)
+      launch_tiles<false, true>(s, g2, w.plan2_cap, st);
     else
-      launch_bf16<false, Cfg2>(g2, w.plan2_cap, st);
+      launch_tiles<false, false>(s, g2, w.plan2_cap, st);
   } else {
     GemmArgsF g2{static_cast<const float*>(h), static_cast<const float*>(hs), nullptr,
                  s.top_k, static_cast<const float*>(w2), static_cast<const float*>(w2s),

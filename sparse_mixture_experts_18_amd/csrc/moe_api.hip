@@ -20,7 +20,8 @@ moe_status check_shape(const moe_shape* s) {
     return MOE_ERR_INVALID;
   if (s->score_fn != MOE_SCORE_SOFTMAX && s->score_fn != MOE_SCORE_SIGMOID)
     return MOE_ERR_INVALID;
-  if (s->dtype != MOE_DTYPE_F32 && s->dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID;
+  if (s->dtype != MOE_DTYPE_F32 && s->dtype != MOE_DTYPE_BF16 && s->dtype != MOE_DTYPE_MXFP8)
+    return MOE_ERR_INVALID;
   if (s->capacity_rule != MOE_CAP_TOKENS && s->capacity_rule != MOE_CAP_ASSIGNMENTS)
     return MOE_ERR_INVALID;
   if (s->renormalize != 0 && s->renormalize != 1) return MOE_ERR_INVALID;
@@ -30,7 +31,8 @@ moe_status check_shape(const moe_shape* s) {
   if (s->top_k % s->topk_groups != 0) return MOE_ERR_INVALID;
   if (s->top_k / s->topk_groups > s->n_experts / s->n_groups) return MOE_ERR_INVALID;
   if (s->n_experts > 512 || s->top_k > 16 || s->n_groups > 64) return MOE_ERR_UNSUPPORTED;
-  const int q = s->dtype == MOE_DTYPE_BF16 ? 64 : 32;
+  // reduction lengths come in whole k-slices of 128 bytes per row
+  const int q = s->dtype == MOE_DTYPE_MXFP8 ? 128 : s->dtype == MOE_DTYPE_BF16 ? 64 : 32;
   if (s->d_model % q || s->d_ff % q || s->d_ff_shared % q) return MOE_ERR_UNSUPPORTED;
   const long long A = s->T * (long long)s->top_k;
   long long wmax = s->d_model;
@@ -70,7 +72,8 @@ Workspace layout_workspace(const moe_shape& s, void* ws) {
   Workspace w{};
   const size_t T = (size_t)s.T, N = (size_t)s.n_experts, k = (size_t)s.top_k;
   const size_t A = T * k, d = (size_t)s.d_model;
-  const size_t es = s.dtype == MOE_DTYPE_BF16 ? 2 : 4;
+  // bytes per activation element (an MXFP8 h takes 1 + 1/32 bytes: fits in 2)
+  const size_t es = act_bf16(s) ? 2 : 4;
   const size_t nchunks = (A + kDispatchChunk - 1) / kDispatchChunk;
   plan_caps(s, w.plan1_cap, w.plan2_cap);
   size_t off = 0;
@@ -101,11 +104,13 @@ Workspace layout_workspace(const moe_shape& s, void* ws) {
   w.y_perm = take(A * d * es);
   w.y_shared = take(T * d * es);
   w.pmean = static_cast<double*>(take(N * 8));
-  w.wsplit = static_cast<bf16_t*>(take(s.dtype == MOE_DTYPE_BF16 ? 3 * N * d * 2 : 0));
+  w.wsplit = static_cast<bf16_t*>(take(act_bf16(s) ? 3 * N * d * 2 : 0));
   w.router_part = static_cast<float*>(take((size_t)router_split_chunks(s) * T * N * 4));
   w.stats_rows = static_cast<double*>(take((A + T) * 4 * 8));
   w.stats_ent = static_cast<double*>(take(T * 2 * 8));
   w.ec_row = static_cast<int32_t*>(take(T * N * 4));
+  w.xq = static_cast<unsigned char*>(
+      take(s.dtype == MOE_DTYPE_MXFP8 ? T * d + T * d / kMxBlock : 0));
   w.total = off;
   return w;
 }
@@ -148,6 +153,17 @@ int64_t moe_capacity(const moe_shape* shape) {
 size_t moe_workspace_bytes(const moe_shape* shape) {
   if (check_shape(shape) != MOE_OK) return 0;
   return layout_workspace(*shape, nullptr).total;
+}
+
+moe_status moe_quantize_mx(const void* in, int32_t in_dtype, int64_t rows, int64_t cols,
+                           void* out, void* stream) {
+  if (!in || !out || rows < 1 || cols < kMxBlock || cols % kMxBlock) return MOE_ERR_INVALID;
+  if (in_dtype != MOE_DTYPE_F32 && in_dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID;
+  if (!aligned16({in, out})) return MOE_ERR_INVALID;
+  if (rows > (int64_t(1) << 40) / cols) return MOE_ERR_UNSUPPORTED;
+  unsigned char* codes = static_cast<unsigned char*>(out);
+  return hip_status(launch_mx_quantize(in, in_dtype, rows, cols, codes, codes + rows * cols,
+                                       static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_route(const moe_shape* shape, const void* x, const float* w_router,

@@ -23,6 +23,38 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
   return static_cast<bf16_t>(u >> 16);
 }
 
+// ---- MXFP8 (OCP Microscaling v1.0: E4M3 elements, one E8M0 scale per 32
+// consecutive values along the reduction axis) ----
+constexpr int kMxBlock = 32;
+
+// shared exponent X of a block from its largest magnitude (NaN excluded by
+// the caller): floor(log2(amax)) - 8, 8 being the exponent of the top E4M3
+// binade, clamped to [-127, 127]; zero (and any fp32 subnormal maximum)
+// gives -127, an infinite maximum 127.  Stored as the E8M0 byte X + 127.
+__device__ __forceinline__ int mx_shared_exp(float amax) {
+  const uint32_t u = __float_as_uint(amax);
+  if (u >= 0x7f800000u) return 127;
+  const int X = (int)(u >> 23) - 127 - 8;
+  return ((u >> 23) == 0 || X < -127) ? -127 : X;
+}
+
+// E4M3 code of v / 2^X: nearest, ties to the even mantissa, saturating at
+// 448; NaN gives the NaN code; the sign bit is kept.  The scaling by 2^-X is
+// exact except for results far below the smallest code (which round to 0).
+__device__ __forceinline__ uint32_t e4m3_code(float v, int X) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fabsf(v);
+  if (!(a == a)) return sign | 0x7Fu;
+  const float s = ldexpf(a, -X);
+  if (!(s < 448.0f)) return sign | 0x7Eu;
+  if (s < 0.015625f) return sign | (uint32_t)rintf(s * 512.0f);  // subnormals: 2^-9 steps
+  // round the fp32 mantissa to 3 bits at bit 20 (ties to even); a carry
+  // moves into the exponent, which is what the next binade's code needs
+  const uint32_t us = __float_as_uint(s);
+  const uint32_t r = us + 0x7FFFFu + ((us >> 20) & 1u);
+  return sign | ((r >> 20) - (120u << 3));
+}
+
 constexpr int kWave = 64;
 constexpr int kDispatchChunk = 512;  // assignments ranked by one block
 
@@ -30,6 +62,9 @@ constexpr int kDispatchChunk = 512;  // assignments ranked by one block
 // families are defined with their kernel.
 constexpr int kBMf = 32;
 constexpr int kBNf = 32;
+
+// activations (x, y, y_perm, y_shared) are bf16 in bf16 and MXFP8 layers
+inline bool act_bf16(const moe_shape& s) { return s.dtype != MOE_DTYPE_F32; }
 
 // one unit of grouped-GEMM work: rows [row0, row0+nrows) of segment `seg`
 // (seg < N: routed expert, seg == N: shared expert), output column tile `nt`
@@ -64,6 +99,7 @@ struct Workspace {
   double* stats_rows;  // [T*k + T][4] per-row output moments (telemetry)
   double* stats_ent;   // [T][2] per-token gate / score entropy (telemetry)
   int32_t* ec_row;     // [T][N] row of each (token, expert) pair, expert choice
+  unsigned char* xq;   // MXFP8 layers: x as a packed MX matrix [T, d]
   size_t total;
   int64_t plan1_cap, plan2_cap;
 };
@@ -110,6 +146,10 @@ hipError_t launch_router_stats(const moe_shape& s, const int32_t* counts, const 
 hipError_t launch_bias_update_seq(const moe_shape& s, const int32_t* topk_idx,
                                   const int32_t* seq_off, int n_seq, float step, float clamp,
                                   float* bias, int32_t* err, const Workspace& w, hipStream_t st);
+
+// MXFP8 quantisation of a [rows, cols] bf16/fp32 matrix (cols % 32 == 0)
+hipError_t launch_mx_quantize(const void* in, int in_dtype, int64_t rows, int64_t cols,
+                              unsigned char* codes, unsigned char* scales, hipStream_t st);
 
 // expert choice: per-expert capacity min(C, T) (-1 without a capacity)
 int64_t ec_capacity(const moe_shape& s);

@@ -382,7 +382,7 @@ __global__ __launch_bounds__(256) void topk_kernel(
 
 // chunks of the split router GEMM for small batches (0: one pass per block)
 int router_split_chunks(const moe_shape& s) {
-  if (s.dtype != MOE_DTYPE_BF16) return 0;
+  if (!act_bf16(s)) return 0;
   const long long blocks = ((s.T + RM_BM - 1) / RM_BM) * ((s.n_experts + RM_BN - 1) / RM_BN);
   const int nkc = (s.d_model + RM_KC - 1) / RM_KC;
   return (blocks < 128 && nkc > 1) ? nkc : 0;
@@ -395,7 +395,7 @@ hipError_t launch_router_gemm(const moe_shape& s, const void* x, const float* w_
                               float* logits, const Workspace& w, hipStream_t st, int* nparts) {
   const int T = (int)s.T, N = s.n_experts, d = s.d_model;
   *nparts = 1;
-  if (s.dtype == MOE_DTYPE_BF16) {
+  if (act_bf16(s)) {
     const long long n = (long long)N * d;
     split3_kernel<<<(int)min((n + 255) / 256, 2048LL), 256, 0, st>>>(w_router, w.wsplit, n);
     const int nkc = router_split_chunks(s);

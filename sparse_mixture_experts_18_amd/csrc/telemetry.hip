@@ -328,7 +328,7 @@ hipError_t launch_router_stats(const moe_shape& s, const int32_t* counts, const 
                                const void* y_perm, const void* y_shared, double* stats,
                                const Workspace& w, hipStream_t st) {
   const int T = (int)s.T, N = s.n_experts, k = s.top_k, d = s.d_model;
-  const bool bf = s.dtype == MOE_DTYPE_BF16;
+  const bool bf = act_bf16(s);
   double* part = w.stats_rows;                       // [T*k][4]
   double* part_sh = w.stats_rows + (size_t)T * k * 4;  // [T][4]
   if (y_perm) {
