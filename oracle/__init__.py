@@ -9,5 +9,5 @@ from .moe_ref import (  # noqa: F401
     group_candidates, moe_layer, router_logits, scores_from_logits,
     router_stats, selection_keys, silu, swiglu_ffn, topk_select,
     MX_BLOCK, E4M3_MAX, e4m3_decode, e4m3_encode, mx_quantize, mx_dequantize,
-    mx_round, swiglu_ffn_mx,
+    mx_round, swiglu_ffn_mx, moe_layer_latent,
 )

@@ -55,6 +55,11 @@ in the sources):
         OCP Microscaling Formats (MX) v1.0 specification, MXFP8 = E4M3
         elements sharing one E8M0 power-of-two scale per 32 consecutive
         values.
+  [LAT] "MoE common taste of open models", section 10 (LatentMoE): the
+        routed-expert path moves into a low-dimensional latent space -- the
+        hidden state is first projected down, and the experts' compute,
+        parameters and dispatch payload are paid in the latent width; the
+        price is an extra down- and up-projection.
   [SEQ] "MoE architecture in practice", section "load-balancing loss"
         (update_bias from per-sequence loads, so that long sequences do not
         dominate), and its long-context section (sequence-level balancing).
@@ -716,3 +721,40 @@ def moe_layer_ec(x: np.ndarray, w_router: np.ndarray, w1, w2, *, C: int, k: int,
         y += swiglu_ffn(x, w1_shared, w2_shared)
     out["y"] = y
     return out
+
+
+# ---------------------------------------------------------------------------
+# LatentMoE ([LAT])
+# ---------------------------------------------------------------------------
+
+
+def moe_layer_latent(x: np.ndarray, w_router: np.ndarray, w_down: np.ndarray,
+                     w_up: np.ndarray, w1, w2, *, top_k: int,
+                     w1_shared: Optional[np.ndarray] = None,
+                     w2_shared: Optional[np.ndarray] = None,
+                     scores_fp32: Optional[np.ndarray] = None,
+                     tokens: Optional[Sequence[int]] = None,
+                     compute_outputs: bool = True, **route_kw) -> Dict[str, np.ndarray]:
+    """One LatentMoE layer forward ([LAT]).  The router, the selection and the
+    dispatch are those of moe_layer, on the hidden state x [T, d]; the routed
+    path runs in the latent width l: z = x W_down^T (W_down [l, d]), the
+    experts E_e (w1 [N, 2*d_ff, l], w2 [N, l, d_ff]) act on z, their gated sum
+    is formed in the latent space, y_lat = sum_j g_j E_j(z), and projected
+    back, y = y_lat W_up^T (W_up [d, l]); the shared expert acts on x at full
+    width and is added.  fp64."""
+    x = np.asarray(x, np.float64)
+    out = moe_layer(x, w_router, w1, w2, top_k=top_k, scores_fp32=scores_fp32,
+                    compute_outputs=False, **route_kw)
+    if not compute_outputs:
+        return out
+    s32 = out["scores"].astype(f32) if scores_fp32 is None else np.asarray(scores_fp32, f32)
+    z = x @ np.asarray(w_down, np.float64).T
+    lat = moe_layer(z, w_router, w1, w2, top_k=top_k, scores_fp32=s32, tokens=tokens,
+                    **route_kw)
+    rows = lat["rows"]
+    y = lat["y"] @ np.asarray(w_up, np.float64).T
+    if w1_shared is not None:
+        y = y + swiglu_ffn(x[rows], w1_shared, w2_shared)
+    out.update(z=z, y_latent=lat["y"], y=y, rows=rows)
+    return out
+

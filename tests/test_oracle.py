@@ -750,3 +750,63 @@ def test_moe_layer_mx_close_to_unquantised_layer():
     assert np.array_equal(a["topk_idx"], b["topk_idx"])
     err = np.linalg.norm(a["y"] - b["y"]) / np.linalg.norm(a["y"])
     assert 1e-3 < err < 0.08
+
+
+# -------------------------------------------------------------- LatentMoE ---
+
+def _latent_case(seed, T=12, d=16, l=8, N=5, f=12, k=2, shared=True):
+    r = rng(seed)
+    x = r.standard_normal((T, d))
+    wr = r.standard_normal((N, d)) / 4
+    wd = r.standard_normal((l, d)) / 4
+    wu = r.standard_normal((d, l)) / 3
+    w1 = r.standard_normal((N, 2 * f, l)) / 3
+    w2 = r.standard_normal((N, l, f)) / 3
+    w1s = r.standard_normal((2 * f, d)) / 4 if shared else None
+    w2s = r.standard_normal((d, f)) / 3 if shared else None
+    return x, wr, wd, wu, w1, w2, w1s, w2s
+
+
+def test_latent_identity_projections_give_the_plain_layer():
+    """l = d and W_down = W_up = I: the LatentMoE layer is the plain layer."""
+    x, wr, _, _, _, _, w1s, w2s = _latent_case(60, l=16)
+    r = rng(61)
+    w1 = r.standard_normal((5, 24, 16)) / 3
+    w2 = r.standard_normal((5, 16, 12)) / 3
+    eye = np.eye(16)
+    a = R.moe_layer_latent(x, wr, eye, eye, w1, w2, top_k=2, w1_shared=w1s, w2_shared=w2s)
+    b = R.moe_layer(x, wr, w1, w2, top_k=2, w1_shared=w1s, w2_shared=w2s)
+    assert np.array_equal(a["topk_idx"], b["topk_idx"])
+    assert np.allclose(a["y"], b["y"], rtol=0, atol=1e-12)
+
+
+def test_latent_explicit_loops():
+    """y_t = W_up (sum_j g_tj E_j(W_down x_t)) + S(x_t), written with loops;
+    the routing does not depend on the projections."""
+    x, wr, wd, wu, w1, w2, w1s, w2s = _latent_case(62)
+    out = R.moe_layer_latent(x, wr, wd, wu, w1, w2, top_k=2, w1_shared=w1s, w2_shared=w2s)
+    plain = R.moe_layer(x, wr, np.zeros((5, 24, 16)), np.zeros((5, 16, 12)), top_k=2,
+                        compute_outputs=False)
+    assert np.array_equal(out["topk_idx"], plain["topk_idx"])
+    T, d, l, f = 12, 16, 8, 12
+    for t in range(T):
+        z = [sum(wd[a, i] * x[t, i] for i in range(d)) for a in range(l)]
+        ylat = [0.0] * l
+        for j in range(2):
+            e = out["topk_idx"][t, j]
+            g = out["topk_w"][t, j]
+            h = []
+            for c in range(f):
+                a_ = sum(w1[e, c, i] * z[i] for i in range(l))
+                u_ = sum(w1[e, f + c, i] * z[i] for i in range(l))
+                h.append(a_ / (1 + math.exp(-a_)) * u_)
+            for i in range(l):
+                ylat[i] += g * sum(w2[e, i, c] * h[c] for c in range(f))
+        for i in range(d):
+            hs = []
+            for c in range(f):
+                a_ = sum(w1s[c, q] * x[t, q] for q in range(d))
+                u_ = sum(w1s[f + c, q] * x[t, q] for q in range(d))
+                hs.append(a_ / (1 + math.exp(-a_)) * u_)
+            ref = sum(wu[i, a] * ylat[a] for a in range(l)) + sum(w2s[i, c] * hs[c] for c in range(f))
+            assert abs(out["y"][t, i] - ref) <= 1e-10 * (1 + abs(ref))
