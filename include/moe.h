@@ -357,6 +357,35 @@ moe_status moe_forward(const moe_shape* shape, const void* x,
                        int32_t* n_kept_dropped, void* ws, size_t ws_bytes,
                        void* stream);
 
+/* LatentMoE layer forward ("MoE common taste of open models", section 10:
+ * the routed-expert path runs in a low-dimensional latent space -- the
+ * hidden state is projected down first, and the experts' compute,
+ * parameters and payload are paid in the latent width, at the price of an
+ * extra down- and up-projection).  Router, selection, gates, capacity and
+ * dispatch exactly as moe_forward, on the hidden state x [T, d_model];
+ * then z = x W_down^T, the routed experts E_e act on z (w1 [N, 2*d_ff,
+ * d_latent], w2 [N, d_latent, d_ff]), y_lat_t = sum_kept g_tj E_j(z_t)
+ * (rounded to the activation dtype), and y = y_lat W_up^T + S(x), the
+ * shared expert at full width (w1_shared [2*d_ff_shared, d_model],
+ * w2_shared [d_model, d_ff_shared]) added before the final rounding.
+ * w_down [d_latent, d_model], w_up [d_model, d_latent], activation dtype
+ * (MOE_DTYPE_F32 or MOE_DTYPE_BF16; MXFP8 is MOE_ERR_UNSUPPORTED).  d_latent
+ * obeys the d_model rules of moe_check_shape.  Optional outputs as in
+ * moe_forward.  The workspace is moe_latent_workspace_bytes(shape,
+ * d_latent) bytes (0 on an invalid shape or width); it is not
+ * interchangeable with a moe_workspace_bytes one. */
+size_t moe_latent_workspace_bytes(const moe_shape* shape, int32_t d_latent);
+moe_status moe_forward_latent(const moe_shape* shape, int32_t d_latent,
+                              const void* x, const float* w_router,
+                              const float* logit_add, const float* bias,
+                              const void* w_down, const void* w_up,
+                              const void* w1, const void* w2,
+                              const void* w1_shared, const void* w2_shared,
+                              void* y, float* scores_out, int32_t* topk_idx,
+                              float* topk_w, int32_t* counts, int32_t* offsets,
+                              int32_t* slot, int32_t* n_kept_dropped, void* ws,
+                              size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -11,7 +11,8 @@ argument order, tensors in place of pointers):
     moe_route, moe_dispatch, moe_expert_plan, moe_expert_ffn, moe_expert_gate_up,
     moe_expert_down, moe_combine, moe_bias_update, moe_bias_update_seq,
     moe_router_stats, moe_router_stats_count, moe_route_ec, moe_combine_ec,
-    moe_forward_ec, moe_ec_capacity, moe_quantize_mx, moe_forward,
+    moe_forward_ec, moe_ec_capacity, moe_quantize_mx, moe_latent_workspace_bytes,
+    moe_forward_latent, moe_forward,
     moe_workspace_bytes, moe_check_shape, moe_capacity, moe_status_string,
     moe_abi_version
 
@@ -123,6 +124,9 @@ _SIGS = {
                                            ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_quantize_mx": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, _P,
                                        _P]),
+    "moe_latent_workspace_bytes": (ctypes.c_size_t, [_S, ctypes.c_int32]),
+    "moe_forward_latent": (ctypes.c_int, [_S, ctypes.c_int32] + [_P] * 19 + [ctypes.c_size_t,
+                                                                           _P]),
     "moe_ec_capacity": (ctypes.c_int64, [_S]),
     "moe_route_ec": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                     _P]),
@@ -412,6 +416,44 @@ def moe_forward_ec(shape, x, w_router, logit_add, w1, w2, w1_shared, w2_shared, 
         _ptr(offsets, "offsets", torch.int32, N + 1), _ptr(row_of, "row_of", torch.int32, T * N),
         p, n, _stream(stream))
     _check(st, "moe_forward_ec")
+
+
+def moe_latent_workspace_bytes(shape: MoeShape, d_latent: int) -> int:
+    return lib().moe_latent_workspace_bytes(ctypes.byref(shape), int(d_latent))
+
+
+def latent_workspace(shape: MoeShape, d_latent: int, device="cuda") -> torch.Tensor:
+    """A 256-byte aligned uint8 workspace of moe_latent_workspace_bytes."""
+    n = moe_latent_workspace_bytes(shape, d_latent)
+    if n == 0:
+        _check(moe_check_shape(shape) or MOE_ERR_INVALID, "moe_latent_workspace_bytes")
+    buf = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    off = (-buf.data_ptr()) % 256
+    return buf[off:off + n]
+
+
+def moe_forward_latent(shape, d_latent, x, w_router, logit_add, bias, w_down, w_up, w1, w2,
+                       w1_shared, w2_shared, y, scores_out, topk_idx, topk_w, counts, offsets,
+                       slot, n_kept_dropped, ws, stream=None):
+    T, N, k, d, f, fs = (shape.T, shape.n_experts, shape.top_k, shape.d_model, shape.d_ff,
+                         shape.d_ff_shared)
+    l = int(d_latent)
+    dt = _dt(shape)
+    p, n = _ws(ws)
+    st = lib().moe_forward_latent(
+        ctypes.byref(shape), l, _ptr(x, "x", dt, T * d),
+        _ptr(w_router, "w_router", torch.float32, N * d),
+        _ptr(logit_add, "logit_add", torch.float32, T * N),
+        _ptr(bias, "bias", torch.float32, N), _ptr(w_down, "w_down", dt, l * d),
+        _ptr(w_up, "w_up", dt, d * l), _ptr(w1, "w1", dt, N * 2 * f * l),
+        _ptr(w2, "w2", dt, N * l * f), _ptr(w1_shared, "w1_shared", dt, 2 * fs * d),
+        _ptr(w2_shared, "w2_shared", dt, d * fs), _ptr(y, "y", dt, T * d),
+        _ptr(scores_out, "scores_out", torch.float32, T * N),
+        _ptr(topk_idx, "topk_idx", torch.int32, T * k),
+        _ptr(topk_w, "topk_w", torch.float32, T * k), _ptr(counts, "counts", torch.int32, N),
+        _ptr(offsets, "offsets", torch.int32, N + 1), _ptr(slot, "slot", torch.int32, T * k),
+        _ptr(n_kept_dropped, "n_kept_dropped", torch.int32, 2), p, n, _stream(stream))
+    _check(st, "moe_forward_latent")
 
 
 def moe_combine(shape, y_perm, y_shared, slot, topk_w, y, stream=None):

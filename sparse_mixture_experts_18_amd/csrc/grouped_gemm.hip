@@ -241,6 +241,9 @@ struct GemmArgs {
   int N;
   const WorkItem* items;
   int32_t* hdr;
+  // plain (non-gated) products only: bf16 [rows, Nout] added to the fp32
+  // result before the final rounding (NULL: nothing added)
+  const unsigned char* addend;
 };
 
 // ---------------------------------------------------------------------------
@@ -663,6 +666,17 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, const WorkItem& it,
         }
       } else if (live) {
         bf16_t* crow = reinterpret_cast<bf16_t*>(Cm) + orow * Nout;
+        if (!GATED && g.addend) {
+          const bf16_t* arow = reinterpret_cast<const bf16_t*>(g.addend) + orow * Nout;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const u32x2_t ad = *reinterpret_cast<const u32x2_t*>(arow + c0 + 8 * q + 4 * fh);
+            v[4 * q] += __uint_as_float(ad[0] << 16);
+            v[4 * q + 1] += __uint_as_float(ad[0] & 0xFFFF0000u);
+            v[4 * q + 2] += __uint_as_float(ad[1] << 16);
+            v[4 * q + 3] += __uint_as_float(ad[1] & 0xFFFF0000u);
+          }
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           u32x2_t pk;
@@ -751,6 +765,7 @@ struct GemmArgsF {
   int N;
   const WorkItem* items;
   const int32_t* hdr;
+  const float* addend;  // plain products: [rows, Nout] added to the result (or NULL)
 };
 
 template <bool GATED>
@@ -806,7 +821,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgsF g) {
     for (int c = 0; c < 4; ++c) {
       const int col = n0 + cq + c;
       if (col >= Nout) continue;
-      crow[col] = GATED ? ag[c] / (1.0f + expf(-ag[c])) * au[c] : ag[c];
+      crow[col] = GATED ? ag[c] / (1.0f + expf(-ag[c])) * au[c]
+                        : ag[c] + (g.addend ? g.addend[(size_t)(it.row0 + r) * Nout + col] : 0.f);
     }
   }
 }
@@ -848,8 +864,8 @@ inline cbytes mx_sc(const void* p, size_t elems) { return p ? cb(p) + elems : nu
 inline bytes mx_sc(void* p, size_t elems) { return p ? mb(p) + elems : nullptr; }
 
 template <bool GATED, bool MX>
-void launch_tiles(const moe_shape& s, const GemmArgs& g, int64_t cap, hipStream_t st) {
-  if (narrow_tiles(s))
+void launch_tiles(bool narrow, const GemmArgs& g, int64_t cap, hipStream_t st) {
+  if (narrow)
     launch_mfma<GATED, MX, typename std::conditional<GATED, Cfg1n, Cfg2n>::type>(g, cap, st);
   else
     launch_mfma<GATED, MX, typename std::conditional<GATED, Cfg1, Cfg2>::type>(g, cap, st);
@@ -897,7 +913,7 @@ hipError_t launch_gemm1(const moe_shape& s, const void* x, const int32_t* perm, 
     GemmArgs g1{cb(x), cb(x), perm, s.top_k, cb(w1), cb(w1s), mb(h), mb(hs),
                 nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                 d, d, f, fs, (long long)2 * f * d, N, w.plan1, w.plan1_hdr};
-    launch_tiles<true, false>(s, g1, w.plan1_cap, st);
+    launch_tiles<true, false>(narrow_tiles(s), g1, w.plan1_cap, st);
   } else if (s.dtype == MOE_DTYPE_MXFP8) {
     hipError_t e = launch_mx_quantize(x, MOE_DTYPE_BF16, s.T, d, w.xq, w.xq + T * d, st);
     if (e != hipSuccess) return e;
@@ -906,7 +922,7 @@ hipError_t launch_gemm1(const moe_shape& s, const void* x, const int32_t* perm, 
                 xs, xs, mx_sc(w1, (size_t)N * 2 * f * d), mx_sc(w1s, (size_t)2 * fs * d),
                 mx_sc(h, A * f), mx_sc(hs, T * fs),
                 d, d, f, fs, (long long)2 * f * d, N, w.plan1, w.plan1_hdr};
-    launch_tiles<true, true>(s, g1, w.plan1_cap, st);
+    launch_tiles<true, true>(narrow_tiles(s), g1, w.plan1_cap, st);
   } else {
     GemmArgsF g1{static_cast<const float*>(x), static_cast<const float*>(x), perm, s.top_k,
                  static_cast<const float*>(w1), static_cast<const float*>(w1s),
@@ -931,9 +947,9 @@ hipError_t launch_gemm2(const moe_shape& s, const void* h, const void* hs, const
                 mx ? mx_sc(w2s, (size_t)d * fs) : nullptr, nullptr, nullptr,
                 f, fs, d, d, (long long)d * f, N, w.plan2, w.plan2_hdr};
     if (mx)
-      launch_tiles<false, true>(s, g2, w.plan2_cap, st);
+      launch_tiles<false, true>(narrow_tiles(s), g2, w.plan2_cap, st);
     else
-      launch_tiles<false, false>(s, g2, w.plan2_cap, st);
+      launch_tiles<false, false>(narrow_tiles(s), g2, w.plan2_cap, st);
   } else {
     GemmArgsF g2{static_cast<const float*>(h), static_cast<const float*>(hs), nullptr,
                  s.top_k, static_cast<const float*>(w2), static_cast<const float*>(w2s),
@@ -941,6 +957,70 @@ hipError_t launch_gemm2(const moe_shape& s, const void* h, const void* hs, const
                  (long long)d * f, N, w.plan2, w.plan2_hdr};
     gemm_f32_kernel<false><<<(int)((w.plan2_cap + 7) / 8 * 8), 256, 0, st>>>(g2);
   }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Dense products over all T rows (the LatentMoE projections and a shared
+// expert run on its own): one segment in the shared-expert slot of the work
+// lists (N = 0), the same kernels as the expert projections.
+// ---------------------------------------------------------------------------
+namespace {
+bool dense_narrow(const moe_shape& s) { return s.dtype != MOE_DTYPE_F32 && s.T <= kNarrowRows; }
+int dense_bm(const moe_shape& s) {
+  if (s.dtype == MOE_DTYPE_F32) return kBMf;
+  return dense_narrow(s) ? Cfg2n::BM : Cfg2::BM;
+}
+// output columns per item of a gated / plain product
+int dense_bn(const moe_shape& s, bool gated) {
+  if (s.dtype == MOE_DTYPE_F32) return kBNf;
+  const bool n = dense_narrow(s);
+  return gated ? (n ? Cfg1n::BNW : Cfg1::BNW) / 2 : (n ? Cfg2n::BNW : Cfg2::BNW);
+}
+}  // namespace
+
+int64_t dense_plan_cap(const moe_shape& s, int Nout, bool gated) {
+  return (int64_t)cdiv(s.T, dense_bm(s)) * cdiv(Nout, dense_bn(s, gated));
+}
+
+// list 1 (gated or plain, Nout1 columns, reduction K1) and, when p2 is given,
+// list 2 (plain, Nout2 columns, reduction K2) of dense products over T rows
+hipError_t launch_dense_plan(const moe_shape& s, bool gated1, int K1, int Nout1, WorkItem* p1,
+                             int32_t* h1, int K2, int Nout2, WorkItem* p2, int32_t* h2,
+                             hipStream_t st) {
+  const int bm = dense_bm(s);
+  const int n1 = cdiv(Nout1, dense_bn(s, gated1));
+  const int n2 = p2 ? cdiv(Nout2, dense_bn(s, false)) : 0;
+  plan_kernel<<<p2 ? 2 : 1, 1024, 0, st>>>(nullptr, 0, (int)s.T, 1, bm, bm, 0, n1, 0, n2, K1,
+                                           K1, p2 ? K2 : 64, p2 ? K2 : 64, p1, h1, p2, h2);
+  return hipGetLastError();
+}
+
+// C [T, Nout] = A [T, K] B^T (gated: SwiGLU of the gate and up halves of B,
+// Nout h columns; plain: plus `addend` when given), over a list built by
+// launch_dense_plan with the same geometry
+hipError_t launch_dense(const moe_shape& s, bool gated, const void* a, const void* b, void* c,
+                        const void* addend, int K, int Nout, const WorkItem* plan, int32_t* hdr,
+                        int64_t cap, hipStream_t st) {
+  if (s.dtype == MOE_DTYPE_F32) {
+    GemmArgsF g{static_cast<const float*>(a), static_cast<const float*>(a), nullptr, 1,
+                static_cast<const float*>(b), static_cast<const float*>(b),
+                static_cast<float*>(c), static_cast<float*>(c), K, K, Nout, Nout, 0, 0, plan,
+                hdr, static_cast<const float*>(addend)};
+    if (gated)
+      gemm_f32_kernel<true><<<(int)((cap + 7) / 8 * 8), 256, 0, st>>>(g);
+    else
+      gemm_f32_kernel<false><<<(int)((cap + 7) / 8 * 8), 256, 0, st>>>(g);
+    return hipGetLastError();
+  }
+  if (s.dtype != MOE_DTYPE_BF16) return hipErrorInvalidValue;
+  GemmArgs g{cb(a), cb(a), nullptr, 1, cb(b), cb(b), mb(c), mb(c),
+             nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+             K, K, Nout, Nout, 0, 0, plan, hdr, cb(addend)};
+  if (gated)
+    launch_tiles<true, false>(dense_narrow(s), g, cap, st);
+  else
+    launch_tiles<false, false>(dense_narrow(s), g, cap, st);
   return hipGetLastError();
 }
 

@@ -68,16 +68,18 @@ int64_t capacity_of(const moe_shape& s) {
   return c > s.top_k ? c : s.top_k;
 }
 
-Workspace layout_workspace(const moe_shape& s, void* ws) {
+// Regions of a workspace: routing and dispatch sized by `sr`, the expert
+// projections by `se` (the same shape, except in a LatentMoE layer, whose
+// experts run at the latent width without the shared expert).
+static Workspace layout_regions(const moe_shape& sr, const moe_shape& se, char* base,
+                                size_t& off) {
   Workspace w{};
-  const size_t T = (size_t)s.T, N = (size_t)s.n_experts, k = (size_t)s.top_k;
-  const size_t A = T * k, d = (size_t)s.d_model;
+  const size_t T = (size_t)sr.T, N = (size_t)sr.n_experts, k = (size_t)sr.top_k;
+  const size_t A = T * k, d = (size_t)sr.d_model, de = (size_t)se.d_model;
   // bytes per activation element (an MXFP8 h takes 1 + 1/32 bytes: fits in 2)
-  const size_t es = act_bf16(s) ? 2 : 4;
+  const size_t es = act_bf16(se) ? 2 : 4;
   const size_t nchunks = (A + kDispatchChunk - 1) / kDispatchChunk;
-  plan_caps(s, w.plan1_cap, w.plan2_cap);
-  size_t off = 0;
-  char* base = static_cast<char*>(ws);
+  plan_caps(se, w.plan1_cap, w.plan2_cap);
   auto take = [&](size_t bytes) -> void* {
     void* p = base ? base + off : nullptr;
     off += align_up(bytes ? bytes : 1);
@@ -99,20 +101,63 @@ Workspace layout_workspace(const moe_shape& s, void* ws) {
   w.plan1 = static_cast<WorkItem*>(take((size_t)w.plan1_cap * sizeof(WorkItem)));
   w.plan2_hdr = static_cast<int32_t*>(take(32 * 4));
   w.plan2 = static_cast<WorkItem*>(take((size_t)w.plan2_cap * sizeof(WorkItem)));
-  w.h = take(A * (size_t)s.d_ff * es);
-  w.h_shared = take(T * (size_t)s.d_ff_shared * es);
-  w.y_perm = take(A * d * es);
-  w.y_shared = take(T * d * es);
+  w.h = take(A * (size_t)se.d_ff * es);
+  w.h_shared = take(T * (size_t)se.d_ff_shared * es);
+  w.y_perm = take(A * de * es);
+  w.y_shared = take(T * de * es);
   w.pmean = static_cast<double*>(take(N * 8));
-  w.wsplit = static_cast<bf16_t*>(take(act_bf16(s) ? 3 * N * d * 2 : 0));
-  w.router_part = static_cast<float*>(take((size_t)router_split_chunks(s) * T * N * 4));
+  w.wsplit = static_cast<bf16_t*>(take(act_bf16(sr) ? 3 * N * d * 2 : 0));
+  w.router_part = static_cast<float*>(take((size_t)router_split_chunks(sr) * T * N * 4));
   w.stats_rows = static_cast<double*>(take((A + T) * 4 * 8));
   w.stats_ent = static_cast<double*>(take(T * 2 * 8));
   w.ec_row = static_cast<int32_t*>(take(T * N * 4));
   w.xq = static_cast<unsigned char*>(
-      take(s.dtype == MOE_DTYPE_MXFP8 ? T * d + T * d / kMxBlock : 0));
+      take(se.dtype == MOE_DTYPE_MXFP8 ? T * de + T * de / kMxBlock : 0));
+  return w;
+}
+
+Workspace layout_workspace(const moe_shape& s, void* ws) {
+  size_t off = 0;
+  Workspace w = layout_regions(s, s, static_cast<char*>(ws), off);
   w.total = off;
   return w;
+}
+
+moe_shape latent_expert_shape(const moe_shape& s, int d_latent) {
+  moe_shape e = s;
+  e.d_model = d_latent;
+  e.d_ff_shared = 0;
+  return e;
+}
+
+LatentWorkspace layout_latent(const moe_shape& s, int d_latent, void* ws) {
+  LatentWorkspace L{};
+  size_t off = 0;
+  char* base = static_cast<char*>(ws);
+  const moe_shape se = latent_expert_shape(s, d_latent);
+  L.w = layout_regions(s, se, base, off);
+  auto take = [&](size_t bytes) -> void* {
+    void* p = base ? base + off : nullptr;
+    off += align_up(bytes ? bytes : 1);
+    return p;
+  };
+  const size_t T = (size_t)s.T, es = act_bf16(s) ? 2 : 4;
+  const int fs = s.d_ff_shared;
+  L.z = take(T * d_latent * es);
+  L.y_lat = take(T * d_latent * es);
+  L.h_sh = take(T * (size_t)fs * es);
+  L.y_sh = take(T * (size_t)s.d_model * es);
+  L.cap_sh1 = fs > 0 ? dense_plan_cap(s, fs, true) : 1;
+  L.cap_down = dense_plan_cap(s, d_latent, false);
+  L.cap_up = dense_plan_cap(s, s.d_model, false);
+  L.hdr_sh1 = static_cast<int32_t*>(take(32 * 4));
+  L.plan_sh1 = static_cast<WorkItem*>(take((size_t)L.cap_sh1 * sizeof(WorkItem)));
+  L.hdr_down = static_cast<int32_t*>(take(32 * 4));
+  L.plan_down = static_cast<WorkItem*>(take((size_t)L.cap_down * sizeof(WorkItem)));
+  L.hdr_up = static_cast<int32_t*>(take(32 * 4));
+  L.plan_up = static_cast<WorkItem*>(take((size_t)L.cap_up * sizeof(WorkItem)));
+  L.total = off;
+  return L;
 }
 
 }  // namespace moe
@@ -482,6 +527,99 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_rou
     return MOE_ERR_HIP;
   return hip_status(
       launch_combine(sh, w.y_perm, shared ? w.y_shared : nullptr, sl, tw, y, s));
+}
+
+}  // extern "C"
+
+// ---- LatentMoE ----
+
+namespace {
+moe_status check_latent(const moe_shape* shape, int32_t d_latent) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (d_latent < 1) return MOE_ERR_INVALID;
+  if (shape->dtype == MOE_DTYPE_MXFP8) return MOE_ERR_UNSUPPORTED;
+  const moe_shape se = latent_expert_shape(*shape, d_latent);
+  return check_shape(&se);
+}
+}  // namespace
+
+extern "C" {
+
+size_t moe_latent_workspace_bytes(const moe_shape* shape, int32_t d_latent) {
+  if (check_latent(shape, d_latent) != MOE_OK) return 0;
+  return layout_latent(*shape, d_latent, nullptr).total;
+}
+
+moe_status moe_forward_latent(const moe_shape* shape, int32_t d_latent, const void* x,
+                              const float* w_router, const float* logit_add, const float* bias,
+                              const void* w_down, const void* w_up, const void* w1,
+                              const void* w2, const void* w1_shared, const void* w2_shared,
+                              void* y, float* scores_out, int32_t* topk_idx, float* topk_w,
+                              int32_t* counts, int32_t* offsets, int32_t* slot,
+                              int32_t* n_kept_dropped, void* ws, size_t ws_bytes,
+                              void* stream) {
+  moe_status st = check_latent(shape, d_latent);
+  if (st != MOE_OK) return st;
+  if (!x || !w_router || !w_down || !w_up || !w1 || !w2 || !y) return MOE_ERR_INVALID;
+  if (shape->d_ff_shared > 0 && (!w1_shared || !w2_shared)) return MOE_ERR_INVALID;
+  if (!aligned16({x, w_router, w_down, w_up, w1, w2, w1_shared, w2_shared, y}) ||
+      !aligned4({logit_add, bias, scores_out, topk_idx, topk_w, counts, offsets, slot,
+                 n_kept_dropped}))
+    return MOE_ERR_INVALID;
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) % 256) != 0) return MOE_ERR_WORKSPACE;
+  const LatentWorkspace L = layout_latent(*shape, d_latent, ws);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  const Workspace& w = L.w;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const moe_shape& sh = *shape;
+  const moe_shape se = latent_expert_shape(sh, d_latent);
+  const int d = sh.d_model, l = d_latent, fs = sh.d_ff_shared;
+  const bool shared = fs > 0;
+  float* sc = scores_out ? scores_out : w.scores;
+  int32_t* ti = topk_idx ? topk_idx : w.topk_idx;
+  float* tw = topk_w ? topk_w : w.topk_w;
+  int32_t* cn = counts ? counts : w.counts;
+  int32_t* of = offsets ? offsets : w.offsets;
+  int32_t* sl = slot ? slot : w.slot;
+  int32_t* nk = n_kept_dropped ? n_kept_dropped : w.nkd;
+  // routing and dispatch on the hidden state
+  int np = 1;
+  if (launch_router_gemm(sh, x, w_router, w.logits, w, s, &np) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_topk(sh, np > 1 ? w.router_part : w.logits, np, nullptr, logit_add, false, bias, sc,
+                  ti, tw, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (launch_dispatch(sh, ti, cn, of, sl, w.perm, nk, w, s) != hipSuccess) return MOE_ERR_HIP;
+  // work lists: the experts at the latent width, the dense products over T rows
+  if (launch_plan(se, of, w, s) != hipSuccess) return MOE_ERR_HIP;
+  hipError_t e = shared ? launch_dense_plan(sh, true, d, fs, L.plan_sh1, L.hdr_sh1, d, l,
+                                            L.plan_down, L.hdr_down, s)
+                        : launch_dense_plan(sh, false, d, l, L.plan_down, L.hdr_down, 0, 0,
+                                            nullptr, nullptr, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  if (launch_dense_plan(sh, false, l, d, L.plan_up, L.hdr_up, 0, 0, nullptr, nullptr, s) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
+  // z = x W_down^T; the routed experts on z; their gated sum at the latent width
+  if (launch_dense(sh, false, x, w_down, L.z, nullptr, d, l, L.plan_down, L.hdr_down,
+                   L.cap_down, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (launch_gemm1(se, L.z, w.perm, w1, nullptr, w.h, nullptr, w, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (launch_gemm2(se, w.h, nullptr, w2, nullptr, w.y_perm, nullptr, w, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (launch_combine(se, w.y_perm, nullptr, sl, tw, L.y_lat, s) != hipSuccess) return MOE_ERR_HIP;
+  // the shared expert at full width, then y = y_lat W_up^T + shared
+  if (shared) {
+    if (launch_dense(sh, true, x, w1_shared, L.h_sh, nullptr, d, fs, L.plan_sh1, L.hdr_sh1,
+                     L.cap_sh1, s) != hipSuccess)
+      return MOE_ERR_HIP;
+    if (launch_dense(sh, false, L.h_sh, w2_shared, L.y_sh, nullptr, fs, d, L.plan_up, L.hdr_up,
+                     L.cap_up, s) != hipSuccess)
+      return MOE_ERR_HIP;
+  }
+  return hip_status(launch_dense(sh, false, L.y_lat, w_up, y, shared ? L.y_sh : nullptr, l, d,
+                                 L.plan_up, L.hdr_up, L.cap_up, s));
 }
 
 }  // extern "C"

@@ -107,6 +107,20 @@ struct Workspace {
 // Carve `ws` (may be NULL to only compute sizes) for a validated shape.
 Workspace layout_workspace(const moe_shape& s, void* ws);
 
+// LatentMoE: the routing regions of the full shape, the expert regions of the
+// latent shape (d_model = d_latent, no shared expert), the latent rows z and
+// y_lat, the shared expert's h and output, and the dense work lists
+struct LatentWorkspace {
+  Workspace w;
+  void *z, *y_lat, *h_sh, *y_sh;
+  WorkItem *plan_sh1, *plan_down, *plan_up;
+  int32_t *hdr_sh1, *hdr_down, *hdr_up;
+  int64_t cap_sh1, cap_down, cap_up;
+  size_t total;
+};
+moe_shape latent_expert_shape(const moe_shape& s, int d_latent);
+LatentWorkspace layout_latent(const moe_shape& s, int d_latent, void* ws);
+
 int64_t capacity_of(const moe_shape& s);  // -1 = dropless
 
 constexpr int kStatsGlobal = 16;   // doubles of global indicators
@@ -146,6 +160,15 @@ hipError_t launch_router_stats(const moe_shape& s, const int32_t* counts, const 
 hipError_t launch_bias_update_seq(const moe_shape& s, const int32_t* topk_idx,
                                   const int32_t* seq_off, int n_seq, float step, float clamp,
                                   float* bias, int32_t* err, const Workspace& w, hipStream_t st);
+
+// dense products over the T rows of a shape (one work-list segment)
+int64_t dense_plan_cap(const moe_shape& s, int Nout, bool gated);
+hipError_t launch_dense_plan(const moe_shape& s, bool gated1, int K1, int Nout1, WorkItem* p1,
+                             int32_t* h1, int K2, int Nout2, WorkItem* p2, int32_t* h2,
+                             hipStream_t st);
+hipError_t launch_dense(const moe_shape& s, bool gated, const void* a, const void* b, void* c,
+                        const void* addend, int K, int Nout, const WorkItem* plan, int32_t* hdr,
+                        int64_t cap, hipStream_t st);
 
 // MXFP8 quantisation of a [rows, cols] bf16/fp32 matrix (cols % 32 == 0)
 hipError_t launch_mx_quantize(const void* in, int in_dtype, int64_t rows, int64_t cols,

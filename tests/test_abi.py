@@ -177,3 +177,45 @@ def test_binding_rejects_cpu_tensors(m):
     x = torch.zeros(64, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         m._ptr(x, "x", torch.bfloat16, 64 * 128)
+
+
+def test_mxfp8_and_latent_host_checks(m):
+    """MXFP8 needs reduction lengths in whole 128-value slices; the quantiser
+    and the LatentMoE entry reject bad arguments before any launch."""
+    L = m.lib()
+    P = ctypes.c_void_p
+    fake = P(4096)
+    assert m.moe_check_shape(shape(dtype="mxfp8", d_model=128, d_ff=128)) == m.MOE_OK
+    assert m.moe_check_shape(shape(dtype="mxfp8", d_model=192, d_ff=128)) == \
+        m.MOE_ERR_UNSUPPORTED
+    assert m.moe_workspace_bytes(shape(dtype="mxfp8", d_model=128, d_ff=128)) > \
+        m.moe_workspace_bytes(shape(dtype="bf16", d_model=128, d_ff=128))
+    # quantiser: cols must be whole blocks of 32, pointers 16-byte aligned, dtype bf16/fp32
+    assert L.moe_quantize_mx(fake, m.MOE_DTYPE_BF16, 4, 48, fake, None) == m.MOE_ERR_INVALID
+    assert L.moe_quantize_mx(fake, m.MOE_DTYPE_BF16, 0, 64, fake, None) == m.MOE_ERR_INVALID
+    assert L.moe_quantize_mx(P(4096 + 4), m.MOE_DTYPE_F32, 4, 64, fake, None) == \
+        m.MOE_ERR_INVALID
+    assert L.moe_quantize_mx(fake, m.MOE_DTYPE_MXFP8, 4, 64, fake, None) == m.MOE_ERR_INVALID
+    assert L.moe_quantize_mx(None, m.MOE_DTYPE_F32, 4, 64, fake, None) == m.MOE_ERR_INVALID
+    # LatentMoE: workspace size and argument checks
+    s = shape(d_ff_shared=128)
+    n = m.moe_latent_workspace_bytes(s, 64)
+    assert n > 0 and n % 256 == 0
+    assert m.moe_latent_workspace_bytes(s, 0) == 0
+    assert m.moe_latent_workspace_bytes(s, 96) == 0          # not a multiple of 64 (bf16)
+    assert m.moe_latent_workspace_bytes(shape(dtype="mxfp8", d_model=128, d_ff=128), 128) == 0
+    big = 1 << 40
+    ws_ok = P(256 * 1000)
+    args = [fake] * 10 + [fake] + [None] * 7
+    # missing w_up, missing shared weights, bad width, small workspace
+    a = list(args); a[5] = None
+    assert L.moe_forward_latent(ctypes.byref(s), 64, *a, ws_ok, big, None) == m.MOE_ERR_INVALID
+    a = list(args); a[8] = None
+    assert L.moe_forward_latent(ctypes.byref(s), 64, *a, ws_ok, big, None) == m.MOE_ERR_INVALID
+    assert L.moe_forward_latent(ctypes.byref(s), 96, *args, ws_ok, big, None) == \
+        m.MOE_ERR_UNSUPPORTED
+    assert L.moe_forward_latent(ctypes.byref(s), 64, *args, ws_ok, 16, None) == \
+        m.MOE_ERR_WORKSPACE
+    ms = shape(dtype="mxfp8", d_model=128, d_ff=128)
+    assert L.moe_forward_latent(ctypes.byref(ms), 128, *args, ws_ok, big, None) == \
+        m.MOE_ERR_UNSUPPORTED

@@ -186,6 +186,63 @@ def make_inputs(cfg: LayerConfig, seed: int = 0, device="cpu",
     return inp
 
 
+@dataclasses.dataclass
+class LatentInputs:
+    base: LayerInputs        # x, router, bias, logit offsets, shared expert (full width)
+    d_latent: int
+    w_down: torch.Tensor     # [d_latent, d]
+    w_up: torch.Tensor       # [d, d_latent]
+    w1: torch.Tensor         # [N, 2*d_ff, d_latent]
+    w2: torch.Tensor         # [N, d_latent, d_ff]
+
+
+def make_latent_inputs(cfg: LayerConfig, d_latent: int, seed: int = 0, device="cpu",
+                       T: Optional[int] = None) -> LatentInputs:
+    """Inputs of a LatentMoE layer of the same workload: the base layer's
+    tokens, router, bias, logit offsets and shared expert, plus the two
+    projections and routed experts of latent width d_latent (normals scaled
+    by 1/sqrt(fan_in), like every other weight)."""
+    T = cfg.T if T is None else T
+    dt = torch_dtype(cfg)
+    N, d, f, l = cfg.n_experts, cfg.d_model, cfg.d_ff, d_latent
+    x = make_x(cfg, seed, device, T)
+    w_router = _normal((N, d), 1.0 / math.sqrt(d), torch.float32, device,
+                       seed, cfg.name, "w_router")
+    inp = LayerInputs(cfg, x, w_router, torch.empty(0, device=device),
+                      torch.empty(0, device=device))
+    if cfg.d_ff_shared > 0:
+        fs = cfg.d_ff_shared
+        inp.w1_shared = _normal((2 * fs, d), 1.0 / math.sqrt(d), dt, device,
+                                seed, cfg.name, "w1_shared")
+        inp.w2_shared = _normal((d, fs), 1.0 / math.sqrt(fs), dt, device,
+                                seed, cfg.name, "w2_shared")
+    if cfg.bias_range > 0:
+        u = torch.rand((N,), generator=_gen(device, seed, cfg.name, "bias"),
+                       device=device, dtype=torch.float32)
+        inp.bias = (u * 2.0 - 1.0) * cfg.bias_range
+    elif cfg.bias_zero:
+        inp.bias = torch.zeros((N,), dtype=torch.float32, device=device)
+    if cfg.has_logit_add:
+        la = torch.zeros((T, N), dtype=torch.float32, device=device)
+        if cfg.zipf_s > 0:
+            ranks = torch.arange(1, N + 1, dtype=torch.float64, device=device)
+            la += (-cfg.zipf_s * torch.log(ranks)).to(torch.float32)[None, :]
+        if cfg.jitter_std > 0:
+            la += _normal((T, N), cfg.jitter_std, torch.float32, device,
+                          seed, cfg.name, "jitter", T)
+        inp.logit_add = la
+    w_down = _normal((l, d), 1.0 / math.sqrt(d), dt, device, seed, cfg.name, "w_down", l)
+    w_up = _normal((d, l), 1.0 / math.sqrt(l), dt, device, seed, cfg.name, "w_up", l)
+    w1 = torch.empty((N, 2 * f, l), dtype=dt, device=device)
+    w2 = torch.empty((N, l, f), dtype=dt, device=device)
+    for e in range(N):
+        w1[e].copy_(_normal((2 * f, l), 1.0 / math.sqrt(l), dt, device, seed, cfg.name,
+                            "w1_latent", l, e))
+        w2[e].copy_(_normal((l, f), 1.0 / math.sqrt(f), dt, device, seed, cfg.name,
+                            "w2_latent", l, e))
+    return LatentInputs(inp, l, w_down, w_up, w1, w2)
+
+
 def to_f64(t: torch.Tensor):
     """Exact upcast of a (bf16 / fp32) tensor to a float64 NumPy array on host."""
     return t.detach().to("cpu", torch.float64).numpy()
