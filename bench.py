@@ -22,6 +22,7 @@ Extra fields beside the contract's:
                 router unchanged): forward rate and the expert projections
                 against the fp8 MFMA and HBM peaks
   expert_choice the same layer routed by expert choice at C = k*T/N
+  latent        the LatentMoE variant of the layer at latent width d/4
 """
 from __future__ import annotations
 
@@ -379,6 +380,43 @@ def main():
         }
         del w1q, w2q, w1sq, w2sq, ws_mx, hq, hsq
 
+    # LatentMoE on the same workload at latent width d/4: routing on x, the
+    # experts (d_ff unchanged) on z = x W_down^T, y = y_lat W_up^T + shared
+    latent = None
+    l = d // 4
+    if cfg.dtype in ("bf16", "f32") and l % (64 if cfg.dtype == "bf16" else 32) == 0:
+        li = W.make_latent_inputs(cfg, l, seed=0, device=dev)
+        ws_l = moe.latent_workspace(shape, l, dev)
+        y_l = torch.empty_like(out["y"])
+
+        def lat_step():
+            moe.moe_forward_latent(shape, l, inp.x, inp.w_router, inp.logit_add, inp.bias,
+                                   li.w_down, li.w_up, li.w1, li.w2, inp.w1_shared,
+                                   inp.w2_shared, y_l, None, None, None, None, None, None,
+                                   None, ws_l)
+        for _ in range(2):
+            lat_step()
+        g_l = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_l):
+            lat_step()
+        for _ in range(2):
+            g_l.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            g_l.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        l_ms = e0.elapsed_time(e1) / args.steps
+        del g_l
+        l_flops = (2.0 * T * d * N + 4.0 * T * d * l + 6.0 * l * cfg.d_ff * n_kept
+                   + 6.0 * T * d * cfg.d_ff_shared)
+        latent = {"d_latent": l, "ms_per_step": round(l_ms, 4),
+                  "tokens/s": round(T / (l_ms * 1e-3), 1),
+                  "tflops": round(l_flops / (l_ms * 1e-3) / 1e12, 2),
+                  "expert_weight_bytes": int(li.w1.numel() + li.w2.numel()) * li.w1.element_size()}
+        del li, ws_l, y_l
+
     res = {
         "metric": METRIC,
         "value": round(T / (ms * 1e-3), 1),
@@ -408,6 +446,7 @@ def main():
         "telemetry": telemetry,
         "expert_choice": expert_choice,
         "mxfp8": mxfp8,
+        "latent": latent,
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
