@@ -571,43 +571,67 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, const WorkItem& it,
 #pragma unroll
       for (int j = 0; j < NT; ++j) sb_w[j] = sc[C::BM + b_row[j]] >> (8 * fh);
     }
-    // bf16: fragments of k-step ks+1 are read while the MFMAs of k-step ks
-    // run (two register sets).  MXFP8 fragments are twice as wide and each
-    // MFMA four times as long, so one set is read per k-step and the MFMAs
-    // start as soon as their own fragments have arrived.
-    constexpr int NB = MX ? 1 : 2;
-    FT bf[NB][NT], af[NB][MS];
-    load_frags<MX, C, MS>(As, Bs, a_row, b_row, fh, 0, af[0], bf[0]);
+    if constexpr (!MX) {
+      // fragments of k-step ks+1 are read while the MFMAs of k-step ks run
+      // (two register sets)
+      FT bf[2][NT], af[2][MS];
+      load_frags<MX, C, MS>(As, Bs, a_row, b_row, fh, 0, af[0], bf[0]);
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const int cur = MX ? 0 : (ks & 1);
-      if (MX && ks > 0) {
-        // keep the next step's fragment reads behind this point, so the two
-        // register sets are never live together
-        __builtin_amdgcn_sched_barrier(0);
-        load_frags<MX, C, MS>(As, Bs, a_row, b_row, fh, ks, af[0], bf[0]);
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const int cur = ks & 1;
+        // refill the buffers of slice kt-1: A behind the first fragment
+        // reads, B one k-step later, so the reads of k-step 0 are not queued
+        // behind a burst of loads
+        if (ks == 0 && kt + SA - 1 < nk) issue_a(kt + SA - 1);
+        if (ks == 1 && kt + SB - 1 < nk) issue_b(kt + SB - 1);
+        if (ks + 1 < KSTEPS)
+          load_frags<MX, C, MS>(As, Bs, a_row, b_row, fh, ks + 1, af[cur ^ 1], bf[cur ^ 1]);
+#pragma unroll
+        for (int i = 0; i < MS - 1; ++i)
+#pragma unroll
+          for (int j = 0; j < NT; ++j)
+            acc[i][j] = mma(bf[cur][j], af[cur][i], acc[i][j], 0, 0);
+        if (last) {
+#pragma unroll
+          for (int j = 0; j < NT; ++j)
+            acc[MS - 1][j] = mma(bf[cur][j], af[cur][MS - 1], acc[MS - 1][j], 0, 0);
+        }
       }
-      // refill the buffers of slice kt-1: A behind the first fragment reads,
-      // B one k-step later, so the reads of k-step 0 are not queued behind
-      // a burst of loads
-      if (ks == 0 && kt + SA - 1 < nk) issue_a(kt + SA - 1);
-      if (ks == 1 && kt + SB - 1 < nk) issue_b(kt + SB - 1);
-      if (!MX && ks + 1 < KSTEPS)
-        load_frags<MX, C, MS>(As, Bs, a_row, b_row, fh, ks + 1, af[(cur ^ 1) % NB],
-                              bf[(cur ^ 1) % NB]);
-      const int sh = 16 * ks;  // MXFP8: block 2ks + h sits 16 ks bits up
+    } else {
+      // MXFP8 fragments are twice as wide and each MFMA four times as long:
+      // one register set, each fragment re-read for the next k-step as soon
+      // as its last MFMA of this step is issued
+      FT bf[NT], af[MS];
+      load_frags<MX, C, MS>(As, Bs, a_row, b_row, fh, 0, af, bf);
 #pragma unroll
-      for (int i = 0; i < MS - 1; ++i)
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const bool more = ks + 1 < KSTEPS;
+        if (ks == 0 && kt + SA - 1 < nk) issue_a(kt + SA - 1);
+        if (ks == 1 && kt + SB - 1 < nk) issue_b(kt + SB - 1);
+        const int sh = 16 * ks;  // block 2ks + h sits 16 ks bits up
 #pragma unroll
-        for (int j = 0; j < NT; ++j)
-          acc[i][j] = mma(bf[cur][j], af[cur][i], acc[i][j], MX ? (int)(sb_w[j] >> sh) : 0,
-                          MX ? (int)(sa_w[i] >> sh) : 0);
-      if (last) {
+        for (int i = 0; i < MS - 1; ++i) {
 #pragma unroll
-        for (int j = 0; j < NT; ++j)
-          acc[MS - 1][j] = mma(bf[cur][j], af[cur][MS - 1], acc[MS - 1][j],
-                               MX ? (int)(sb_w[j] >> sh) : 0,
-                               MX ? (int)(sa_w[MS - 1] >> sh) : 0);
+          for (int j = 0; j < NT; ++j)
+            acc[i][j] = mma(bf[j], af[i], acc[i][j], (int)(sb_w[j] >> sh), (int)(sa_w[i] >> sh));
+          if (more)
+            af[i] = Frag<MX>::read(As + a_row[i] * C::ROWB, ks + 1, fh, C::swz(a_row[i]));
+        }
+        if (last) {
+#pragma unroll
+          for (int j = 0; j < NT; ++j) {
+            acc[MS - 1][j] = mma(bf[j], af[MS - 1], acc[MS - 1][j], (int)(sb_w[j] >> sh),
+                                 (int)(sa_w[MS - 1] >> sh));
+            if (more) bf[j] = Frag<MX>::read(Bs + b_row[j] * C::ROWB, ks + 1, fh, C::swz(b_row[j]));
+          }
+          if (more)
+            af[MS - 1] = Frag<MX>::read(As + a_row[MS - 1] * C::ROWB, ks + 1, fh,
+                                        C::swz(a_row[MS - 1]));
+        } else if (more) {
+#pragma unroll
+          for (int j = 0; j < NT; ++j)
+            bf[j] = Frag<MX>::read(Bs + b_row[j] * C::ROWB, ks + 1, fh, C::swz(b_row[j]));
+        }
       }
     }
   }
