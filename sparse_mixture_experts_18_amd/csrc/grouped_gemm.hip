@@ -244,6 +244,7 @@ struct GemmArgs {
   // plain (non-gated) products only: bf16 [rows, Nout] added to the fp32
   // result before the final rounding (NULL: nothing added)
   const unsigned char* addend;
+  int a_rows_r, a_rows_s;  // MXFP8: rows of the A matrices (bounds of their scale arrays)
 };
 
 // ---------------------------------------------------------------------------
@@ -290,16 +291,15 @@ struct GCfg {
   static constexpr int DROWS = 1024 / ROWB;   // rows per wave DMA instruction
   static constexpr int A_BYTES = BM * ROWB, B_BYTES = BNW * ROWB;
   static constexpr int A_LOADS = A_BYTES / 1024 / WAVES, B_LOADS = B_BYTES / 1024 / WAVES;
-  static constexpr int SCL = WAVES * 64 * 4;  // MXFP8 scale bytes of one slice
+  static constexpr int SGB = WAVES * 64 * 16;  // MXFP8 scale bytes of a 4-slice group
   // LDS per block; items with few rows use it for deeper rings.  160 KiB is
   // the whole CU (one block per CU); 80 KiB lets two blocks share a CU.
   static constexpr int LDS_BYTES = LDS_KIB_ * 1024;
   static constexpr int BLOCKS_PER_CU = 160 / LDS_KIB_;
   static constexpr int MAXS = MAXS_;  // deepest ring that items with few rows get
   static_assert(A_LOADS * 1024 * WAVES == A_BYTES && B_LOADS * 1024 * WAVES == B_BYTES, "");
-  static_assert(SA * (A_BYTES + SCL) + SB * B_BYTES <= LDS_BYTES, "LDS");
+  static_assert(SA * A_BYTES + SB * B_BYTES <= LDS_BYTES, "LDS");
   static_assert(SB >= SA && SA >= 2 && SB <= SA + 1, "B runs at most one slice ahead of A");
-  static_assert(BM + BNW <= WAVES * 64, "one scale DMA per wave covers every row");
   static_assert(ROWB == 128, "k-slices are 128 bytes per row");
   __device__ static __forceinline__ int swz(int r) { return (r / RP) % CPR; }
 };
@@ -312,6 +312,15 @@ struct GCfg {
 #endif
 using Cfg1 = GCfg<MOE_GEMM1_CFG>;
 using Cfg2 = GCfg<MOE_GEMM2_CFG>;
+// MXFP8 layers (the scale DMA needs BM + BNW <= 64 * WAVES)
+#ifndef MOE_GEMM1_MX_CFG
+#define MOE_GEMM1_MX_CFG 2, 4, 2, 64, 2, 2
+#endif
+#ifndef MOE_GEMM2_MX_CFG
+#define MOE_GEMM2_MX_CFG 2, 4, 2, 64, 2, 2
+#endif
+using Cfg1x = GCfg<MOE_GEMM1_MX_CFG>;
+using Cfg2x = GCfg<MOE_GEMM2_MX_CFG>;
 // Layers with few rows per expert (decode batches) stream the weights with
 // short items: 64 rows x 128 weight rows, four waves, and the LDS spent on a
 // four-deep ring.  Twice as many items as weight slabs of 256 rows spread
@@ -343,10 +352,12 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 // k-slice offset is the scalar soffset, so a load costs one VGPR.  Lane i
 // of a wave writes its 16 (or 4) bytes to lds_wave_base + 16 i (4 i).
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
-__device__ __forceinline__ rsrc_t make_rsrc(const unsigned char* base) {
-  // raw buffer (stride 0), every 32-bit offset in range; gfx9 dword 3
+__device__ __forceinline__ rsrc_t make_rsrc(const unsigned char* base,
+                                            uint32_t bytes = 0xFFFFFFFFu) {
+  // raw buffer (stride 0) of `bytes` bytes; reads past the end return 0;
+  // gfx9 dword 3
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(base), (short)0,
-                                           (int)0xFFFFFFFFu, 0x00020000);
+                                           (int)bytes, 0x00020000);
 }
 __device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff,
                                       unsigned char* lds_wave_base) {
@@ -419,6 +430,7 @@ template <bool GATED, bool MX, class C, int MS>
 __device__ __forceinline__ void gemm_body(const GemmArgs& g, const WorkItem& it,
                                           unsigned char* lds, int msub) {
   typedef typename Frag<MX>::T FT;
+  static_assert(!MX || C::BM + C::BNW <= C::WAVES * 64, "one scale DMA per wave covers every row");
   constexpr int ES = MX ? 1 : 2;         // bytes per element
   constexpr int KSTEPS = Frag<MX>::STEPS;
   const bool shared = it.seg == g.N;
@@ -465,12 +477,15 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, const WorkItem& it,
     const int r = (w * C::B_LOADS + j) * C::DROWS + drow;
     b_off[j] = (uint32_t)b_src(r) * (uint32_t)Kb + (dpos ^ C::swz(r)) * 16;
   }
-  // MXFP8 scales: lane gl = 64w + lane fetches the 4 scale bytes of a slice
-  // for tile row gl (gl < BM) or weight row gl - BM (gl < BM + BNW); the
-  // remaining lanes repeat weight row 0 into slots nobody reads.  BM is a
-  // multiple of 64, so each wave reads from one array (a uniform base).
+  // MXFP8 scales travel in groups of four slices: every fourth iteration
+  // lane gl = 64w + lane fetches 16 bytes -- the scale bytes of those four
+  // slices -- of tile row gl (gl < BM) or weight row gl - BM (gl < BM +
+  // BNW); the remaining lanes repeat weight row 0 into slots nobody reads.
+  // BM is a multiple of 64, so each wave reads from one array (a uniform
+  // base).  The buffer ends at the array's end: the bytes a short last
+  // group reads past it come back as 0 and are never used.
   const unsigned char* s_base = nullptr;
-  uint32_t s_off = 0;
+  uint32_t s_off = 0, s_bytes = 0;
   if (MX) {
     static_assert(C::BM % 64 == 0, "");
     const int gl = w * 64 + lane;
@@ -478,35 +493,43 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, const WorkItem& it,
     if (w * 64 < C::BM) {
       s_base = shared ? g.as_shared : g.as_routed;
       s_off = (uint32_t)a_src(gl) * (uint32_t)kb;
+      s_bytes = (uint32_t)(shared ? g.a_rows_s : g.a_rows_r) * (uint32_t)kb;
     } else {
       const int r = gl - C::BM < C::BNW ? gl - C::BM : 0;
       s_base = shared ? g.bs_shared : g.bs_routed + (long long)it.seg * (g.b_stride / kMxBlock);
       s_off = (uint32_t)b_src(r) * (uint32_t)kb;
+      s_bytes = (uint32_t)(GATED ? 2 * Nout : Nout) * (uint32_t)kb;
     }
   }
 
-  // LDS: SA buffers of the A slice (only the live rows; MXFP8: then the
-  // slice's scale bytes), then SB buffers of the B slice.  Items with fewer
-  // rows have smaller A slices and get deeper rings (their short MFMA phase
-  // hides less latency per slice).
-  constexpr int A_SL = C::RG * MS * 32 * C::ROWB + (MX ? C::SCL : 0);  // bytes of one A stage
-  constexpr int SDEEP = (C::LDS_BYTES / (A_SL + C::B_BYTES)) < C::MAXS
-                            ? (C::LDS_BYTES / (A_SL + C::B_BYTES)) : C::MAXS;
+  // LDS: SA buffers of the A slice (only the live rows), then SB buffers of
+  // the B slice, then (MXFP8) two scale-group buffers.  Items with fewer rows
+  // have smaller A slices and get deeper rings (their short MFMA phase hides
+  // less latency per slice).
+  constexpr int A_SL = C::RG * MS * 32 * C::ROWB;  // bytes of one A stage
+  constexpr int SGL = MX ? 2 * C::SGB : 0;         // scale-group buffers
+  constexpr int RING = C::LDS_BYTES - SGL;
+  constexpr int SDEEP = (RING / (A_SL + C::B_BYTES)) < C::MAXS
+                            ? (RING / (A_SL + C::B_BYTES)) : C::MAXS;
   constexpr int SA = SDEEP > C::SA ? SDEEP : C::SA;
   constexpr int SB = SDEEP > C::SB ? SDEEP : C::SB;
-  static_assert(SA * A_SL + SB * C::B_BYTES <= C::LDS_BYTES, "LDS");
+  static_assert(SA * A_SL + SB * C::B_BYTES <= RING, "LDS");
+  static_assert(SA <= 4 && SB == SA, "a window of SA-2 iterations holds at most one group load");
   unsigned char* const Abuf = lds;
   unsigned char* const Bbuf = lds + SA * A_SL;
-  constexpr int SC_OFF = C::RG * MS * 32 * C::ROWB;  // scale bytes inside an A stage
+  unsigned char* const Gbuf = lds + RING;
   const int nk = Kb / C::ROWB;
+  const int ng = (nk + 3) >> 2;  // scale groups
   const rsrc_t ra = make_rsrc(A), rb = make_rsrc(B);
-  const rsrc_t rs = make_rsrc(MX ? s_base : A);
+  const rsrc_t rs = make_rsrc(MX ? s_base : A, MX ? s_bytes : 0xFFFFFFFFu);
+  auto issue_g = [&](int gi) {  // scale group gi (slices 4gi .. 4gi+3)
+    if (MX) dma16(rs, s_off + 16 * gi, 0, Gbuf + (gi & 1) * C::SGB + w * 1024);
+  };
   auto issue_a = [&](int kt) {
     unsigned char* st = Abuf + (kt % SA) * A_SL;
     const uint32_t k0 = kt * C::ROWB;
 #pragma unroll
     for (int j = 0; j < AL; ++j) dma16(ra, a_off[j], k0, st + (w * AL + j) * 1024);
-    if (MX) dma4(rs, s_off, kt * 4, st + SC_OFF + w * 256);
   };
   auto issue_b = [&](int kt) {
     unsigned char* st = Bbuf + (kt % SB) * C::B_BYTES;
@@ -539,14 +562,15 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, const WorkItem& it,
       b_row[j] = (cg * NT + j) * 32 + fr;
   }
 
-  // Issue order: iteration j issues A(j+SA-1), then B(j+SB-1); the prologue
-  // plays iterations -(SB-1) .. -1.  Vector-memory loads retire in order, so
-  // at iteration kt the loads of slice kt are complete once no more than the
-  // younger ones are outstanding: B(kt+1) .. B(kt+SB-2) and A(kt+1) ..
-  // A(kt+SA-2) when B leads by one slice, A/B(kt+1 .. kt+SA-2) otherwise.
-  constexpr int LEAD = SB - SA;
-  constexpr int ALX = AL + (MX ? 1 : 0);  // loads per A issue
-  constexpr int YOUNGER = (SA - 2) * (ALX + C::B_LOADS) + LEAD * C::B_LOADS;
+  // Issue order: iteration j issues (MXFP8, j a multiple of 4: scale group
+  // j/4 + 1,) A(j+SA-1), then B(j+SB-1); the prologue plays iterations
+  // -(SB-1) .. -1 after scale group 0.  Vector-memory loads retire in order,
+  // so at iteration kt the loads of slice kt are complete once no more than
+  // the younger ones are outstanding: A/B(kt+1 .. kt+SA-2), and the scale
+  // group loaded in one of those iterations.  A scale group is loaded three
+  // or more iterations before its first slice, so it is complete by then.
+  constexpr int YOUNGER = (SA - 2) * (AL + C::B_LOADS);
+  issue_g(0);
 #pragma unroll
   for (int j = -(SB - 1); j < 0; ++j) {
     if (j + SA - 1 >= 0 && j + SA - 1 < nk) issue_a(j + SA - 1);
@@ -554,22 +578,39 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, const WorkItem& it,
   }
 
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + SB - 2 < nk) wait_vm<YOUNGER>();
-    else wait_vm<0>();
+    // a scale group among the younger loads: one of iterations kt-SA+2 ..
+    // kt-1 was a multiple of 4 that issued one
+    bool grp = false;
+    if (MX) {
+#pragma unroll
+      for (int i = 1; i <= SA - 2; ++i) {
+        const int it2 = kt - i;
+        grp = grp || (it2 >= 0 && (it2 & 3) == 0 && (it2 >> 2) + 1 < ng);
+      }
+    }
+    if (kt + SB - 2 < nk) {
+      if (grp) wait_vm<YOUNGER + 1>();
+      else wait_vm<YOUNGER>();
+    } else {
+      wait_vm<0>();
+    }
     // every wave's part of slice kt is now in LDS, and every wave is done
     // with slice kt-1, whose buffers the next loads overwrite
     __builtin_amdgcn_s_barrier();
     const unsigned char* As = Abuf + (kt % SA) * A_SL;
     const unsigned char* Bs = Bbuf + (kt % SB) * C::B_BYTES;
-    // MXFP8 scales of this slice: byte b of a row's word is its block b; the
-    // lane of half h takes block 2ks + h into bits 0..7
+    // MXFP8 scales of this slice: word kt % 4 of a row's 16 bytes in its
+    // group buffer; byte b of the word is block b of the slice; the lane of
+    // half h takes block 2ks + h into bits 0..7
     uint32_t sa_w[MS], sb_w[NT];
     if (MX) {
-      const uint32_t* sc = reinterpret_cast<const uint32_t*>(As + SC_OFF);
+      if ((kt & 3) == 0 && (kt >> 2) + 1 < ng) issue_g((kt >> 2) + 1);
+      const uint32_t* sc =
+          reinterpret_cast<const uint32_t*>(Gbuf + ((kt >> 2) & 1) * C::SGB) + (kt & 3);
 #pragma unroll
-      for (int i = 0; i < MS; ++i) sa_w[i] = sc[a_row[i]] >> (8 * fh);
+      for (int i = 0; i < MS; ++i) sa_w[i] = sc[4 * a_row[i]] >> (8 * fh);
 #pragma unroll
-      for (int j = 0; j < NT; ++j) sb_w[j] = sc[C::BM + b_row[j]] >> (8 * fh);
+      for (int j = 0; j < NT; ++j) sb_w[j] = sc[4 * (C::BM + b_row[j])] >> (8 * fh);
     }
     if constexpr (!MX) {
       // fragments of k-step ks+1 are read while the MFMAs of k-step ks run
@@ -889,10 +930,12 @@ inline bytes mx_sc(void* p, size_t elems) { return p ? mb(p) + elems : nullptr; 
 
 template <bool GATED, bool MX>
 void launch_tiles(bool narrow, const GemmArgs& g, int64_t cap, hipStream_t st) {
+  using Wide = typename std::conditional<MX, typename std::conditional<GATED, Cfg1x, Cfg2x>::type,
+                                         typename std::conditional<GATED, Cfg1, Cfg2>::type>::type;
   if (narrow)
     launch_mfma<GATED, MX, typename std::conditional<GATED, Cfg1n, Cfg2n>::type>(g, cap, st);
   else
-    launch_mfma<GATED, MX, typename std::conditional<GATED, Cfg1, Cfg2>::type>(g, cap, st);
+    launch_mfma<GATED, MX, Wide>(g, cap, st);
 }
 
 struct PlanGeom {
@@ -903,10 +946,11 @@ struct PlanGeom {
 PlanGeom plan_geom(const moe_shape& s) {
   const bool bf = s.dtype != MOE_DTYPE_F32;  // bf16 or MXFP8 MFMA tiles
   const bool nar = narrow_tiles(s);
-  const int bm1 = bf ? (nar ? Cfg1n::BM : Cfg1::BM) : kBMf;
-  const int bm2 = bf ? (nar ? Cfg2n::BM : Cfg2::BM) : kBMf;
-  const int bn1 = bf ? (nar ? Cfg1n::BNW : Cfg1::BNW) / 2 : kBNf;
-  const int bn2 = bf ? (nar ? Cfg2n::BNW : Cfg2::BNW) : kBNf;
+  const bool mx = s.dtype == MOE_DTYPE_MXFP8;
+  const int bm1 = bf ? (nar ? Cfg1n::BM : mx ? Cfg1x::BM : Cfg1::BM) : kBMf;
+  const int bm2 = bf ? (nar ? Cfg2n::BM : mx ? Cfg2x::BM : Cfg2::BM) : kBMf;
+  const int bn1 = bf ? (nar ? Cfg1n::BNW : mx ? Cfg1x::BNW : Cfg1::BNW) / 2 : kBNf;
+  const int bn2 = bf ? (nar ? Cfg2n::BNW : mx ? Cfg2x::BNW : Cfg2::BNW) : kBNf;
   const bool sh = s.d_ff_shared > 0;
   return PlanGeom{bm1, bm2, cdiv(s.d_ff, bn1), sh ? cdiv(s.d_ff_shared, bn1) : 0,
                   cdiv(s.d_model, bn2), sh ? cdiv(s.d_model, bn2) : 0};
@@ -945,7 +989,8 @@ hipError_t launch_gemm1(const moe_shape& s, const void* x, const int32_t* perm, 
     GemmArgs g1{w.xq, w.xq, perm, s.top_k, cb(w1), cb(w1s), mb(h), mb(hs),
                 xs, xs, mx_sc(w1, (size_t)N * 2 * f * d), mx_sc(w1s, (size_t)2 * fs * d),
                 mx_sc(h, A * f), mx_sc(hs, T * fs),
-                d, d, f, fs, (long long)2 * f * d, N, w.plan1, w.plan1_hdr};
+                d, d, f, fs, (long long)2 * f * d, N, w.plan1, w.plan1_hdr, nullptr,
+                (int)T, (int)T};
     launch_tiles<true, true>(narrow_tiles(s), g1, w.plan1_cap, st);
   } else {
     GemmArgsF g1{static_cast<const float*>(x), static_cast<const float*>(x), perm, s.top_k,
@@ -969,7 +1014,8 @@ hipError_t launch_gemm2(const moe_shape& s, const void* h, const void* hs, const
                 mx ? mx_sc(h, A * f) : nullptr, mx ? mx_sc(hs, T * fs) : nullptr,
                 mx ? mx_sc(w2, (size_t)N * d * f) : nullptr,
                 mx ? mx_sc(w2s, (size_t)d * fs) : nullptr, nullptr, nullptr,
-                f, fs, d, d, (long long)d * f, N, w.plan2, w.plan2_hdr};
+                f, fs, d, d, (long long)d * f, N, w.plan2, w.plan2_hdr, nullptr,
+                (int)A, (int)T};
     if (mx)
       launch_tiles<false, true>(narrow_tiles(s), g2, w.plan2_cap, st);
     else
