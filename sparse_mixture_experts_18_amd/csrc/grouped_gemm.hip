@@ -350,7 +350,7 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 // Direct global -> LDS loads through a buffer resource: the base address
 // sits in scalar registers, each lane supplies a 32-bit offset and the
 // k-slice offset is the scalar soffset, so a load costs one VGPR.  Lane i
-// of a wave writes its 16 (or 4) bytes to lds_wave_base + 16 i (4 i).
+// of a wave writes its 16 bytes to lds_wave_base + 16 i.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ rsrc_t make_rsrc(const unsigned char* base,
                                             uint32_t bytes = 0xFFFFFFFFu) {
@@ -362,10 +362,6 @@ __device__ __forceinline__ rsrc_t make_rsrc(const unsigned char* base,
 __device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff,
                                       unsigned char* lds_wave_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lptr_t)(lds_wave_base), 16, voff, soff, 0, 0);
-}
-__device__ __forceinline__ void dma4(rsrc_t r, uint32_t voff, uint32_t soff,
-                                     unsigned char* lds_wave_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lptr_t)(lds_wave_base), 4, voff, soff, 0, 0);
 }
 
 // wait until at most n vector-memory ops of this wave are outstanding
