@@ -52,6 +52,9 @@ def parse():
                    help="tokens of the batch the oracle runs on (about 10 s on the host)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--stage-iters", type=int, default=10)
+    p.add_argument("--skip", default="",
+                   help="comma list of extra sections to leave out: ec, mx, latent, telemetry "
+                        "(profiler runs use it to keep one kernel's dispatches apart)")
     return p.parse_args()
 
 
@@ -139,6 +142,10 @@ def cpu_baseline(cfg, inp, n_tokens: int) -> dict:
 
 def main():
     args = parse()
+    skip = {t.strip() for t in args.skip.split(",") if t.strip()}
+    bad = skip - {"ec", "mx", "latent", "telemetry"}
+    if bad:
+        raise SystemExit(f"--skip: unknown sections {sorted(bad)}")
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this build measures one GPU: the layer forward runs "
@@ -289,20 +296,22 @@ def main():
 
     # router telemetry over this forward's outputs (HBM-bound: it reads the
     # kept expert rows, the shared rows, the scores and the gates once)
-    stats = torch.empty(moe.moe_router_stats_count(shape), dtype=torch.float64, device=dev)
-    tl_ms = timed(lambda: moe.moe_router_stats(shape, cn, of, tw, sc, inp.bias, yp, ysh, stats,
-                                               ws), args.stage_iters)
-    tl_bytes = esz * (n_kept + (T if cfg.d_ff_shared else 0)) * d + 4 * T * (N + k) + 8 * N
-    tl_gbs = tl_bytes / (tl_ms * 1e-3) / 1e9
-    telemetry = {"kernels": "row_stats, expert_stats, entropy, stats_final (moe_router_stats)",
-                 "avg_ms": round(tl_ms, 4), "algorithmic_bytes": tl_bytes,
-                 "GB/s": round(tl_gbs, 1), "hbm_frac": round(tl_gbs / PEAK_HBM_GBS, 4)}
+    telemetry = None
+    if "telemetry" not in skip:
+        stats = torch.empty(moe.moe_router_stats_count(shape), dtype=torch.float64, device=dev)
+        tl_ms = timed(lambda: moe.moe_router_stats(shape, cn, of, tw, sc, inp.bias, yp, ysh,
+                                                   stats, ws), args.stage_iters)
+        tl_bytes = esz * (n_kept + (T if cfg.d_ff_shared else 0)) * d + 4 * T * (N + k) + 8 * N
+        tl_gbs = tl_bytes / (tl_ms * 1e-3) / 1e9
+        telemetry = {"kernels": "row_stats, expert_stats, entropy, stats_final (moe_router_stats)",
+                     "avg_ms": round(tl_ms, 4), "algorithmic_bytes": tl_bytes,
+                     "GB/s": round(tl_gbs, 1), "hbm_frac": round(tl_gbs / PEAK_HBM_GBS, 4)}
 
     # expert-choice routing on the same layer: every expert takes its
     # C = k*T/N tokens (the same number of expert rows as token choice)
     ec_shape = shape.replace(capacity_factor=1.0, capacity_rule=moe.MOE_CAP_ASSIGNMENTS)
     expert_choice = None
-    if moe.moe_ec_capacity(ec_shape) * N <= T * k:
+    if "ec" not in skip and moe.moe_ec_capacity(ec_shape) * N <= T * k:
         y_ec = torch.empty_like(out["y"])
         ws_ec = moe.workspace(ec_shape, dev)
 
@@ -325,7 +334,7 @@ def main():
     # quantised once by moe_quantize_mx, then the same forward and the two
     # expert projections timed as above
     mxfp8 = None
-    if cfg.dtype == "bf16" and d % 128 == 0 and cfg.d_ff % 128 == 0 and \
+    if "mx" not in skip and cfg.dtype == "bf16" and d % 128 == 0 and cfg.d_ff % 128 == 0 and \
             cfg.d_ff_shared % 128 == 0:
         mx_shape = shape.replace(dtype=moe.MOE_DTYPE_MXFP8)
         ws_mx = moe.workspace(mx_shape, dev)
@@ -384,7 +393,8 @@ def main():
     # experts (d_ff unchanged) on z = x W_down^T, y = y_lat W_up^T + shared
     latent = None
     l = d // 4
-    if cfg.dtype in ("bf16", "f32") and l % (64 if cfg.dtype == "bf16" else 32) == 0:
+    if "latent" not in skip and cfg.dtype in ("bf16", "f32") and \
+            l % (64 if cfg.dtype == "bf16" else 32) == 0:
         li = W.make_latent_inputs(cfg, l, seed=0, device=dev)
         ws_l = moe.latent_workspace(shape, l, dev)
         y_l = torch.empty_like(out["y"])
