@@ -48,7 +48,7 @@ def parse():
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", default="dsv3")
-    p.add_argument("--cpu-sample-tokens", type=int, default=48,
+    p.add_argument("--cpu-sample-tokens", type=int, default=64,
                    help="tokens of the batch the oracle runs on (about 10 s on the host)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--stage-iters", type=int, default=10)
