@@ -10,15 +10,18 @@
 // GEMM1: h[s, c] = silu(x_t . Wg_e[c]) * (x_t . Wu_e[c])   t = perm[s] / k
 // GEMM2: y_perm[s, n] = h[s] . W2_e[n]
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16, fp32 accumulation, work items of up
-// to 256 rows x 256 weight rows (64 x 128 for layers with few rows per
-// expert), both operands K-contiguous (weights in nn.Linear [out, in]
-// layout), staged through LDS by direct DMA with an XOR swizzle of the
-// 16-byte chunks.  The work list (segment, row block, column tile) is built
-// on the device from the dispatch offsets, so no host synchronisation is
-// needed.  Persistent blocks, one per CU: each XCD walks its own contiguous,
-// cost-balanced run of the list (same expert, same weight slab), which keeps
-// that slab in the XCD's L2 across the row blocks.
+// MFMA path (bf16: v_mfma_f32_32x32x16_bf16; MXFP8: the block-scaled
+// v_mfma_scale_f32_32x32x64_f8f6f4), fp32 accumulation, work items of up to
+// 256 rows x 256 weight rows (64 x 128 for layers with few rows per expert),
+// both operands K-contiguous (weights in nn.Linear [out, in] layout), staged
+// through LDS by direct buffer DMA with an XOR swizzle of the 16-byte chunks.
+// The work list (segment, row block, column tile) is built on the device
+// from the dispatch offsets, so no host synchronisation is needed.
+// Persistent blocks, one per CU: each XCD walks its own contiguous,
+// cost-balanced run of the list (same expert, same weight slab), so sibling
+// row blocks that share a slab run close together on one L2.  The same
+// kernels run the dense products of the LatentMoE layer over a one-segment
+// list.  An fp32 VALU path serves fp32 layers.
 #include <type_traits>
 
 #include "moe_internal.h"
