@@ -687,7 +687,8 @@ def moe_layer_ec(x: np.ndarray, w_router: np.ndarray, w1, w2, *, C: int, k: int,
                  w1_shared: Optional[np.ndarray] = None,
                  w2_shared: Optional[np.ndarray] = None,
                  scores_fp32: Optional[np.ndarray] = None,
-                 compute_outputs: bool = True) -> Dict[str, np.ndarray]:
+                 compute_outputs: bool = True,
+                 ffn: Callable = swiglu_ffn) -> Dict[str, np.ndarray]:
     """One expert-choice MoE layer forward ([EC]): scores as in token choice,
     each expert takes its top-C tokens, y_t = sum over the experts that took
     t of s[t, e] * E_e(x_t) (the raw score is the gate), plus the shared
@@ -715,10 +716,10 @@ def moe_layer_ec(x: np.ndarray, w_router: np.ndarray, w1, w2, *, C: int, k: int,
         if t.size == 0:
             continue
         w1e, w2e = _expert_weights(w1, w2, e)
-        o = swiglu_ffn(x[t], w1e, w2e)
+        o = ffn(x[t], w1e, w2e)
         y[t] += s32[t, e].astype(np.float64)[:, None] * o
     if w1_shared is not None:
-        y += swiglu_ffn(x, w1_shared, w2_shared)
+        y += ffn(x, w1_shared, w2_shared)
     out["y"] = y
     return out
 

@@ -108,3 +108,42 @@ def test_ec_rejects_overfull_capacity():
     with pytest.raises(moe.MoeError) as e:
         run_ec(inp, ec_shape(cfg, cfg.T, cf=0.0))  # no capacity
     assert e.value.status == moe.MOE_ERR_INVALID
+
+
+EC_MX = {
+    "ec_mx_small": W.LayerConfig("ec_mx_small", T=512, d_model=512, n_experts=16, top_k=4,
+                                 d_ff=256, d_ff_shared=256, score_fn="sigmoid",
+                                 dtype="mxfp8"),
+    "decode": W.CONFIGS["decode"].replace(dtype="mxfp8"),
+}
+
+
+@pytest.mark.parametrize("name,T,cf,rule", [("ec_mx_small", None, 1.0, None),
+                                            ("decode", None, 8.0, moe.MOE_CAP_TOKENS)])
+def test_ec_forward_mxfp8_matches_oracle(name, T, cf, rule):
+    """Expert choice with MXFP8 experts: the same selection, experts through
+    the MXFP8 path (weights quantised by moe_quantize_mx on the GPU, by
+    mx_quantize in the oracle)."""
+    cfg = EC_MX[name]
+    T = T or cfg.T
+    say(f"[ec mx] {name} T={T}")
+    inp = W.make_inputs(cfg, seed=32, device="cuda", T=T)
+    shape = ec_shape(cfg, T, cf, rule)
+    q = [moe.quantize_mx(t) if t is not None else None
+         for t in (inp.w1, inp.w2, inp.w1_shared, inp.w2_shared)]
+    y = torch.empty((T, shape.d_model), dtype=torch.bfloat16, device="cuda")
+    sc = torch.empty((T, shape.n_experts), dtype=torch.float32, device="cuda")
+    ws = moe.workspace(shape)
+    moe.moe_forward_ec(shape, inp.x, inp.w_router, inp.logit_add, q[0], q[1], q[2], q[3], y,
+                       sc, None, None, ws)
+    torch.cuda.synchronize()
+    mr = lambda t: oracle.mx_round(host(t).astype(np.float64))
+    ref = oracle.moe_layer_ec(
+        host(inp.x), host(inp.w_router), lambda e: (mr(inp.w1[e]), mr(inp.w2[e])), None,
+        C=moe.moe_ec_capacity(shape), k=shape.top_k,
+        w1_shared=None if inp.w1_shared is None else mr(inp.w1_shared),
+        w2_shared=None if inp.w2_shared is None else mr(inp.w2_shared),
+        scores_fp32=host(sc), ffn=oracle.swiglu_ffn_mx)
+    err = rel_l2(host(y), ref["y"])
+    say(f"  [ec mx] {name} rel L2 {err:.3e}")
+    assert err <= 2e-2
