@@ -688,12 +688,15 @@ def moe_layer_ec(x: np.ndarray, w_router: np.ndarray, w1, w2, *, C: int, k: int,
                  w2_shared: Optional[np.ndarray] = None,
                  scores_fp32: Optional[np.ndarray] = None,
                  compute_outputs: bool = True,
-                 ffn: Callable = swiglu_ffn) -> Dict[str, np.ndarray]:
+                 ffn: Callable = swiglu_ffn,
+                 tokens: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
     """One expert-choice MoE layer forward ([EC]): scores as in token choice,
     each expert takes its top-C tokens, y_t = sum over the experts that took
     t of s[t, e] * E_e(x_t) (the raw score is the gate), plus the shared
     expert; a token no expert took gets only the shared term.  The sum over
-    experts runs in ascending e."""
+    experts runs in ascending e.  ``tokens`` restricts the expert stage to
+    those rows (the selection always covers all T tokens); out["y"] then
+    holds those rows in the given order."""
     x = np.asarray(x)
     T = x.shape[0]
     N = w_router.shape[0]
@@ -711,16 +714,18 @@ def moe_layer_ec(x: np.ndarray, w_router: np.ndarray, w1, w2, *, C: int, k: int,
         return out
     d = x.shape[1]
     y = np.zeros((T, d), np.float64)
+    sel = np.ones(T, bool) if tokens is None else np.isin(np.arange(T), tokens)
     for e in range(N):
-        t = np.nonzero(chosen[:, e])[0]
+        t = np.nonzero(chosen[:, e] & sel)[0]
         if t.size == 0:
             continue
         w1e, w2e = _expert_weights(w1, w2, e)
         o = ffn(x[t], w1e, w2e)
         y[t] += s32[t, e].astype(np.float64)[:, None] * o
+    rows = np.arange(T) if tokens is None else np.asarray(tokens, np.int64)
     if w1_shared is not None:
-        y += ffn(x, w1_shared, w2_shared)
-    out["y"] = y
+        y[rows] += ffn(x[rows], w1_shared, w2_shared)
+    out["y"] = y[rows]
     return out
 
 

@@ -147,3 +147,29 @@ def test_ec_forward_mxfp8_matches_oracle(name, T, cf, rule):
     err = rel_l2(host(y), ref["y"])
     say(f"  [ec mx] {name} rel L2 {err:.3e}")
     assert err <= 2e-2
+
+
+def test_ec_forward_full_size_dsv3_sampled():
+    """The dsv3 layer at full size (T = 8192, C = k*T/N = 256 per expert):
+    selection bit-exact over all tokens, outputs on sampled tokens."""
+    cfg = W.CONFIGS["dsv3"]
+    T = cfg.T
+    say(f"[ec] dsv3 full T={T}")
+    inp = W.make_inputs(cfg, seed=33, device="cuda")
+    shape = ec_shape(cfg, T)
+    o = run_ec(inp, shape)
+    check_selection(o, shape)
+    y = torch.empty((T, shape.d_model), dtype=torch.bfloat16, device="cuda")
+    sc = torch.empty((T, shape.n_experts), dtype=torch.float32, device="cuda")
+    ws = moe.workspace(shape)
+    moe.moe_forward_ec(shape, inp.x, inp.w_router, inp.logit_add, inp.w1, inp.w2,
+                       inp.w1_shared, inp.w2_shared, y, sc, None, None, ws)
+    torch.cuda.synchronize()
+    tokens = [0, 4321, T - 1]
+    ref = oracle.moe_layer_ec(
+        host(inp.x), host(inp.w_router), weight_source(inp), None,
+        C=moe.moe_ec_capacity(shape), k=shape.top_k, w1_shared=host(inp.w1_shared),
+        w2_shared=host(inp.w2_shared), scores_fp32=host(sc), tokens=tokens)
+    err = rel_l2(host(y)[tokens], ref["y"])
+    say(f"  rel L2 {err:.3e} over {len(tokens)} tokens")
+    assert err <= tol_for(cfg)
