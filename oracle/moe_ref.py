@@ -656,7 +656,8 @@ def expert_choice_select(s32: np.ndarray, C: int) -> np.ndarray:
     key = np.asarray(s32, f32).copy()
     key[key == 0] = f32(0.0)
     T = key.shape[0]
-    r = _ranks(np.ascontiguousarray(key.T))          # [N, T]: rank of t in column e
+    # [N, T]: rank of t in column e (a few experts per pass: T x T pairs each)
+    r = _ranks(np.ascontiguousarray(key.T), chunk=max(1, (1 << 24) // max(T * T, 1)))
     return (r < min(int(C), T)).T
 
 
