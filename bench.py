@@ -23,6 +23,8 @@ Extra fields beside the contract's:
                 against the fp8 MFMA and HBM peaks
   expert_choice the same layer routed by expert choice at C = k*T/N
   latent        the LatentMoE variant of the layer at latent width d/4
+  ep8_share     the expert FFNs at one GPU's share under 8-way expert
+                parallelism (N/8 experts, k*T rows spread evenly over them)
 """
 from __future__ import annotations
 
@@ -53,7 +55,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--stage-iters", type=int, default=10)
     p.add_argument("--skip", default="",
-                   help="comma list of extra sections to leave out: ec, mx, latent, telemetry "
+                   help="comma list of extra sections to leave out: ec, mx, latent, telemetry, ep "
                         "(profiler runs use it to keep one kernel's dispatches apart)")
     return p.parse_args()
 
@@ -143,7 +145,7 @@ def cpu_baseline(cfg, inp, n_tokens: int) -> dict:
 def main():
     args = parse()
     skip = {t.strip() for t in args.skip.split(",") if t.strip()}
-    bad = skip - {"ec", "mx", "latent", "telemetry"}
+    bad = skip - {"ec", "mx", "latent", "telemetry", "ep"}
     if bad:
         raise SystemExit(f"--skip: unknown sections {sorted(bad)}")
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -389,6 +391,39 @@ def main():
         }
         del w1q, w2q, w1sq, w2sq, ws_mx, hq, hsq
 
+    # One GPU's share of the layer under 8-way expert parallelism: 32 of the
+    # experts, each receiving the rows that 8 GPUs' batches (8 x T tokens,
+    # top-k, balanced) send it -- k*T*8/N rows -- plus the shared expert on
+    # the local T tokens.  The received rows are the local x rows (synthetic,
+    # balanced routing: token t -> experts (t + (N/8/k) j) mod N/8), so the
+    # expert kernels run at the per-GPU shape without any exchange.
+    ep_share = None
+    if "ep" not in skip and cfg.n_experts % 8 == 0 and cfg.n_experts // 8 >= k and \
+            (cfg.n_experts // 8) % k == 0 and cfg.dtype == "bf16":
+        n_loc = cfg.n_experts // 8
+        ep_shape = shape.replace(n_experts=n_loc, n_groups=1, topk_groups=1)
+        ws_ep = moe.workspace(ep_shape, dev)
+        stride = n_loc // k
+        tt = torch.arange(T, device=dev, dtype=torch.int32)[:, None]
+        jj = torch.arange(k, device=dev, dtype=torch.int32)[None, :]
+        ti_ep = ((tt + stride * jj) % n_loc).to(torch.int32).contiguous()
+        cn_ep = torch.empty((n_loc,), dtype=torch.int32, device=dev)
+        of_ep = torch.empty((n_loc + 1,), dtype=torch.int32, device=dev)
+        moe.moe_dispatch(ep_shape, ti_ep, cn_ep, of_ep, sl, pm, nkd, ws_ep)
+        w1_ep, w2_ep = inp.w1[:n_loc], inp.w2[:n_loc]
+        moe.moe_expert_plan(ep_shape, of_ep, ws_ep)
+        ep_ms = timed(lambda: moe.moe_expert_ffn(ep_shape, inp.x, pm, None, w1_ep, w2_ep,
+                                                 inp.w1_shared, inp.w2_shared, yp, ysh, ws_ep),
+                      args.stage_iters)
+        ep_flops = 6.0 * d * cfg.d_ff * T * k + 6.0 * T * d * cfg.d_ff_shared
+        ep_share = {"experts": n_loc, "rows_per_expert": T * k // n_loc,
+                    "expert_ffn_ms": round(ep_ms, 4),
+                    "TFLOP/s": round(ep_flops / (ep_ms * 1e-3) / 1e12, 2),
+                    "mfma_frac": round(ep_flops / (ep_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                    "note": "both expert projections (+ shared expert) in one moe_expert_ffn "
+                            "call; no all-to-all"}
+        del ws_ep
+
     # LatentMoE on the same workload at latent width d/4: routing on x, the
     # experts (d_ff unchanged) on z = x W_down^T, y = y_lat W_up^T + shared
     latent = None
@@ -457,6 +492,7 @@ def main():
         "expert_choice": expert_choice,
         "mxfp8": mxfp8,
         "latent": latent,
+        "ep8_share": ep_share,
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
