@@ -18,8 +18,9 @@
 // The work list (segment, row block, column tile) is built on the device
 // from the dispatch offsets, so no host synchronisation is needed.
 // Persistent blocks, one per CU: each XCD walks its own contiguous,
-// cost-balanced run of the list (same expert, same weight slab), so sibling
-// row blocks that share a slab run close together on one L2.  The same
+// cost-balanced run of the list (whole experts, dealt to the XCDs by cost),
+// so sibling row blocks that share a weight slab run close together on one
+// L2.  The same
 // kernels run the dense products of the LatentMoE layer over a one-segment
 // list.  An fp32 VALU path serves fp32 layers.
 #include <type_traits>
@@ -87,6 +88,10 @@ __device__ __forceinline__ void block_exclusive_scan2(int* sh0, int* sh1, int v0
 #define MOE_COST_FIXED 2
 #endif
 
+#ifndef MOE_PLAN_DEAL
+#define MOE_PLAN_DEAL 1
+#endif
+
 // Work-list header (int32): [0] item count, [1..9] XCD range starts
 // (xcd x owns items [hdr[1+x], hdr[2+x])), [16..23] per-XCD item counters.
 constexpr int kHdrStart = 1, kHdrCtr = 16, kHdrDone = 24;  // header: 32 ints
@@ -98,9 +103,13 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
                                                     WorkItem* __restrict__ plan1,
                                                     int32_t* __restrict__ hdr1,
                                                     WorkItem* __restrict__ plan2,
-                                                    int32_t* __restrict__ hdr2) {
+                                                    int32_t* __restrict__ hdr2, int deal) {
   __shared__ int sh0[64], sh1[64];
   __shared__ int st1s[1025], st2s[1025], mt1s[1024], mt2s[1024], rbases[1024], rowss[1024];
+#if MOE_PLAN_DEAL
+  __shared__ long long ucost[1024];
+  __shared__ int uslot[1024];
+#endif
   const int s = threadIdx.x;
   const int S = N + has_shared;
   int rows = 0, rbase = 0, n1t = 0, n2t = 0;
@@ -128,10 +137,6 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     st2s[1024] = tot2;
   }
   __syncthreads();
-  // Items in segment-major, then column tile, then row block order.  Block p
-  // builds work list p.  Thread s fills a contiguous chunk of the list; an
-  // item's cost is its 32-row sub-tiles (plus a fixed part) times its k-slices.
-  // The list is then cut into 8 ranges of equal cost, one per XCD.
   {
     const int pass = blockIdx.x;
     const int* st = pass ? st2s : st1s;
@@ -140,6 +145,89 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     WorkItem* plan = pass ? plan2 : plan1;
     int32_t* hdr = pass ? hdr2 : hdr1;
     const int tot = pass ? tot2 : tot1;
+#if MOE_PLAN_DEAL
+    // Lists of routed experts on the wide tiles.  Units: each routed expert
+    // (all its column tiles) and each column tile of the shared expert.  A
+    // unit's cost is the sum of its items' costs (32-row sub-tiles plus a
+    // fixed part, times k-slices).  Units are ranked by cost (descending,
+    // ties by index) and dealt to the 8 XCDs in snake order (ranks 0..7 to
+    // XCDs 0..7, ranks 8..15 to XCDs 7..0, ...): every XCD gets the same
+    // total and a similar mix, and a unit never straddles two XCDs, so a
+    // list of about one item per CU leaves no CU with two.  Each XCD's range
+    // takes its units alternately from the large and the small end of its
+    // share (largest, smallest, second largest, ...), so compute-bound and
+    // weight-bound items run side by side; inside a unit, column tile then
+    // row block, so sibling row blocks of one weight slab are drawn in a
+    // row.  The small-row tiles stream the weights at a cost that hardly
+    // depends on the rows, so their lists keep the plain order and an
+    // equal-cost cut at item granularity.
+    const int nrt = pass ? nt2_r : nt1_r, nst = pass ? nt2_s : nt1_s;
+    const int U = N + (has_shared ? nst : 0);
+    if (deal && N > 0 && U <= 1016) {
+      long long c = -1;  // threads without a unit rank after every unit
+      int useg = 0, t0 = 0, t1 = 0;
+      if (s < U) {
+        useg = s < N ? s : N;
+        t0 = s < N ? 0 : s - N;
+        t1 = s < N ? nrt : t0 + 1;
+        const int R = rowss[useg], mt = mts[useg];
+        c = 0;
+        if (mt > 0) {
+          // row blocks as in the walk below: mt - 1 blocks of `part` rows
+          const int part = ((R + mt - 1) / mt + 31) / 32 * 32;
+          const long long sub = (long long)(mt - 1) * (part / 32) + (R - (mt - 1) * part + 31) / 32;
+          c = (long long)(t1 - t0) * (sub + (long long)MOE_COST_FIXED * mt) * (useg < N ? kr : ks);
+        }
+      }
+      ucost[s] = c;
+      uslot[s] = -1;
+      __syncthreads();
+      const int R8 = (U + 7) >> 3;
+      if (s < U) {
+        int rank = 0;
+        for (int v = 0; v < U; ++v) {
+          const long long cv = ucost[v];
+          rank += (cv > c) || (cv == c && v < s);
+        }
+        const int rd = rank >> 3, p = rank & 7;
+        const int x = (rd & 1) ? 7 - p : p;
+        // position of round rd in the XCD's order 0, R8-1, 1, R8-2, ...
+        const int j = rd <= (R8 - 1) / 2 ? 2 * rd : 2 * (R8 - 1 - rd) + 1;
+        uslot[x * R8 + j] = s;
+      }
+      __syncthreads();
+      // thread q lays out slot q: XCD q / R8, position q % R8
+      const int u = uslot[s];
+      int useg2 = 0, u0 = 0, u1 = 0, mt = 0;
+      if (u >= 0) {
+        useg2 = u < N ? u : N;
+        u0 = u < N ? 0 : u - N;
+        u1 = u < N ? nrt : u0 + 1;
+        mt = mts[useg2];
+      }
+      int base, dummy_ex, total, dummy_tot;
+      block_exclusive_scan2(sh0, sh1, mt * (u1 - u0), 0, base, dummy_ex, total, dummy_tot);
+      if (s == 0) {
+        hdr[0] = total;
+        hdr[kHdrStart + 8] = total;
+        for (int x = 0; x < 8; ++x) hdr[kHdrCtr + x] = 0;
+        hdr[kHdrDone] = 0;
+      }
+      if (s < 8 * R8 && s % R8 == 0) hdr[kHdrStart + s / R8] = base;
+      if (u >= 0 && mt > 0) {
+        const int R = rowss[useg2];
+        const int part = ((R + mt - 1) / mt + 31) / 32 * 32;
+        int i = base;
+        for (int nt = u0; nt < u1; ++nt)
+          for (int m = 0; m < mt; ++m)
+            plan[i++] = WorkItem{useg2, rbases[useg2] + m * part, min(part, R - m * part), nt};
+      }
+      return;
+    }
+#endif
+    // Otherwise (one-segment dense lists): items in segment-major, then column
+    // tile, then row block order.  Thread s fills a contiguous chunk of the
+    // list; the list is then cut into 8 ranges of equal cost, one per XCD.
     const int chunk = (tot + 1023) / 1024;
     const int i0 = min(tot, s * chunk), i1 = min(tot, i0 + chunk);
     // segment of item i0: the last segment with st[seg] <= i0 (empty ones skipped)
@@ -253,8 +341,9 @@ struct GemmArgs {
 // ---------------------------------------------------------------------------
 // MFMA grouped GEMM (bf16, or MXFP8 with per-32 block scales).
 //
-// Block tile: up to BM rows (assignments) x BNW weight rows, k-slices of 128
-// bytes per row (64 bf16 or 128 MXFP8 values).  RG x CG waves: wave (rg, cg)
+// Block tile: up to BM rows (assignments) x BNW weight rows, k-slices of BK
+// bf16 per row (64-byte or 128-byte rows) or 128 MXFP8 values (128-byte
+// rows).  RG x CG waves: wave (rg, cg)
 // owns the weight rows of column group cg (GATED: gate rows 32cg..32cg+31 and
 // the matching up rows, i.e. 32 h columns, so SwiGLU is applied in
 // registers; plain: 64 output columns) and the 32-row MFMA sub-tiles i with
@@ -275,9 +364,9 @@ struct GemmArgs {
 // MXFP8: v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, fp32 accumulation),
 // two 64-deep k-steps per slice.  Lane (r, h) of a fragment holds row r and
 // k 16h..16h+15 and 32+16h..32+16h+15 of the step, and gives the scale of
-// row r for the step's 32-value block h.  The scale bytes of a slice (four
-// per row) travel with the A slice: one 4-byte DMA per lane per wave, rows
-// of A first, then the weight rows.
+// row r for the step's 32-value block h.  The scale bytes travel in groups
+// of four slices (16 bytes per row): one 16-byte DMA per lane every fourth
+// slice, rows of A first, then the weight rows.
 // ---------------------------------------------------------------------------
 template <int RG_, int CG_, int NTW_, int BK_, int SA_, int SB_, int MSW_ = 4, int LDS_KIB_ = 160,
           int MAXS_ = 4>
@@ -303,7 +392,11 @@ struct GCfg {
   static_assert(A_LOADS * 1024 * WAVES == A_BYTES && B_LOADS * 1024 * WAVES == B_BYTES, "");
   static_assert(SA * A_BYTES + SB * B_BYTES <= LDS_BYTES, "LDS");
   static_assert(SB >= SA && SA >= 2 && SB <= SA + 1, "B runs at most one slice ahead of A");
-  static_assert(ROWB == 128, "k-slices are 128 bytes per row");
+  static_assert(ROWB == 128 || ROWB == 64, "k-slices are 64 or 128 bytes per row");
+  // row sub-tiles per wave come in multiples of MSQ, so that an A stage is a
+  // whole number of 1 KiB DMA blocks per wave
+  static constexpr int MSQ = (RG * 32 * ROWB >= 1024 * WAVES) ? 1 : 1024 * WAVES / (RG * 32 * ROWB);
+  static_assert((RG * 32 * ROWB * MSQ) % (1024 * WAVES) == 0 && MSW % MSQ == 0, "A stage DMA");
   __device__ static __forceinline__ int swz(int r) { return (r / RP) % CPR; }
 };
 
@@ -338,6 +431,14 @@ using Cfg2x = GCfg<MOE_GEMM2_MX_CFG>;
 #endif
 using Cfg1n = GCfg<MOE_GEMM1_SMALL_CFG>;
 using Cfg2n = GCfg<MOE_GEMM2_SMALL_CFG>;
+#ifndef MOE_GEMM1_SMALL_MX_CFG
+#define MOE_GEMM1_SMALL_MX_CFG 2, 2, 2, 64, 2, 2, 1, 160, 4
+#endif
+#ifndef MOE_GEMM2_SMALL_MX_CFG
+#define MOE_GEMM2_SMALL_MX_CFG 2, 2, 2, 64, 2, 2, 1, 160, 4
+#endif
+using Cfg1nx = GCfg<MOE_GEMM1_SMALL_MX_CFG>;
+using Cfg2nx = GCfg<MOE_GEMM2_SMALL_MX_CFG>;
 
 // mean rows per expert at or below which the small-row tiles are used
 #ifndef MOE_SMALL_ROWS
@@ -383,7 +484,6 @@ struct Frag;
 template <>
 struct Frag<false> {
   typedef bf16x8_t T;
-  static constexpr int STEPS = 4;
   __device__ static __forceinline__ T read(const unsigned char* row, int ks, int fh, int sw) {
     return *reinterpret_cast<const bf16x8_t*>(row + (((2 * ks + fh) ^ sw) << 4));
   }
@@ -391,7 +491,6 @@ struct Frag<false> {
 template <>
 struct Frag<true> {
   typedef i32x8_t T;
-  static constexpr int STEPS = 2;
   __device__ static __forceinline__ T read(const unsigned char* row, int ks, int fh, int sw) {
     const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(row + (((4 * ks + fh) ^ sw) << 4));
     const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(row + (((4 * ks + 2 + fh) ^ sw) << 4));
@@ -430,8 +529,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, const WorkItem& it,
                                           unsigned char* lds, int msub) {
   typedef typename Frag<MX>::T FT;
   static_assert(!MX || C::BM + C::BNW <= C::WAVES * 64, "one scale DMA per wave covers every row");
+  static_assert(!MX || C::ROWB == 128, "MXFP8 slices are two 64-deep k-steps");
   constexpr int ES = MX ? 1 : 2;         // bytes per element
-  constexpr int KSTEPS = Frag<MX>::STEPS;
+  constexpr int KSTEPS = MX ? 2 : C::ROWB / 32;  // k-steps per slice: 64-deep / 16-deep
   const bool shared = it.seg == g.N;
   const int K = shared ? g.K_s : g.K_r;
   const int Kb = K * ES;                 // bytes per operand row
@@ -513,7 +613,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, const WorkItem& it,
   constexpr int SA = SDEEP > C::SA ? SDEEP : C::SA;
   constexpr int SB = SDEEP > C::SB ? SDEEP : C::SB;
   static_assert(SA * A_SL + SB * C::B_BYTES <= RING, "LDS");
-  static_assert(SA <= 4 && SB == SA, "a window of SA-2 iterations holds at most one group load");
+  static_assert(SB == SA && (!MX || SA <= 4),
+                "MXFP8: a window of SA-2 iterations holds at most one group load");
   unsigned char* const Abuf = lds;
   unsigned char* const Bbuf = lds + SA * A_SL;
   unsigned char* const Gbuf = lds + RING;
@@ -774,8 +875,11 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& g, int item, unsigned 
                     __builtin_amdgcn_readfirstlane(ld.nrows), __builtin_amdgcn_readfirstlane(ld.nt)};
   const int msub = (it.nrows + 31) >> 5;  // live 32-row sub-tiles
   const int ms = (msub + C::RG - 1) / C::RG;  // sub-tiles of the busiest wave
-  constexpr int M2 = C::MSW < 2 ? C::MSW : 2, M3 = C::MSW < 3 ? C::MSW : 3;
-  if (ms <= 1) gemm_body<GATED, MX, C, 1>(g, it, lds, msub);
+  // instances with 1, 2, 3 and MSW sub-tiles per wave, rounded up to MSQ
+  constexpr int Q = C::MSQ;
+  constexpr int M1 = Q, M2 = C::MSW < 2 ? C::MSW : (2 + Q - 1) / Q * Q;
+  constexpr int M3 = C::MSW < 3 ? C::MSW : (3 + Q - 1) / Q * Q;
+  if (ms <= 1) gemm_body<GATED, MX, C, M1>(g, it, lds, msub);
   else if (ms <= 2) gemm_body<GATED, MX, C, M2>(g, it, lds, msub);
   else if (ms <= 3) gemm_body<GATED, MX, C, M3>(g, it, lds, msub);
   else gemm_body<GATED, MX, C, C::MSW>(g, it, lds, msub);
@@ -931,8 +1035,11 @@ template <bool GATED, bool MX>
 void launch_tiles(bool narrow, const GemmArgs& g, int64_t cap, hipStream_t st) {
   using Wide = typename std::conditional<MX, typename std::conditional<GATED, Cfg1x, Cfg2x>::type,
                                          typename std::conditional<GATED, Cfg1, Cfg2>::type>::type;
+  using Narrow =
+      typename std::conditional<MX, typename std::conditional<GATED, Cfg1nx, Cfg2nx>::type,
+                                typename std::conditional<GATED, Cfg1n, Cfg2n>::type>::type;
   if (narrow)
-    launch_mfma<GATED, MX, typename std::conditional<GATED, Cfg1n, Cfg2n>::type>(g, cap, st);
+    launch_mfma<GATED, MX, Narrow>(g, cap, st);
   else
     launch_mfma<GATED, MX, Wide>(g, cap, st);
 }
@@ -946,10 +1053,11 @@ PlanGeom plan_geom(const moe_shape& s) {
   const bool bf = s.dtype != MOE_DTYPE_F32;  // bf16 or MXFP8 MFMA tiles
   const bool nar = narrow_tiles(s);
   const bool mx = s.dtype == MOE_DTYPE_MXFP8;
-  const int bm1 = bf ? (nar ? Cfg1n::BM : mx ? Cfg1x::BM : Cfg1::BM) : kBMf;
-  const int bm2 = bf ? (nar ? Cfg2n::BM : mx ? Cfg2x::BM : Cfg2::BM) : kBMf;
-  const int bn1 = bf ? (nar ? Cfg1n::BNW : mx ? Cfg1x::BNW : Cfg1::BNW) / 2 : kBNf;
-  const int bn2 = bf ? (nar ? Cfg2n::BNW : mx ? Cfg2x::BNW : Cfg2::BNW) : kBNf;
+  const int bm1 = bf ? (nar ? (mx ? Cfg1nx::BM : Cfg1n::BM) : mx ? Cfg1x::BM : Cfg1::BM) : kBMf;
+  const int bm2 = bf ? (nar ? (mx ? Cfg2nx::BM : Cfg2n::BM) : mx ? Cfg2x::BM : Cfg2::BM) : kBMf;
+  const int bn1 =
+      bf ? (nar ? (mx ? Cfg1nx::BNW : Cfg1n::BNW) : mx ? Cfg1x::BNW : Cfg1::BNW) / 2 : kBNf;
+  const int bn2 = bf ? (nar ? (mx ? Cfg2nx::BNW : Cfg2n::BNW) : mx ? Cfg2x::BNW : Cfg2::BNW) : kBNf;
   const bool sh = s.d_ff_shared > 0;
   return PlanGeom{bm1, bm2, cdiv(s.d_ff, bn1), sh ? cdiv(s.d_ff_shared, bn1) : 0,
                   cdiv(s.d_model, bn2), sh ? cdiv(s.d_model, bn2) : 0};
@@ -964,7 +1072,7 @@ hipError_t launch_plan(const moe_shape& s, const int32_t* offsets, const Workspa
   plan_kernel<<<2, 1024, 0, st>>>(offsets, s.n_experts, (int)s.T, fs > 0 ? 1 : 0, pg.bm1,
                                   pg.bm2, pg.nt1_r, pg.nt1_s, pg.nt2_r, pg.nt2_s, s.d_model,
                                   s.d_model, s.d_ff, fs > 0 ? fs : 64, w.plan1, w.plan1_hdr,
-                                  w.plan2, w.plan2_hdr);
+                                  w.plan2, w.plan2_hdr, narrow_tiles(s) ? 0 : 1);
   return hipGetLastError();
 }
 
@@ -1061,7 +1169,7 @@ hipError_t launch_dense_plan(const moe_shape& s, bool gated1, int K1, int Nout1,
   const int n1 = cdiv(Nout1, dense_bn(s, gated1));
   const int n2 = p2 ? cdiv(Nout2, dense_bn(s, false)) : 0;
   plan_kernel<<<p2 ? 2 : 1, 1024, 0, st>>>(nullptr, 0, (int)s.T, 1, bm, bm, 0, n1, 0, n2, K1,
-                                           K1, p2 ? K2 : 64, p2 ? K2 : 64, p1, h1, p2, h2);
+                                           K1, p2 ? K2 : 64, p2 ? K2 : 64, p1, h1, p2, h2, 0);
   return hipGetLastError();
 }
 
