@@ -391,7 +391,8 @@ struct GCfg {
   static constexpr int MAXS = MAXS_;  // deepest ring that items with few rows get
   static_assert(A_LOADS * 1024 * WAVES == A_BYTES && B_LOADS * 1024 * WAVES == B_BYTES, "");
   static_assert(SA * A_BYTES + SB * B_BYTES <= LDS_BYTES, "LDS");
-  static_assert(SB >= SA && SA >= 2 && SB <= SA + 1, "B runs at most one slice ahead of A");
+  static_assert(SA >= 2 && SB >= 2 && (SB == SA || SA == SB + 1),
+                "equal rings, or A one slice deeper than B");
   static_assert(ROWB == 128 || ROWB == 64, "k-slices are 64 or 128 bytes per row");
   // row sub-tiles per wave come in multiples of MSQ, so that an A stage is a
   // whole number of 1 KiB DMA blocks per wave
@@ -400,11 +401,13 @@ struct GCfg {
   __device__ static __forceinline__ int swz(int r) { return (r / RP) % CPR; }
 };
 
+// bf16 wide tiles: 256 x 256, three A stages and two B stages (160 KiB): the
+// gathered token rows get one more slice of lead than the weight rows
 #ifndef MOE_GEMM1_CFG
-#define MOE_GEMM1_CFG 2, 4, 2, 64, 2, 2
+#define MOE_GEMM1_CFG 2, 4, 2, 64, 3, 2
 #endif
 #ifndef MOE_GEMM2_CFG
-#define MOE_GEMM2_CFG 2, 4, 2, 64, 2, 2
+#define MOE_GEMM2_CFG 2, 4, 2, 64, 3, 2
 #endif
 using Cfg1 = GCfg<MOE_GEMM1_CFG>;
 using Cfg2 = GCfg<MOE_GEMM2_CFG>;
@@ -613,8 +616,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, const WorkItem& it,
   constexpr int SA = SDEEP > C::SA ? SDEEP : C::SA;
   constexpr int SB = SDEEP > C::SB ? SDEEP : C::SB;
   static_assert(SA * A_SL + SB * C::B_BYTES <= RING, "LDS");
-  static_assert(SB == SA && (!MX || SA <= 4),
-                "MXFP8: a window of SA-2 iterations holds at most one group load");
+  static_assert((SB == SA || (!MX && SA == SB + 1)) && (!MX || SA <= 4),
+                "MXFP8: equal rings, and a window of SA-2 iterations holds at most one group load");
   unsigned char* const Abuf = lds;
   unsigned char* const Bbuf = lds + SA * A_SL;
   unsigned char* const Gbuf = lds + RING;
@@ -638,6 +641,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, const WorkItem& it,
     for (int j = 0; j < C::B_LOADS; ++j)
       dma16(rb, b_off[j], k0, st + (w * C::B_LOADS + j) * 1024);
   };
+
 
   constexpr int NT = C::NTW, HT = NT / 2;  // weight tiles per wave; GATED: gate tiles
   f32x16_t acc[MS][NT];
@@ -669,12 +673,20 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, const WorkItem& it,
   // the younger ones are outstanding: A/B(kt+1 .. kt+SA-2), and the scale
   // group loaded in one of those iterations.  A scale group is loaded three
   // or more iterations before its first slice, so it is complete by then.
-  constexpr int YOUNGER = (SA - 2) * (AL + C::B_LOADS);
+  //
+  // With an A ring one slice deeper than the B ring (bf16), iteration j
+  // issues B(j+SB-1) first, then A(j+SA-1) = A(j+SB): the younger loads at
+  // iteration kt are A(kt+1) and A/B of iterations kt-SB+2 .. kt-1.
+  constexpr bool BFIRST = SA > SB;
+  constexpr int YOUNGER = BFIRST ? AL + (SB - 2) * (AL + C::B_LOADS)
+                                 : (SA - 2) * (AL + C::B_LOADS);
+  constexpr int SMAX = SA > SB ? SA : SB;
   issue_g(0);
 #pragma unroll
-  for (int j = -(SB - 1); j < 0; ++j) {
+  for (int j = -(SMAX - 1); j < 0; ++j) {
+    if (BFIRST && j + SB - 1 >= 0 && j + SB - 1 < nk) issue_b(j + SB - 1);
     if (j + SA - 1 >= 0 && j + SA - 1 < nk) issue_a(j + SA - 1);
-    if (j + SB - 1 < nk) issue_b(j + SB - 1);
+    if (!BFIRST && j + SB - 1 >= 0 && j + SB - 1 < nk) issue_b(j + SB - 1);
   }
 
   for (int kt = 0; kt < nk; ++kt) {
@@ -688,7 +700,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, const WorkItem& it,
         grp = grp || (it2 >= 0 && (it2 & 3) == 0 && (it2 >> 2) + 1 < ng);
       }
     }
-    if (kt + SB - 2 < nk) {
+    if (kt + SMAX - 2 < nk) {  // every younger load was issued
       if (grp) wait_vm<YOUNGER + 1>();
       else wait_vm<YOUNGER>();
     } else {
@@ -720,11 +732,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, const WorkItem& it,
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
         const int cur = ks & 1;
-        // refill the buffers of slice kt-1: A behind the first fragment
-        // reads, B one k-step later, so the reads of k-step 0 are not queued
-        // behind a burst of loads
-        if (ks == 0 && kt + SA - 1 < nk) issue_a(kt + SA - 1);
-        if (ks == 1 && kt + SB - 1 < nk) issue_b(kt + SB - 1);
+        // refill the buffers of slice kt-1 (with a deeper A ring, B first):
+        // the first set behind the first fragment reads, the second one
+        // k-step later, so the reads of k-step 0 are not queued behind a
+        // burst of loads
+        if (ks == (BFIRST ? 1 : 0) && kt + SA - 1 < nk) issue_a(kt + SA - 1);
+        if (ks == (BFIRST ? 0 : 1) && kt + SB - 1 < nk) issue_b(kt + SB - 1);
         if (ks + 1 < KSTEPS)
           load_frags<MX, C, MS>(As, Bs, a_row, b_row, fh, ks + 1, af[cur ^ 1], bf[cur ^ 1]);
 #pragma unroll
