@@ -449,6 +449,11 @@ using Cfg2nx = GCfg<MOE_GEMM2_SMALL_MX_CFG>;
 #endif
 constexpr int kNarrowRows = MOE_SMALL_ROWS;
 
+// bf16 outputs staged through LDS and stored as whole rows
+#ifndef MOE_STAGED_EPI
+#define MOE_STAGED_EPI 1
+#endif
+
 typedef __attribute__((address_space(1))) void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
@@ -798,6 +803,16 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, const WorkItem& it,
   // per 32 columns: the two lanes l and l^32 hold the 32 columns of a row.
   constexpr int OT = GATED ? HT : NT;  // output tiles per wave
   constexpr bool QOUT = MX && GATED;   // h is stored as MXFP8
+  // bf16 outputs go through LDS (the ring is free once every wave is past
+  // the last slice): each wave writes its tiles there, then the block stores
+  // whole rows, 16 bytes per lane with consecutive lanes on consecutive
+  // chunks, so each store instruction writes full cache lines instead of 16
+  // bytes of 32 different rows.  Rows are padded by 16 bytes (bank spread).
+  constexpr bool STAGE = MOE_STAGED_EPI && !QOUT;
+  constexpr int OC = GATED ? C::BNW / 2 : C::BNW;  // output columns of an item
+  constexpr int RSB = OC * 2 + 16;                 // bytes per staged row
+  static_assert(!STAGE || C::BM * RSB <= C::LDS_BYTES, "staged output tile fits in LDS");
+  if (STAGE) __builtin_amdgcn_s_barrier();
 #pragma unroll
   for (int i = 0; i < MS; ++i) {
     if (i == MS - 1 && !last) continue;
@@ -842,9 +857,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, const WorkItem& it,
             (shared ? g.cs_shared : g.cs_routed)[orow * (Nout / kMxBlock) + c0 / kMxBlock] =
                 (unsigned char)(X + 127);
         }
-      } else if (live) {
+      } else if (STAGE || live) {
         bf16_t* crow = reinterpret_cast<bf16_t*>(Cm) + orow * Nout;
-        if (!GATED && g.addend) {
+        if (!GATED && g.addend && live) {
           const bf16_t* arow = reinterpret_cast<const bf16_t*>(g.addend) + orow * Nout;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -860,8 +875,24 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, const WorkItem& it,
           u32x2_t pk;
           pk[0] = (uint32_t)f32_to_bf16(v[4 * q]) | ((uint32_t)f32_to_bf16(v[4 * q + 1]) << 16);
           pk[1] = (uint32_t)f32_to_bf16(v[4 * q + 2]) | ((uint32_t)f32_to_bf16(v[4 * q + 3]) << 16);
-          *reinterpret_cast<u32x2_t*>(crow + c0 + 8 * q + 4 * fh) = pk;
+          if (STAGE)
+            *reinterpret_cast<u32x2_t*>(lds + row * RSB + ((c0 - n0) + 8 * q + 4 * fh) * 2) = pk;
+          else
+            *reinterpret_cast<u32x2_t*>(crow + c0 + 8 * q + 4 * fh) = pk;
         }
+      }
+    }
+  }
+  if (STAGE) {
+    __syncthreads();
+    constexpr int CH = OC / 8;  // 16-byte chunks per staged row
+    const int live_ch = min(OC, Nout - n0) / 8;
+    const int nch = it.nrows * CH;
+    for (int q = tid; q < nch; q += C::THREADS) {
+      const int r = q / CH, ch = q - r * CH;
+      if (ch < live_ch) {
+        const i32x4_t v = *reinterpret_cast<const i32x4_t*>(lds + r * RSB + ch * 16);
+        *reinterpret_cast<i32x4_t*>(Cm + ((size_t)(it.row0 + r) * Nout + n0 + ch * 8) * 2) = v;
       }
     }
   }
@@ -908,10 +939,11 @@ __attribute__((amdgpu_waves_per_eu(C::WAVES * C::BLOCKS_PER_CU / 4))) void gemm_
   const int x = blockIdx.x & 7;
   const int beg = g.hdr[kHdrStart + x], end = g.hdr[kHdrStart + x + 1];
   for (;;) {
+    __syncthreads();  // every wave is done with the previous item's LDS
     if (threadIdx.x == 0) s_item = beg + atomicAdd(&g.hdr[kHdrCtr + x], 1);
-    __syncthreads();  // also: every wave is done with the previous item's LDS
-    const int item = __builtin_amdgcn_readfirstlane(s_item);
     __syncthreads();
+    const int item = __builtin_amdgcn_readfirstlane(s_item);
+    __syncthreads();  // read before the next DMA overwrites it
     if (item >= end) break;
     gemm_item<GATED, MX, C>(g, item, lds);
   }
