@@ -34,7 +34,11 @@ __device__ __forceinline__ uint4 pack8(const float* f) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// one block per token; threads walk the row in 16-byte vectors
+// one block per token; threads walk the row in 16-byte vectors.  All of a
+// vector's k expert rows are loaded before the first is added (KM >= k
+// slots, unrolled), so the loads are in flight together; the sum still runs
+// in ascending j.
+template <int KM>
 __global__ __launch_bounds__(CB_THREADS) void combine_bf16_kernel(
     const bf16_t* __restrict__ y_perm, const bf16_t* __restrict__ y_shared,
     const int32_t* __restrict__ slot, const float* __restrict__ topk_w, bf16_t* __restrict__ y,
@@ -47,21 +51,33 @@ __global__ __launch_bounds__(CB_THREADS) void combine_bf16_kernel(
     s_w[threadIdx.x] = topk_w[(size_t)t * k + threadIdx.x];
   }
   __syncthreads();
+  int sl[KM];
+  float gw[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    sl[j] = j < k ? s_slot[j] : -1;
+    gw[j] = j < k ? s_w[j] : 0.f;
+  }
   const int nv = d / 8;
   for (int v = threadIdx.x; v < nv; v += CB_THREADS) {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int sl = s_slot[j];
-      if (sl < 0) continue;
-      const float gw = s_w[j];
-      float e[8];
-      unpack8(reinterpret_cast<const uint4*>(y_perm + (size_t)sl * d)[v], e);
+    uint4 raw[KM];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += gw * e[i];
+    for (int j = 0; j < KM; ++j)
+      if (sl[j] >= 0) raw[j] = reinterpret_cast<const uint4*>(y_perm + (size_t)sl[j] * d)[v];
+    uint4 rs = make_uint4(0, 0, 0, 0);
+    if (y_shared) rs = reinterpret_cast<const uint4*>(y_shared + (size_t)t * d)[v];
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      if (sl[j] < 0) continue;  // beyond k, or a dropped assignment
+      float e[8];
+      unpack8(raw[j], e);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += gw[j] * e[i];
     }
     if (y_shared) {
       float e[8];
-      unpack8(reinterpret_cast<const uint4*>(y_shared + (size_t)t * d)[v], e);
+      unpack8(rs, e);
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] += e[i];
     }
@@ -142,8 +158,12 @@ __global__ __launch_bounds__(512) void bias_step_kernel(const int32_t* __restric
 hipError_t launch_combine(const moe_shape& s, const void* y_perm, const void* y_shared,
                           const int32_t* slot, const float* topk_w, void* y, hipStream_t st) {
   const int T = (int)s.T, d = s.d_model, k = s.top_k;
-  if (act_bf16(s))
-    combine_bf16_kernel<<<T, CB_THREADS, 0, st>>>(
+  if (act_bf16(s) && k <= 8)
+    combine_bf16_kernel<8><<<T, CB_THREADS, 0, st>>>(
+        static_cast<const bf16_t*>(y_perm), static_cast<const bf16_t*>(y_shared), slot, topk_w,
+        static_cast<bf16_t*>(y), d, k);
+  else if (act_bf16(s))
+    combine_bf16_kernel<16><<<T, CB_THREADS, 0, st>>>(
         static_cast<const bf16_t*>(y_perm), static_cast<const bf16_t*>(y_shared), slot, topk_w,
         static_cast<bf16_t*>(y), d, k);
   else

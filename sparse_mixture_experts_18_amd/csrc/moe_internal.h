@@ -183,4 +183,30 @@ hipError_t launch_ec_combine(const moe_shape& s, const void* y_perm, const void*
                              const int32_t* row_of, const float* scores, void* y,
                              hipStream_t st);
 
+// Direct global -> LDS loads through a buffer resource: the base address
+// sits in scalar registers, each lane supplies a 32-bit offset and a
+// uniform offset (a k-slice) goes in the scalar soffset, so a load costs one
+// VGPR.  Lane i of a wave writes its 16 bytes to lds_wave_base + 16 i.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const unsigned char* base,
+                                            uint32_t bytes = 0xFFFFFFFFu) {
+  // raw buffer (stride 0) of `bytes` bytes; reads past the end return 0;
+  // gfx9 dword 3
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(base), (short)0,
+                                           (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff,
+                                      unsigned char* lds_wave_base) {
+  typedef __attribute__((address_space(3))) void* lptr_t;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lptr_t)(lds_wave_base), 16, voff, soff, 0, 0);
+}
+
+// wait until at most n vector-memory ops of this wave are outstanding (they
+// retire in order)
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 }  // namespace moe

@@ -195,6 +195,112 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const bf16_t* __restri
   }
 }
 
+// The same product for batches that take no k split: 128 tokens x 64
+// experts per block, eight waves of 32 x 32 (x the three planes), k-slices of
+// 64 through a four-stage LDS ring filled by direct DMA (two slices in
+// flight while one is consumed), and an XCD-aware tile order: blocks of XCD
+// x take the x-th eighth of the tiles in column-major order, so an XCD works
+// on one or two expert tiles and keeps their 2.75 MB of weight planes in its
+// L2.  Every logit is computed by the same MFMA sequence as in
+// router_mfma_kernel (same operand order, k-steps in order, chunk sums
+// formed and added the same way), so the two kernels agree bit for bit.
+constexpr int R2_BM = 128, R2_BN = 64, R2_ST = 4;
+constexpr int R2_A = R2_BM * 128, R2_B = 3 * R2_BN * 128, R2_STAGE = R2_A + R2_B;
+
+__global__ __launch_bounds__(512) void router_mfma2_kernel(const bf16_t* __restrict__ x,
+                                                           const bf16_t* __restrict__ ws,
+                                                           float* __restrict__ out, int T, int N,
+                                                           int d) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[R2_ST * R2_STAGE];
+  const int ntm = (T + R2_BM - 1) / R2_BM, ntn = (N + R2_BN - 1) / R2_BN;
+  const int Q = ntm * ntn, per = (Q + 7) / 8;
+  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+  const int q = xcd * per + local;
+  if (local >= per || q >= Q) return;  // uniform over the block
+  const int m0 = (q % ntm) * R2_BM, n0 = (q / ntm) * R2_BN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // DMA: a wave load covers 8 rows of 128 bytes; lane -> row lane / 8 at LDS
+  // chunk position lane % 8, fetching the global chunk that belongs there
+  const int drow = lane >> 3, dpos = lane & 7;
+  const size_t plane = (size_t)N * d;
+  uint32_t a_off[2], b_off[3];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {  // A rows (w*2 + j)*8 + drow of 128
+    const int tr = (w * 2 + j) * 8 + drow;
+    a_off[j] = (uint32_t)((size_t)min(m0 + tr, T - 1) * d * 2) + ((dpos ^ rswz(tr)) << 4);
+  }
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {  // B rows (w*3 + j)*8 + drow of 3 x 64 (plane-major)
+    const int br = (w * 3 + j) * 8 + drow;
+    const int t = br / R2_BN, e = br % R2_BN;
+    b_off[j] = (uint32_t)((t * plane + (size_t)min(n0 + e, N - 1) * d) * 2) +
+               ((dpos ^ rswz(br)) << 4);
+  }
+  const rsrc_t ra = make_rsrc(reinterpret_cast<const unsigned char*>(x));
+  const rsrc_t rb = make_rsrc(reinterpret_cast<const unsigned char*>(ws));
+  const int nk = d / 64;
+  auto issue = [&](int kt) {
+    unsigned char* st = lds + (kt % R2_ST) * R2_STAGE;
+    const uint32_t k0 = (uint32_t)kt * 128;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dma16(ra, a_off[j], k0, st + (w * 2 + j) * 1024);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) dma16(rb, b_off[j], k0, st + R2_A + (w * 3 + j) * 1024);
+  };
+#pragma unroll
+  for (int kt = 0; kt < R2_ST - 1; ++kt)
+    if (kt < nk) issue(kt);
+
+  const int wm = w & 3, wn = w >> 2, fr = lane & 31, fh = lane >> 5;
+  const int ar = wm * 32 + fr, br = wn * 32 + fr;
+  constexpr int SL = RM_KC / 64;  // slices per chunk
+  f32x16_t acc[3], tot;
+#pragma unroll
+  for (int t = 0; t < 3; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+  for (int kt = 0; kt < nk; ++kt) {
+    // slice kt is complete once only the loads of slices kt+1, kt+2 remain
+    if (kt + R2_ST - 2 < nk) wait_vm<(R2_ST - 2) * 5>();
+    else wait_vm<0>();
+    __builtin_amdgcn_s_barrier();  // ... in every wave; slice kt-1 is free
+    if (kt + R2_ST - 1 < nk) issue(kt + R2_ST - 1);
+    const unsigned char* As = lds + (kt % R2_ST) * R2_STAGE;
+    const unsigned char* Bs = As + R2_A;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int ch = 2 * ks + fh;
+      const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(As + ar * 128 + ((ch ^ rswz(ar)) << 4));
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        const int rr = t * R2_BN + br;
+        const bf16x8_t bfr =
+            *reinterpret_cast<const bf16x8_t*>(Bs + rr * 128 + ((ch ^ rswz(rr)) << 4));
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr, acc[t], 0, 0, 0);
+      }
+    }
+    if ((kt + 1) % SL == 0 || kt + 1 == nk) {  // end of a chunk
+      const bool first = kt < SL;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = (acc[2][r] + acc[1][r]) + acc[0][r];
+        tot[r] = first ? p : tot[r] + p;
+      }
+#pragma unroll
+      for (int t = 0; t < 3; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+    }
+  }
+  const int col = n0 + wn * 32 + fr;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = m0 + wm * 32 + 8 * (r >> 2) + 4 * fh + (r & 3);
+    if (row < T && col < N) out[(size_t)row * N + col] = tot[r];
+  }
+}
+
 // ---------------------------------------------------------------------------
 // K2: one wavefront per token.  Lane l holds experts [l*P, l*P+P).
 // ---------------------------------------------------------------------------
@@ -404,6 +510,11 @@ hipError_t launch_router_gemm(const moe_shape& s, const void* x, const float* w_
       router_mfma_kernel<<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(x), w.wsplit,
                                                w.router_part, T, N, d, 1);
       *nparts = nkc;
+    } else if ((size_t)T * d * 2 < (1ull << 31) && (size_t)3 * N * d * 2 < (1ull << 31)) {
+      // (32-bit buffer offsets)
+      const int Q = ((T + R2_BM - 1) / R2_BM) * ((N + R2_BN - 1) / R2_BN);
+      router_mfma2_kernel<<<8 * ((Q + 7) / 8), 512, 0, st>>>(static_cast<const bf16_t*>(x),
+                                                              w.wsplit, logits, T, N, d);
     } else {
       dim3 grid((T + RM_BM - 1) / RM_BM, (N + RM_BN - 1) / RM_BN, 1);
       router_mfma_kernel<<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(x), w.wsplit, logits,
