@@ -248,6 +248,40 @@ def test_determinism_bitwise():
         assert torch.equal(a[k], b[k]), k
 
 
+def _route_logits(inp, shape):
+    T, N, k = shape.T, shape.n_experts, shape.top_k
+    dev = inp.x.device
+    ws = moe.workspace(shape, dev)
+    logits = torch.empty((T, N), dtype=torch.float32, device=dev)
+    scores = torch.empty((T, N), dtype=torch.float32, device=dev)
+    ti = torch.empty((T, k), dtype=torch.int32, device=dev)
+    tw = torch.empty((T, k), dtype=torch.float32, device=dev)
+    moe.moe_route(shape, inp.x, inp.w_router, inp.logit_add, None, inp.bias, logits, scores,
+                  ti, tw, ws)
+    torch.cuda.synchronize()
+    return logits
+
+
+def test_router_kernels_agree_on_ragged_shapes():
+    """A batch of 4133 tokens runs the router GEMM without the k split (the
+    DMA-fed large-batch kernel: 128-token tiles, the last one 37 rows deep;
+    96 experts, the second 64-expert tile half full; d = 576, so the last
+    512-wide k-chunk is one slice); batches of 64 tokens take the k split.
+    Rows 100..163 and the last 64 rows agree bit for bit, and every logit is
+    within the fp32 bound of the oracle's fp64 product."""
+    cfg = W.CONFIGS["mixtral"].replace(name="ragged_router", T=4133, d_model=576,
+                                       n_experts=96, top_k=4, d_ff=64)
+    inp = W.make_inputs(cfg, seed=6, device="cuda")
+    full = _route_logits(inp, moe.MoeShape.from_config(cfg))
+    for lo, hi in [(100, 164), (4069, 4133)]:
+        sub = W.LayerInputs(cfg, inp.x[lo:hi].contiguous(), inp.w_router, inp.w1, inp.w2,
+                            inp.w1_shared, inp.w2_shared, inp.bias, None)
+        part = _route_logits(sub, moe.MoeShape.from_config(cfg, T=hi - lo))
+        assert torch.equal(part, full[lo:hi]), (lo, hi)
+    x = host(inp.x).astype(np.float64)
+    router_tolerance_ok(x, host(inp.w_router).astype(np.float64), None, host(full), terms=3)
+
+
 @pytest.mark.parametrize("name", ["dsv3", "decode"])
 def test_batch_invariance_dropless(name):
     """A token's scores, choice, gates and output do not depend on the batch it
