@@ -12,7 +12,8 @@
 //
 // MFMA path (bf16: v_mfma_f32_32x32x16_bf16; MXFP8: the block-scaled
 // v_mfma_scale_f32_32x32x64_f8f6f4), fp32 accumulation, work items of up to
-// 256 rows x 256 weight rows (64 x 128 for layers with few rows per expert),
+// 384 (gate/up) or 256 (down) rows x 256 weight rows (64 x 128 for layers
+// with few rows per expert),
 // both operands K-contiguous (weights in nn.Linear [out, in] layout), staged
 // through LDS by direct buffer DMA with an XOR swizzle of the 16-byte chunks.
 // The work list (segment, row block, column tile) is built on the device
@@ -390,7 +391,9 @@ struct GCfg {
   static constexpr int BLOCKS_PER_CU = 160 / LDS_KIB_;
   static constexpr int MAXS = MAXS_;  // deepest ring that items with few rows get
   static_assert(A_LOADS * 1024 * WAVES == A_BYTES && B_LOADS * 1024 * WAVES == B_BYTES, "");
-  static_assert(SA * A_BYTES + SB * B_BYTES <= LDS_BYTES, "LDS");
+  // the full-height tile needs at least two stages of each operand (shorter
+  // items take the configured depths, or deeper rings, when they fit)
+  static_assert(2 * A_BYTES + 2 * B_BYTES <= LDS_BYTES, "LDS");
   static_assert(SA >= 2 && SB >= 2 && (SB == SA || SA == SB + 1),
                 "equal rings, or A one slice deeper than B");
   static_assert(ROWB == 128 || ROWB == 64, "k-slices are 64 or 128 bytes per row");
@@ -401,10 +404,16 @@ struct GCfg {
   __device__ static __forceinline__ int swz(int r) { return (r / RP) % CPR; }
 };
 
-// bf16 wide tiles: 256 x 256, three A stages and two B stages (160 KiB): the
-// gathered token rows get one more slice of lead than the weight rows
+// bf16 wide tiles.  Gate/up: up to 384 rows x 256 weight rows (six 32-row
+// sub-tiles per wave), so an expert of up to 384 rows streams its weights
+// once and each k-slice carries 1.5x the MFMA work per byte of 256-row
+// tiles; items of up to 256 rows take three A stages and two B stages
+// (160 KiB: the gathered token rows get one more slice of lead than the
+// weight rows), taller ones two of each.  Down: 256 x 256, three A and two
+// B stages (its bf16 output tile is staged through LDS, which a 384-row
+// tile would not fit).
 #ifndef MOE_GEMM1_CFG
-#define MOE_GEMM1_CFG 2, 4, 2, 64, 3, 2
+#define MOE_GEMM1_CFG 2, 4, 2, 64, 3, 2, 6
 #endif
 #ifndef MOE_GEMM2_CFG
 #define MOE_GEMM2_CFG 2, 4, 2, 64, 3, 2
@@ -592,8 +601,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, const WorkItem& it,
   constexpr int RING = C::LDS_BYTES - SGL;
   constexpr int SDEEP = (RING / (A_SL + C::B_BYTES)) < C::MAXS
                             ? (RING / (A_SL + C::B_BYTES)) : C::MAXS;
-  constexpr int SA = SDEEP > C::SA ? SDEEP : C::SA;
-  constexpr int SB = SDEEP > C::SB ? SDEEP : C::SB;
+  constexpr bool CFG_FITS = C::SA * A_SL + C::SB * C::B_BYTES <= RING;
+  constexpr int SA = SDEEP > C::SA ? SDEEP : (CFG_FITS ? C::SA : SDEEP);
+  constexpr int SB = SDEEP > C::SB ? SDEEP : (CFG_FITS ? C::SB : SDEEP);
   static_assert(SA * A_SL + SB * C::B_BYTES <= RING, "LDS");
   static_assert((SB == SA || (!MX && SA == SB + 1)) && (!MX || SA <= 4),
                 "MXFP8: equal rings, and a window of SA-2 iterations holds at most one group load");
@@ -703,7 +713,39 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, const WorkItem& it,
 #pragma unroll
       for (int j = 0; j < NT; ++j) sb_w[j] = sc[4 * (C::BM + b_row[j])] >> (8 * fh);
     }
-    if constexpr (!MX) {
+    if constexpr (!MX && MS * NT * 16 + 2 * (MS + NT) * 4 > 224) {
+      // tall tiles: the weight fragments of a k-step stay in registers, the
+      // row fragments rotate through two registers (each read one sub-tile
+      // ahead), so the fragments fit next to the accumulators
+      FT bf[NT], a_cur, a_nxt;
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        bf[j] = Frag<MX>::read(Bs + b_row[j] * C::ROWB, 0, fh, C::swz(b_row[j]));
+      a_cur = Frag<MX>::read(As + a_row[0] * C::ROWB, 0, fh, C::swz(a_row[0]));
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const bool more = ks + 1 < KSTEPS;
+        if (ks == (BFIRST ? 1 : 0) && kt + SA - 1 < nk) issue_a(kt + SA - 1);
+        if (ks == (BFIRST ? 0 : 1) && kt + SB - 1 < nk) issue_b(kt + SB - 1);
+#pragma unroll
+        for (int i = 0; i < MS; ++i) {
+          if (i + 1 < MS)
+            a_nxt = Frag<MX>::read(As + a_row[i + 1] * C::ROWB, ks, fh, C::swz(a_row[i + 1]));
+          else if (more)
+            a_nxt = Frag<MX>::read(As + a_row[0] * C::ROWB, ks + 1, fh, C::swz(a_row[0]));
+          if (i < MS - 1 || last) {
+#pragma unroll
+            for (int j = 0; j < NT; ++j) acc[i][j] = mma(bf[j], a_cur, acc[i][j], 0, 0);
+          }
+          if (i == MS - 1 && more) {
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+              bf[j] = Frag<MX>::read(Bs + b_row[j] * C::ROWB, ks + 1, fh, C::swz(b_row[j]));
+          }
+          a_cur = a_nxt;
+        }
+      }
+    } else if constexpr (!MX) {
       // fragments of k-step ks+1 are read while the MFMAs of k-step ks run
       // (two register sets)
       FT bf[2][NT], af[2][MS];
@@ -782,10 +824,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, const WorkItem& it,
   // whole rows, 16 bytes per lane with consecutive lanes on consecutive
   // chunks, so each store instruction writes full cache lines instead of 16
   // bytes of 32 different rows.  Rows are padded by 16 bytes (bank spread).
-  constexpr bool STAGE = MOE_STAGED_EPI && !QOUT;
   constexpr int OC = GATED ? C::BNW / 2 : C::BNW;  // output columns of an item
   constexpr int RSB = OC * 2 + 16;                 // bytes per staged row
-  static_assert(!STAGE || C::BM * RSB <= C::LDS_BYTES, "staged output tile fits in LDS");
+  constexpr bool STAGE = MOE_STAGED_EPI && !QOUT && C::BM * RSB <= C::LDS_BYTES;
   if (STAGE) __builtin_amdgcn_s_barrier();
 #pragma unroll
   for (int i = 0; i < MS; ++i) {
@@ -897,9 +938,13 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& g, int item, unsigned 
   constexpr int Q = C::MSQ;
   constexpr int M1 = Q, M2 = C::MSW < 2 ? C::MSW : (2 + Q - 1) / Q * Q;
   constexpr int M3 = C::MSW < 3 ? C::MSW : (3 + Q - 1) / Q * Q;
+  constexpr int M4 = C::MSW < 4 ? C::MSW : (4 + Q - 1) / Q * Q;
+  constexpr int M5 = C::MSW < 5 ? C::MSW : (5 + Q - 1) / Q * Q;
   if (ms <= 1) gemm_body<GATED, MX, C, M1>(g, it, lds, msub);
   else if (ms <= 2) gemm_body<GATED, MX, C, M2>(g, it, lds, msub);
   else if (ms <= 3) gemm_body<GATED, MX, C, M3>(g, it, lds, msub);
+  else if (C::MSW > 4 && ms <= 4) gemm_body<GATED, MX, C, M4>(g, it, lds, msub);
+  else if (C::MSW > 5 && ms <= 5) gemm_body<GATED, MX, C, M5>(g, it, lds, msub);
   else gemm_body<GATED, MX, C, C::MSW>(g, it, lds, msub);
 }
 
