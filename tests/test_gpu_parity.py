@@ -176,6 +176,10 @@ SMALL = [
     _small_cfg("s_cap0", T=33, n_experts=4, top_k=1, capacity_factor=0.1),
     _small_cfg("s_sig_norenorm", T=200, n_experts=100, top_k=7, score_fn="sigmoid",
                renormalize=False, jitter_std=0.3, dtype="f32", d_model=64, d_ff=96),
+    # experts of ~250-400 rows and a 1600-row shared expert: gate/up items of
+    # five and six 32-row sub-tiles per wave (the tall tiles), partial column tiles
+    _small_cfg("s_tall_rows", T=1600, n_experts=5, top_k=1, d_model=192, d_ff=320,
+               d_ff_shared=192),
 ]
 
 
