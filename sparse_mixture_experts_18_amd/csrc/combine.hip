@@ -16,6 +16,7 @@ namespace moe {
 namespace {
 
 constexpr int CB_THREADS = 256;
+typedef unsigned int u4v __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ void unpack8(const uint4& v, float* o) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -63,7 +64,13 @@ __global__ __launch_bounds__(CB_THREADS) void combine_bf16_kernel(
     uint4 raw[KM];
 #pragma unroll
     for (int j = 0; j < KM; ++j)
-      if (sl[j] >= 0) raw[j] = reinterpret_cast<const uint4*>(y_perm + (size_t)sl[j] * d)[v];
+      if (sl[j] >= 0) {
+        // each expert row is read once: non-temporal loads keep it from
+        // displacing reusable lines in the caches
+        const u4v t = __builtin_nontemporal_load(
+            reinterpret_cast<const u4v*>(y_perm + (size_t)sl[j] * d) + v);
+        raw[j] = make_uint4(t[0], t[1], t[2], t[3]);
+      }
     uint4 rs = make_uint4(0, 0, 0, 0);
     if (y_shared) rs = reinterpret_cast<const uint4*>(y_shared + (size_t)t * d)[v];
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
