@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const XT* __restrict__ y
   double s = 0.0, q = 0.0, mx = -INFINITY, ma = 0.0;
   for (int c = lane; c < nch; c += kWave) {
     float f[E];
-    Chunk<XT>::get(p[c], f);
+    Chunk<XT>::get(__builtin_nontemporal_load(p + c), f);  // each row is read once
 #pragma unroll
     for (int i = 0; i < E; ++i) {
       const double v = (double)f[i];
