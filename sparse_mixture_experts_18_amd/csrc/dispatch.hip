@@ -42,7 +42,7 @@ __global__ __launch_bounds__(kDispatchChunk) void rank_kernel(const int32_t* __r
   int r = 0;
   bool last = true;
   for (int j = 0; j < kWave; ++j) {
-    const int ej = __shfl(e, j, kWave);
+    const int ej = __builtin_amdgcn_readlane(e, j);
     if (ej == e) {
       r += j < lane;
       last = last && !(j > lane);
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(kDispatchChunk) void dispatch_one_chunk_kernel(
   int r = 0;
   bool last = true;
   for (int j = 0; j < kWave; ++j) {
-    const int ej = __shfl(e, j, kWave);
+    const int ej = __builtin_amdgcn_readlane(e, j);
     if (ej == e) {
       r += j < lane;
       last = last && !(j > lane);

@@ -325,17 +325,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
   return v;
 }
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint32_t lo = __shfl_xor((uint32_t)v, o, kWave);
-    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, kWave);
-    uint64_t w = ((uint64_t)hi << 32) | lo;
-    v = w > v ? w : v;
-  }
-  return v;
-}
-
 constexpr int TK_WAVES = 4;
 
 template <int P>
@@ -449,35 +438,59 @@ __global__ __launch_bounds__(256) void topk_kernel(
       if (e < N && !gsel[wv][e / gsz]) ok[p] = 0u;
     }
   }
-  // k rounds of wave arg-max on (key desc, index asc); lane j keeps round j
+  // Selection: the k largest (key, -index) pairs among the candidates
+  // (ok > 0; a valid shape has at least k).  tau, the k-th largest order key,
+  // is found bit by bit from wave ballots; every key above tau is taken, then
+  // the ties at tau in ascending expert order.  Lane j then receives the pick
+  // of rank j (key descending, index ascending): the order in which k rounds
+  // of arg-max would take them.
+  uint32_t tau = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = tau | (1u << b);
+    int cnt = 0;
+#pragma unroll
+    for (int p = 0; p < P; ++p) cnt += __popcll(__ballot(ok[p] >= cand));
+    if (cnt >= k) tau = cand;
+  }
+  int need = k;  // ties at tau to take
+  int below = 0;  // ties at tau in the lanes below this one
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    need -= __popcll(__ballot(ok[p] > tau));
+    const uint64_t tm = __ballot(ok[p] == tau);
+    below += __builtin_amdgcn_mbcnt_hi((uint32_t)(tm >> 32),
+                                       __builtin_amdgcn_mbcnt_lo((uint32_t)tm, 0u));
+  }
+  uint64_t selm[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const bool tie = ok[p] == tau;
+    selm[p] = __ballot(ok[p] > tau || (tie && below < need));
+    below += tie;
+  }
   int my_e = 0;
   float my_s = 0.f;
-  for (int j = 0; j < k; ++j) {
-    uint64_t best = 0;
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-      uint64_t c = ((uint64_t)ok[p] << 32) |
-                   (uint32_t)(0xffffffffu - (uint32_t)(lane * P + p));
-      best = c > best ? c : best;
-    }
-    best = wave_max_u64(best);
-    const int e = (int)(0xffffffffu - (uint32_t)best);
-    float sv = 0.f;
+  for (int p = 0; p < P; ++p) {
+    for (uint64_t m = selm[p]; m; m &= m - 1) {
+      const int l = __builtin_ctzll(m);
+      const uint32_t okm = __builtin_amdgcn_readlane(ok[p], l);
+      const float sm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s[p]), l));
+      const int em = l * P + p;
+      int rank = 0;
 #pragma unroll
-    for (int p = 0; p < P; ++p)
-      if (lane * P + p == e) {
-        sv = s[p];
-        ok[p] = 0u;
+      for (int q = 0; q < P; ++q)
+        rank += __popcll(__ballot(ok[q] > okm || (ok[q] == okm && lane * P + q < em)));
+      if (lane == rank) {
+        my_e = em;
+        my_s = sm;
       }
-    sv = __shfl(sv, e / P, kWave);
-    if (lane == j) {
-      my_e = e;
-      my_s = sv;
     }
   }
   // renormalise: fp32 sum in ascending j
   float sum = 0.f;
-  for (int j = 0; j < k; ++j) sum += __shfl(my_s, j, kWave);
+  for (int j = 0; j < k; ++j)
+    sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), j));
   if (valid && lane < k) {
     topk_idx[(size_t)t * k + lane] = my_e;
     topk_w[(size_t)t * k + lane] = renorm ? my_s / sum : my_s;
