@@ -227,6 +227,56 @@ def test_injected_tie_scores_bit_exact():
             assert (ref[10] == np.arange(5)).all()
 
 
+@pytest.mark.parametrize("N,k,groups", [(24, 5, (1, 1)), (100, 7, (1, 1)), (130, 1, (1, 1)),
+                                         (256, 8, (8, 4)), (512, 16, (1, 1)),
+                                         (512, 16, (16, 8))])
+def test_topk_selection_specials_every_lane_width(N, k, groups):
+    """Selection over 1, 2, 4 and 8 experts per lane: keys from a few values
+    (ties at the k-th key), all-equal rows, exactly k-1 keys above a run of
+    ties, NaN, +-0 and +-inf, with a selection bias; indices against the
+    oracle's (key desc, index asc) rule, weights against its renormalisation."""
+    T = 300
+    cfg = _small_cfg("sel", T=T, n_experts=N, top_k=k, n_groups=groups[0],
+                     topk_groups=groups[1], bias_zero=True)
+    sh = moe.MoeShape.from_config(cfg)
+    r = np.random.default_rng(N * 31 + k)
+    s = r.choice(np.array([0.0, 0.25, 0.5, 1.0], np.float32), (T, N))
+    s[0] = 0.5
+    s[1, ::3] = np.nan
+    s[2] = -0.0
+    s[2, ::2] = 0.0
+    s[3, 5], s[3, 7] = np.inf, -np.inf
+    s[4] = -np.inf
+    s[5] = np.abs(r.standard_normal(N)).astype(np.float32)
+    s[6] = 0.0
+    s[6, N - k + 1:] = 1.0
+    s[7] = r.random(N).astype(np.float32)  # distinct
+    bias = np.zeros(N, np.float32)
+    bias[r.random(N) < 0.3] = 0.25  # moves keys onto the neighbouring value
+    for b in (None, bias):
+        scores = torch.from_numpy(s).cuda()
+        bt = None if b is None else torch.from_numpy(b).cuda()
+        ws = moe.workspace(sh)
+        ti = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        tw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        moe.moe_route(sh, None, None, None, scores, bt, None, None, ti, tw, ws)
+        torch.cuda.synchronize()
+        keys = oracle.selection_keys(s, b)
+        cand = None
+        if groups[0] > 1:
+            cand = oracle.group_candidates(keys, groups[0], groups[1], k // groups[1])
+        ref = oracle.topk_select(keys, k, cand)
+        assert (host(ti) == ref).all(), (b is None, np.nonzero((host(ti) != ref).any(1))[0][:5])
+        with np.errstate(invalid="ignore"):  # rows of infinities or zeros
+            g = oracle.gate_weights(s, ref, True)
+        fin = np.isfinite(g).all(1)
+        assert fin.sum() > T // 2
+        assert np.allclose(host(tw)[fin], g[fin], rtol=2e-6, atol=0)
+        if b is None and groups == (1, 1):
+            assert (ref[0] == np.arange(k)).all()
+            assert (ref[6, : k - 1] == np.arange(N - k + 1, N)).all() and ref[6, k - 1] == 0
+
+
 def test_identical_tokens_drop_closed_form():
     cfg = _small_cfg("same", T=200, n_experts=8, top_k=2, capacity_factor=1.0)
     inp = W.make_inputs(cfg, seed=2, device="cuda")
