@@ -12,8 +12,8 @@
 //
 // MFMA path (bf16: v_mfma_f32_32x32x16_bf16; MXFP8: the block-scaled
 // v_mfma_scale_f32_32x32x64_f8f6f4), fp32 accumulation, work items of up to
-// 384 (gate/up) or 256 (down) rows x 256 weight rows (64 x 128 for layers
-// with few rows per expert),
+// 384 (gate/up) or 256 (down) rows x 256 weight rows (64 x 128 and 64 x 256
+// for layers with few rows per expert),
 // both operands K-contiguous (weights in nn.Linear [out, in] layout), staged
 // through LDS by direct buffer DMA with an XOR swizzle of the 16-byte chunks.
 // The work list (segment, row block, column tile) is built on the device
@@ -430,16 +430,19 @@ using Cfg2 = GCfg<MOE_GEMM2_CFG>;
 using Cfg1x = GCfg<MOE_GEMM1_MX_CFG>;
 using Cfg2x = GCfg<MOE_GEMM2_MX_CFG>;
 // Layers with few rows per expert (decode batches) stream the weights with
-// short items: 64 rows x 128 weight rows, four waves, and the LDS spent on a
-// four-deep ring.  Twice as many items as weight slabs of 256 rows spread
-// the touched experts' weights over every CU, and the deeper ring keeps more
-// bytes in flight per CU.  The k order of every output is the same as with
-// the wide tiles, so the choice never changes a result.
+// short items and the LDS spent on a four-deep ring.  Gate/up: 64 rows x 128
+// weight rows on four waves -- twice as many items as weight slabs of 256
+// rows spread the touched experts' weights over every CU.  Down: 64 rows x
+// 256 weight rows on eight waves -- its reduction is only d_ff long, so the
+// wider slice (twice the bytes in flight per CU) and half the items (each
+// with its own ring fill and epilogue) pay more than the finer spread.  The
+// k order of every output is the same as with the wide tiles, so the choice
+// never changes a result.
 #ifndef MOE_GEMM1_SMALL_CFG
 #define MOE_GEMM1_SMALL_CFG 2, 2, 2, 64, 2, 2, 1, 160, 4
 #endif
 #ifndef MOE_GEMM2_SMALL_CFG
-#define MOE_GEMM2_SMALL_CFG 2, 2, 2, 64, 2, 2, 1, 160, 4
+#define MOE_GEMM2_SMALL_CFG 2, 4, 2, 64, 2, 2, 1, 160, 4
 #endif
 using Cfg1n = GCfg<MOE_GEMM1_SMALL_CFG>;
 using Cfg2n = GCfg<MOE_GEMM2_SMALL_CFG>;
@@ -447,7 +450,7 @@ using Cfg2n = GCfg<MOE_GEMM2_SMALL_CFG>;
 #define MOE_GEMM1_SMALL_MX_CFG 2, 2, 2, 64, 2, 2, 1, 160, 4
 #endif
 #ifndef MOE_GEMM2_SMALL_MX_CFG
-#define MOE_GEMM2_SMALL_MX_CFG 2, 2, 2, 64, 2, 2, 1, 160, 4
+#define MOE_GEMM2_SMALL_MX_CFG 2, 4, 2, 64, 2, 2, 1, 160, 4
 #endif
 using Cfg1nx = GCfg<MOE_GEMM1_SMALL_MX_CFG>;
 using Cfg2nx = GCfg<MOE_GEMM2_SMALL_MX_CFG>;
