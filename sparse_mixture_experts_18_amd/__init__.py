@@ -510,20 +510,26 @@ def forward(shape: MoeShape, x, w_router, w1, w2, *, logit_add=None, bias=None,
     slot and n_kept_dropped."""
     dev = x.device
     T, N, k, d = shape.T, shape.n_experts, shape.top_k, shape.d_model
-    out = {"y": torch.empty((T, d), dtype=shape.torch_dtype, device=dev)}
-    if outputs:
-        out.update(
-            scores=torch.empty((T, N), dtype=torch.float32, device=dev),
-            topk_idx=torch.empty((T, k), dtype=torch.int32, device=dev),
-            topk_w=torch.empty((T, k), dtype=torch.float32, device=dev),
-            counts=torch.empty((N,), dtype=torch.int32, device=dev),
-            offsets=torch.empty((N + 1,), dtype=torch.int32, device=dev),
-            slot=torch.empty((T * k,), dtype=torch.int32, device=dev),
-            n_kept_dropped=torch.empty((2,), dtype=torch.int32, device=dev))
-    if ws is None:
-        ws = workspace(shape, dev)
+    st = torch.cuda.current_stream(dev) if stream is None else stream
+    # allocate on the stream the kernels run on: the caching allocator then
+    # reuses a freed block only for later work on that stream, so the
+    # workspace freed on return is never handed to other work while the
+    # kernels still use it
+    with torch.cuda.stream(st):
+        out = {"y": torch.empty((T, d), dtype=shape.torch_dtype, device=dev)}
+        if outputs:
+            out.update(
+                scores=torch.empty((T, N), dtype=torch.float32, device=dev),
+                topk_idx=torch.empty((T, k), dtype=torch.int32, device=dev),
+                topk_w=torch.empty((T, k), dtype=torch.float32, device=dev),
+                counts=torch.empty((N,), dtype=torch.int32, device=dev),
+                offsets=torch.empty((N + 1,), dtype=torch.int32, device=dev),
+                slot=torch.empty((T * k,), dtype=torch.int32, device=dev),
+                n_kept_dropped=torch.empty((2,), dtype=torch.int32, device=dev))
+        if ws is None:
+            ws = workspace(shape, dev)
     g = out.get
     moe_forward(shape, x, w_router, logit_add, bias, w1, w2, w1_shared, w2_shared, out["y"],
                 g("scores"), g("topk_idx"), g("topk_w"), g("counts"), g("offsets"), g("slot"),
-                g("n_kept_dropped"), ws, stream)
+                g("n_kept_dropped"), ws, st)
     return out

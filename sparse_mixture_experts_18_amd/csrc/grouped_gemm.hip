@@ -24,6 +24,7 @@
 // L2.  The same
 // kernels run the dense products of the LatentMoE layer over a one-segment
 // list.  An fp32 VALU path serves fp32 layers.
+#include <atomic>
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -85,13 +86,7 @@ __device__ __forceinline__ void block_exclusive_scan2(int* sh0, int* sh1, int v0
 
 // Cost of an item for the XCD split: (live 32-row sub-tiles + a fixed part for
 // the weight slice every item streams) x k-slices.
-#ifndef MOE_COST_FIXED
-#define MOE_COST_FIXED 2
-#endif
-
-#ifndef MOE_PLAN_DEAL
-#define MOE_PLAN_DEAL 1
-#endif
+constexpr int kCostFixed = 2;
 
 // Work-list header (int32): [0] item count, [1..9] XCD range starts
 // (xcd x owns items [hdr[1+x], hdr[2+x])), [16..23] per-XCD item counters.
@@ -107,10 +102,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
                                                     int32_t* __restrict__ hdr2, int deal) {
   __shared__ int sh0[64], sh1[64];
   __shared__ int st1s[1025], st2s[1025], mt1s[1024], mt2s[1024], rbases[1024], rowss[1024];
-#if MOE_PLAN_DEAL
   __shared__ long long ucost[1024];
   __shared__ int uslot[1024];
-#endif
   const int s = threadIdx.x;
   const int S = N + has_shared;
   int rows = 0, rbase = 0, n1t = 0, n2t = 0;
@@ -146,7 +139,6 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     WorkItem* plan = pass ? plan2 : plan1;
     int32_t* hdr = pass ? hdr2 : hdr1;
     const int tot = pass ? tot2 : tot1;
-#if MOE_PLAN_DEAL
     // Lists of routed experts on the wide tiles.  Units: each routed expert
     // (all its column tiles) and each column tile of the shared expert.  A
     // unit's cost is the sum of its items' costs (32-row sub-tiles plus a
@@ -177,7 +169,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
           // row blocks as in the walk below: mt - 1 blocks of `part` rows
           const int part = ((R + mt - 1) / mt + 31) / 32 * 32;
           const long long sub = (long long)(mt - 1) * (part / 32) + (R - (mt - 1) * part + 31) / 32;
-          c = (long long)(t1 - t0) * (sub + (long long)MOE_COST_FIXED * mt) * (useg < N ? kr : ks);
+          c = (long long)(t1 - t0) * (sub + (long long)kCostFixed * mt) * (useg < N ? kr : ks);
         }
       }
       ucost[s] = c;
@@ -225,7 +217,6 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
       }
       return;
     }
-#endif
     // Otherwise (one-segment dense lists): items in segment-major, then column
     // tile, then row block order.  Thread s fills a contiguous chunk of the
     // list; the list is then cut into 8 ranges of equal cost, one per XCD.
@@ -259,7 +250,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
         // so the row blocks that share a weight slab run at the same pace
         const int part = ((rowss[seg] + mt - 1) / mt + 31) / 32 * 32;
         const int nr = min(part, rowss[seg] - m * part);
-        const int cost = (((nr + 31) >> 5) + MOE_COST_FIXED) * (seg < N ? kr : ks);
+        const int cost = (((nr + 31) >> 5) + kCostFixed) * (seg < N ? kr : ks);
         visit(i, WorkItem{seg, rbases[seg] + m * part, nr, nt}, cost);
         if (++m == mt) {
           m = 0;
@@ -412,23 +403,11 @@ struct GCfg {
 // weight rows), taller ones two of each.  Down: 256 x 256, three A and two
 // B stages (its bf16 output tile is staged through LDS, which a 384-row
 // tile would not fit).
-#ifndef MOE_GEMM1_CFG
-#define MOE_GEMM1_CFG 2, 4, 2, 64, 3, 2, 6
-#endif
-#ifndef MOE_GEMM2_CFG
-#define MOE_GEMM2_CFG 2, 4, 2, 64, 3, 2
-#endif
-using Cfg1 = GCfg<MOE_GEMM1_CFG>;
-using Cfg2 = GCfg<MOE_GEMM2_CFG>;
+using Cfg1 = GCfg<2, 4, 2, 64, 3, 2, 6>;
+using Cfg2 = GCfg<2, 4, 2, 64, 3, 2>;
 // MXFP8 layers (the scale DMA needs BM + BNW <= 64 * WAVES)
-#ifndef MOE_GEMM1_MX_CFG
-#define MOE_GEMM1_MX_CFG 2, 4, 2, 64, 2, 2
-#endif
-#ifndef MOE_GEMM2_MX_CFG
-#define MOE_GEMM2_MX_CFG 2, 4, 2, 64, 2, 2
-#endif
-using Cfg1x = GCfg<MOE_GEMM1_MX_CFG>;
-using Cfg2x = GCfg<MOE_GEMM2_MX_CFG>;
+using Cfg1x = GCfg<2, 4, 2, 64, 2, 2>;
+using Cfg2x = GCfg<2, 4, 2, 64, 2, 2>;
 // Layers with few rows per expert (decode batches) stream the weights with
 // short items and the LDS spent on a four-deep ring.  Gate/up: 64 rows x 128
 // weight rows on four waves -- twice as many items as weight slabs of 256
@@ -438,33 +417,17 @@ using Cfg2x = GCfg<MOE_GEMM2_MX_CFG>;
 // with its own ring fill and epilogue) pay more than the finer spread.  The
 // k order of every output is the same as with the wide tiles, so the choice
 // never changes a result.
-#ifndef MOE_GEMM1_SMALL_CFG
-#define MOE_GEMM1_SMALL_CFG 2, 2, 2, 64, 2, 2, 1, 160, 4
-#endif
-#ifndef MOE_GEMM2_SMALL_CFG
-#define MOE_GEMM2_SMALL_CFG 2, 4, 2, 64, 2, 2, 1, 160, 4
-#endif
-using Cfg1n = GCfg<MOE_GEMM1_SMALL_CFG>;
-using Cfg2n = GCfg<MOE_GEMM2_SMALL_CFG>;
-#ifndef MOE_GEMM1_SMALL_MX_CFG
-#define MOE_GEMM1_SMALL_MX_CFG 2, 2, 2, 64, 2, 2, 1, 160, 4
-#endif
-#ifndef MOE_GEMM2_SMALL_MX_CFG
-#define MOE_GEMM2_SMALL_MX_CFG 2, 4, 2, 64, 2, 2, 1, 160, 4
-#endif
-using Cfg1nx = GCfg<MOE_GEMM1_SMALL_MX_CFG>;
-using Cfg2nx = GCfg<MOE_GEMM2_SMALL_MX_CFG>;
+using Cfg1n = GCfg<2, 2, 2, 64, 2, 2, 1, 160, 4>;
+using Cfg2n = GCfg<2, 4, 2, 64, 2, 2, 1, 160, 4>;
+using Cfg1nx = GCfg<2, 2, 2, 64, 2, 2, 1, 160, 4>;
+using Cfg2nx = GCfg<2, 4, 2, 64, 2, 2, 1, 160, 4>;
+// Row blocks of the dense (one-segment) lists are sized by the plain
+// configurations and also run on the gated ones; a work item may never be
+// taller than the tile that runs it.
+static_assert(Cfg2::BM <= Cfg1::BM && Cfg2n::BM <= Cfg1n::BM, "dense row blocks fit both tiles");
 
 // mean rows per expert at or below which the small-row tiles are used
-#ifndef MOE_SMALL_ROWS
-#define MOE_SMALL_ROWS 64
-#endif
-constexpr int kNarrowRows = MOE_SMALL_ROWS;
-
-// bf16 outputs staged through LDS and stored as whole rows
-#ifndef MOE_STAGED_EPI
-#define MOE_STAGED_EPI 1
-#endif
+constexpr int kNarrowRows = 64;
 
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
@@ -829,7 +792,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, const WorkItem& it,
   // bytes of 32 different rows.  Rows are padded by 16 bytes (bank spread).
   constexpr int OC = GATED ? C::BNW / 2 : C::BNW;  // output columns of an item
   constexpr int RSB = OC * 2 + 16;                 // bytes per staged row
-  constexpr bool STAGE = MOE_STAGED_EPI && !QOUT && C::BM * RSB <= C::LDS_BYTES;
+  constexpr bool STAGE = !QOUT && C::BM * RSB <= C::LDS_BYTES;
   if (STAGE) __builtin_amdgcn_s_barrier();
 #pragma unroll
   for (int i = 0; i < MS; ++i) {
@@ -917,16 +880,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, const WorkItem& it,
 }
 
 // Work distribution.  Block b runs on XCD b % 8 (the hardware deals blocks
-// round-robin over the XCDs).  Persistent mode: one block per CU takes items
-// of its XCD's equal-cost range from a per-XCD counter.  Otherwise: one block
-// per item, XCD x running the contiguous range [x*per, (x+1)*per) in order.
-// Either way siblings that share a weight slab or a row block run close
-// together on one L2, and an item's result does not depend on which block
-// computes it.
-#ifndef MOE_PERSISTENT
-#define MOE_PERSISTENT 1
-#endif
-
+// round-robin over the XCDs).  One block per CU takes items of its XCD's
+// equal-cost range from a per-XCD counter, so siblings that share a weight
+// slab or a row block run close together on one L2; an item's result does
+// not depend on which block computes it.
 
 template <bool GATED, bool MX, class C>
 __device__ __forceinline__ void gemm_item(const GemmArgs& g, int item, unsigned char* lds) {
@@ -956,7 +913,6 @@ __global__ __launch_bounds__(C::THREADS)
 __attribute__((amdgpu_waves_per_eu(C::WAVES * C::BLOCKS_PER_CU / 4))) void gemm_mfma_kernel(
     GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds[C::LDS_BYTES];
-#if MOE_PERSISTENT
   int& s_item = *reinterpret_cast<int*>(lds);  // LDS is idle between items
   const int x = blockIdx.x & 7;
   const int beg = g.hdr[kHdrStart + x], end = g.hdr[kHdrStart + x + 1];
@@ -976,11 +932,6 @@ __attribute__((amdgpu_waves_per_eu(C::WAVES * C::BLOCKS_PER_CU / 4))) void gemm_
     for (int i = 0; i < 8; ++i) atomicExch(&g.hdr[kHdrCtr + i], 0);
     atomicExch(&g.hdr[kHdrDone], 0);
   }
-#else
-  const int item = xcd_item(g.hdr[0]);
-  if (item < 0) return;
-  gemm_item<GATED, MX, C>(g, item, lds);
-#endif
 }
 
 // ---------------------------------------------------------------------------
@@ -1064,24 +1015,29 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgsF g) {
 
 inline int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 
-// persistent blocks: per compute unit, a multiple of the 8 XCDs
+// persistent blocks: per compute unit, a multiple of the 8 XCDs.  The CU
+// count of a device is read once and kept in an atomic (every thread that
+// races on the first call stores the same value)
 int persistent_grid(int per_cu) {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cached[dev] == 0) {
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
       cus = 256;
-    cached[dev] = (cus + 7) / 8 * 8;
+    n = (cus + 7) / 8 * 8;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev] * per_cu;
+  return n * per_cu;
 }
 
 template <bool GATED, bool MX, class C>
 void launch_mfma(const GemmArgs& g, int64_t cap, hipStream_t st) {
-  const int grid = MOE_PERSISTENT ? persistent_grid(C::BLOCKS_PER_CU) : (int)((cap + 7) / 8 * 8);
+  (void)cap;
+  const int grid = persistent_grid(C::BLOCKS_PER_CU);
   gemm_mfma_kernel<GATED, MX, C><<<grid, C::THREADS, 0, st>>>(g);
 }
 

@@ -8,6 +8,8 @@
 // aux-loss-free section; the article's BiasBalancedRouter), optional group
 // limit ("MoE industrial evolution", section 4), top-k with ties to the lower
 // expert index, renormalised gates.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -541,22 +543,32 @@ hipError_t launch_router_gemm(const moe_shape& s, const void* x, const float* w_
   return hipGetLastError();
 }
 
+template <int P>
+static void launch_topk_p(dim3 grid, hipStream_t st, const float* logits, int nparts,
+                          float* logits_out, const float* logit_add, bool logits_are_scores,
+                          const float* bias, float* scores_out, int32_t* topk_idx,
+                          float* topk_w, int T, const moe_shape& s) {
+  topk_kernel<P><<<grid, 256, 0, st>>>(logits, nparts, logits_out, logit_add,
+                                       logits_are_scores ? 1 : 0, bias, scores_out, topk_idx,
+                                       topk_w, T, s.n_experts, s.top_k, s.score_fn,
+                                       s.renormalize, s.n_groups, s.topk_groups);
+}
+
 hipError_t launch_topk(const moe_shape& s, const float* logits, int nparts, float* logits_out,
                        const float* logit_add, bool logits_are_scores, const float* bias,
                        float* scores_out, int32_t* topk_idx, float* topk_w, hipStream_t st) {
   const int T = (int)s.T, N = s.n_experts;
   dim3 grid((T + TK_WAVES - 1) / TK_WAVES);
   const int P = (N + 63) / 64;
-#define MOE_TOPK(PP)                                                                        \
-  topk_kernel<PP><<<grid, 256, 0, st>>>(logits, nparts, logits_out, logit_add,             \
-                                        logits_are_scores ? 1 : 0, bias,                   \
-                                        scores_out, topk_idx, topk_w, T, N, s.top_k,       \
-                                        s.score_fn, s.renormalize, s.n_groups, s.topk_groups)
-  if (P <= 1) MOE_TOPK(1);
-  else if (P <= 2) MOE_TOPK(2);
-  else if (P <= 4) MOE_TOPK(4);
-  else MOE_TOPK(8);
-#undef MOE_TOPK
+  auto run = [&](auto tag) {
+    launch_topk_p<decltype(tag)::value>(grid, st, logits, nparts, logits_out, logit_add,
+                                        logits_are_scores, bias, scores_out, topk_idx, topk_w,
+                                        T, s);
+  };
+  if (P <= 1) run(std::integral_constant<int, 1>());
+  else if (P <= 2) run(std::integral_constant<int, 2>());
+  else if (P <= 4) run(std::integral_constant<int, 4>());
+  else run(std::integral_constant<int, 8>());
   return hipGetLastError();
 }
 
