@@ -37,7 +37,8 @@
  *   - All tensor pointers are DEVICE pointers owned by the caller; the
  *     library never allocates or frees memory.  Scratch space is the
  *     caller's workspace `ws` of `ws_bytes` >= moe_workspace_bytes(shape),
- *     256-byte aligned.  Entry points that take a workspace use disjoint
+ *     256-byte aligned (moe_forward_noalloc alone uses a static device
+ *     array of the library instead).  Entry points that take a workspace use disjoint
  *     regions of the same layout, so one workspace serves every call of one
  *     shape; two calls sharing a workspace must not overlap in time.
  *   - Activation and weight pointers (x, w_router, w1, w2, w1_shared,
@@ -106,7 +107,9 @@ typedef enum moe_status {
   MOE_ERR_INVALID = 1,     /* null required pointer or inconsistent shape */
   MOE_ERR_UNSUPPORTED = 2, /* valid but outside what the kernels handle   */
   MOE_ERR_WORKSPACE = 3,   /* ws NULL or ws_bytes too small              */
-  MOE_ERR_HIP = 4          /* a kernel launch failed                      */
+  MOE_ERR_HIP = 4,         /* a kernel launch failed                      */
+  MOE_ERR_SCRATCH = 5      /* moe_forward_noalloc: the shape needs more
+                              scratch than MOE_NOALLOC_SCRATCH_BYTES       */
 } moe_status;
 
 enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
@@ -356,6 +359,33 @@ moe_status moe_forward(const moe_shape* shape, const void* x,
                        int32_t* counts, int32_t* offsets, int32_t* slot,
                        int32_t* n_kept_dropped, void* ws, size_t ws_bytes,
                        void* stream);
+
+/* moe_forward without a caller workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments, kernels and outputs as
+ * moe_forward (bitwise equal results), minus ws / ws_bytes: the scratch the
+ * layer needs (moe_workspace_bytes(shape) bytes) comes from a static device
+ * array of MOE_NOALLOC_SCRATCH_BYTES (64 MiB) that the library holds on every
+ * GPU it runs on until the process ends -- enough for decode-sized layers
+ * (e.g. 64 tokens, d_model 2048, 128 experts top-8, d_ff 768 takes about
+ * 5 MiB).  The call allocates nothing and never synchronises; its first
+ * call on a device looks up that device's array once (with the device
+ * current).  Every call on one GPU shares the array and leaves the last
+ * call's contents in it: calls that overlap in time on one GPU (two
+ * streams, or two host threads) race and give undefined results; calls
+ * ordered on one stream are safe.  Errors: those of moe_forward, and
+ * MOE_ERR_SCRATCH when moe_workspace_bytes(shape) exceeds the array
+ * (checked before anything is enqueued); MOE_ERR_HIP if the array's address
+ * cannot be obtained. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_forward_noalloc(const moe_shape* shape, const void* x,
+                               const float* w_router, const float* logit_add,
+                               const float* bias, const void* w1,
+                               const void* w2, const void* w1_shared,
+                               const void* w2_shared, void* y, float* scores_out,
+                               int32_t* topk_idx, float* topk_w,
+                               int32_t* counts, int32_t* offsets, int32_t* slot,
+                               int32_t* n_kept_dropped, void* stream);
 
 /* LatentMoE layer forward ("MoE common taste of open models", section 10:
  * the routed-expert path runs in a low-dimensional latent space -- the

@@ -12,7 +12,7 @@ argument order, tensors in place of pointers):
     moe_expert_down, moe_combine, moe_bias_update, moe_bias_update_seq,
     moe_router_stats, moe_router_stats_count, moe_route_ec, moe_combine_ec,
     moe_forward_ec, moe_ec_capacity, moe_quantize_mx, moe_latent_workspace_bytes,
-    moe_forward_latent, moe_forward,
+    moe_forward_latent, moe_forward, moe_forward_noalloc,
     moe_workspace_bytes, moe_check_shape, moe_capacity, moe_status_string,
     moe_abi_version
 
@@ -31,7 +31,9 @@ import torch  # loads the HIP runtime the library binds to
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
-MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP, \
+    MOE_ERR_SCRATCH = range(6)
+NOALLOC_SCRATCH_BYTES = 64 << 20  # the static scratch array of moe_forward_noalloc
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_DTYPE_F32, MOE_DTYPE_BF16, MOE_DTYPE_MXFP8 = 0, 1, 2
 MX_BLOCK = 32
@@ -135,6 +137,7 @@ _SIGS = {
                                       ctypes.c_size_t, _P]),
     "moe_forward": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                    _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_forward_noalloc": (ctypes.c_int, [_S] + [_P] * 17),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -498,6 +501,29 @@ def moe_forward(shape, x, w_router, logit_add, bias, w1, w2, w1_shared, w2_share
         _ptr(offsets, "offsets", torch.int32, N + 1), _ptr(slot, "slot", torch.int32, T * k),
         _ptr(n_kept_dropped, "n_kept_dropped", torch.int32, 2), p, n, _stream(stream))
     _check(st, "moe_forward")
+
+
+def moe_forward_noalloc(shape, x, w_router, logit_add, bias, w1, w2, w1_shared, w2_shared, y,
+                        scores_out, topk_idx, topk_w, counts, offsets, slot, n_kept_dropped,
+                        stream=None):
+    """moe_forward with the library's static scratch array instead of a
+    workspace (no allocation anywhere in the call)."""
+    T, N, k, d, f, fs = (shape.T, shape.n_experts, shape.top_k, shape.d_model, shape.d_ff,
+                         shape.d_ff_shared)
+    dt = _dt(shape)
+    st = lib().moe_forward_noalloc(
+        ctypes.byref(shape), _ptr(x, "x", dt, T * d),
+        _ptr(w_router, "w_router", torch.float32, N * d),
+        _ptr(logit_add, "logit_add", torch.float32, T * N),
+        _ptr(bias, "bias", torch.float32, N), _wptr(w1, "w1", shape, N * 2 * f * d),
+        _wptr(w2, "w2", shape, N * d * f), _wptr(w1_shared, "w1_shared", shape, 2 * fs * d),
+        _wptr(w2_shared, "w2_shared", shape, d * fs), _ptr(y, "y", dt, T * d),
+        _ptr(scores_out, "scores_out", torch.float32, T * N),
+        _ptr(topk_idx, "topk_idx", torch.int32, T * k),
+        _ptr(topk_w, "topk_w", torch.float32, T * k), _ptr(counts, "counts", torch.int32, N),
+        _ptr(offsets, "offsets", torch.int32, N + 1), _ptr(slot, "slot", torch.int32, T * k),
+        _ptr(n_kept_dropped, "n_kept_dropped", torch.int32, 2), _stream(stream))
+    _check(st, "moe_forward_noalloc")
 
 
 # ---- convenience ------------------------------------------------------------

@@ -2,6 +2,7 @@
 #include <math.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include "moe_internal.h"
 
@@ -184,6 +185,9 @@ const char* moe_status_string(moe_status st) {
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape outside the kernels' limits";
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing, misaligned or too small";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: kernel launch failed";
+    case MOE_ERR_SCRATCH:
+      return "MOE_ERR_SCRATCH: the shape needs more scratch than the static 64 MiB array of "
+             "moe_forward_noalloc";
   }
   return "MOE_ERR_UNKNOWN";
 }
@@ -487,12 +491,16 @@ moe_status moe_forward_ec(const moe_shape* shape, const void* x, const float* w_
   return hip_status(launch_ec_combine(sh, w.y_perm, shared ? w.y_shared : nullptr, ro, sc, y, s));
 }
 
-moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_router,
-                       const float* logit_add, const float* bias, const void* w1,
-                       const void* w2, const void* w1_shared, const void* w2_shared, void* y,
-                       float* scores_out, int32_t* topk_idx, float* topk_w, int32_t* counts,
-                       int32_t* offsets, int32_t* slot, int32_t* n_kept_dropped, void* ws,
-                       size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+// ---- the layer forward (moe_forward and moe_forward_noalloc) ----
+namespace {
+moe_status check_forward_args(const moe_shape* shape, const void* x, const float* w_router,
+                              const float* logit_add, const float* bias, const void* w1,
+                              const void* w2, const void* w1_shared, const void* w2_shared,
+                              void* y, float* scores_out, int32_t* topk_idx, float* topk_w,
+                              int32_t* counts, int32_t* offsets, int32_t* slot,
+                              int32_t* n_kept_dropped) {
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
   if (!x || !w_router || !w1 || !w2 || !y) return MOE_ERR_INVALID;
@@ -501,10 +509,15 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_rou
       !aligned4({logit_add, bias, scores_out, topk_idx, topk_w, counts, offsets, slot,
                  n_kept_dropped}))
     return MOE_ERR_INVALID;
-  Workspace w;
-  if ((st = check_ws(shape, ws, ws_bytes, w)) != MOE_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const moe_shape& sh = *shape;
+  return MOE_OK;
+}
+
+moe_status run_forward(const moe_shape& sh, const void* x, const float* w_router,
+                       const float* logit_add, const float* bias, const void* w1,
+                       const void* w2, const void* w1_shared, const void* w2_shared, void* y,
+                       float* scores_out, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                       int32_t* offsets, int32_t* slot, int32_t* n_kept_dropped,
+                       const Workspace& w, hipStream_t s) {
   float* sc = scores_out ? scores_out : w.scores;
   int32_t* ti = topk_idx ? topk_idx : w.topk_idx;
   float* tw = topk_w ? topk_w : w.topk_w;
@@ -527,6 +540,73 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_rou
     return MOE_ERR_HIP;
   return hip_status(
       launch_combine(sh, w.y_perm, shared ? w.y_shared : nullptr, sl, tw, y, s));
+}
+
+
+// The allocation-free forward's scratch: one static device array.  In host
+// code `noalloc_scratch_array` names a host-side stand-in, never a device
+// address: its device address is looked up once per device, with that device
+// current, and only that address is handed to kernels.
+constexpr size_t kNoallocScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char noalloc_scratch_array[kNoallocScratchBytes];
+
+hipError_t noalloc_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(noalloc_scratch_array));
+    if (e != hipSuccess) return e;
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 255)) return hipErrorInvalidValue;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+extern "C" {
+
+moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_router,
+                       const float* logit_add, const float* bias, const void* w1,
+                       const void* w2, const void* w1_shared, const void* w2_shared, void* y,
+                       float* scores_out, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                       int32_t* offsets, int32_t* slot, int32_t* n_kept_dropped, void* ws,
+                       size_t ws_bytes, void* stream) {
+  moe_status st = check_forward_args(shape, x, w_router, logit_add, bias, w1, w2, w1_shared,
+                                     w2_shared, y, scores_out, topk_idx, topk_w, counts,
+                                     offsets, slot, n_kept_dropped);
+  if (st != MOE_OK) return st;
+  Workspace w;
+  if ((st = check_ws(shape, ws, ws_bytes, w)) != MOE_OK) return st;
+  return run_forward(*shape, x, w_router, logit_add, bias, w1, w2, w1_shared, w2_shared, y,
+                     scores_out, topk_idx, topk_w, counts, offsets, slot, n_kept_dropped, w,
+                     static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_forward_noalloc(const moe_shape* shape, const void* x, const float* w_router,
+                               const float* logit_add, const float* bias, const void* w1,
+                               const void* w2, const void* w1_shared, const void* w2_shared,
+                               void* y, float* scores_out, int32_t* topk_idx, float* topk_w,
+                               int32_t* counts, int32_t* offsets, int32_t* slot,
+                               int32_t* n_kept_dropped, void* stream) {
+  moe_status st = check_forward_args(shape, x, w_router, logit_add, bias, w1, w2, w1_shared,
+                                     w2_shared, y, scores_out, topk_idx, topk_w, counts,
+                                     offsets, slot, n_kept_dropped);
+  if (st != MOE_OK) return st;
+  if (layout_workspace(*shape, nullptr).total > kNoallocScratchBytes) return MOE_ERR_SCRATCH;
+  void* base = nullptr;
+  if (noalloc_scratch(&base) != hipSuccess) return MOE_ERR_HIP;
+  const Workspace w = layout_workspace(*shape, base);
+  return run_forward(*shape, x, w_router, logit_add, bias, w1, w2, w1_shared, w2_shared, y,
+                     scores_out, topk_idx, topk_w, counts, offsets, slot, n_kept_dropped, w,
+                     static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

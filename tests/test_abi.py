@@ -48,7 +48,7 @@ def test_every_declared_symbol_is_exported(m):
 
 def test_abi_version_and_status_strings(m):
     assert m.moe_abi_version() == 1
-    for st in range(5):
+    for st in range(6):
         s = m.moe_status_string(st)
         assert s.startswith("MOE_")
     assert m.moe_status_string(99) == "MOE_ERR_UNKNOWN"
@@ -169,6 +169,33 @@ def test_invalid_arguments_fail_before_launch(m):
                                 None, ws_ok, big, None) == m.MOE_ERR_INVALID
     # the work-list builder needs the segment offsets
     assert L.moe_expert_plan(ctypes.byref(s), None, ws_ok, big, None) == m.MOE_ERR_INVALID
+
+
+def test_noalloc_forward_host_checks(m):
+    """The allocation-free forward validates like moe_forward and rejects a
+    shape whose scratch exceeds its static array before touching the GPU."""
+    L = m.lib()
+    P = ctypes.c_void_p
+    fake = P(4096)
+    s = shape()
+    assert m.moe_workspace_bytes(s) <= m.NOALLOC_SCRATCH_BYTES
+    big = shape(T=8192, d_model=7168, n_experts=256, top_k=8, d_ff=2048, d_ff_shared=2048,
+                n_groups=8, topk_groups=4)
+    assert m.moe_workspace_bytes(big) > m.NOALLOC_SCRATCH_BYTES
+    args = [fake, fake, None, None, fake, fake, None, None, fake] + [None] * 7
+    a = list(args); a[6] = a[7] = fake  # the shared expert's weights
+    assert L.moe_forward_noalloc(ctypes.byref(big), *a, None) == m.MOE_ERR_SCRATCH
+    assert m.moe_status_string(m.MOE_ERR_SCRATCH).startswith("MOE_ERR_SCRATCH")
+    # argument errors come first, as in moe_forward
+    a[0] = None
+    assert L.moe_forward_noalloc(ctypes.byref(big), *a, None) == m.MOE_ERR_INVALID
+    assert L.moe_forward_noalloc(ctypes.byref(shape(top_k=9)), *args, None) == \
+        m.MOE_ERR_INVALID
+    sh = shape(d_ff_shared=128)
+    assert L.moe_forward_noalloc(ctypes.byref(sh), *args, None) == m.MOE_ERR_INVALID
+    # the decode layer fits
+    dec = shape(T=64, d_model=2048, n_experts=128, top_k=8, d_ff=768)
+    assert m.moe_workspace_bytes(dec) < m.NOALLOC_SCRATCH_BYTES // 8
 
 
 def test_binding_rejects_cpu_tensors(m):
