@@ -18,6 +18,7 @@
 //          pre-drop counts; kept = min(count, C); offsets = exclusive scan
 //   place  pos = base + rank; slot / perm
 #include "moe_internal.h"
+#include "route_device.h"
 
 namespace moe {
 namespace {
@@ -129,73 +130,11 @@ __global__ __launch_bounds__(256) void place_kernel(const int32_t* __restrict__ 
   }
 }
 
-// the three steps in one block when all assignments fit one chunk (decode
-// batches): the chunk base positions are all zero, so the chunk's histogram
-// is the expert counts; same integer results as the three launches
 __global__ __launch_bounds__(kDispatchChunk) void dispatch_one_chunk_kernel(
     const int32_t* __restrict__ topk_idx, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ slot, int32_t* __restrict__ perm,
     int32_t* __restrict__ nkd, int A, int N, long long C) {
-  __shared__ int cnt[RK_WAVES][512];
-  __shared__ int sh[512];
-  __shared__ int off[512];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  for (int i = tid; i < RK_WAVES * 512; i += kDispatchChunk) (&cnt[0][0])[i] = 0;
-  __syncthreads();
-  const int a = tid;
-  int e = a < A ? topk_idx[a] : -1;
-  if (e >= N || e < 0) e = -1;
-  int r = 0;
-  bool last = true;
-  for (int j = 0; j < kWave; ++j) {
-    const int ej = __builtin_amdgcn_readlane(e, j);
-    if (ej == e) {
-      r += j < lane;
-      last = last && !(j > lane);
-    }
-  }
-  if (e >= 0 && last) cnt[wv][e] = r + 1;
-  __syncthreads();
-  int kept = 0;
-  if (tid < N) {
-    int run = 0;
-#pragma unroll
-    for (int w = 0; w < RK_WAVES; ++w) {
-      const int v = cnt[w][tid];
-      cnt[w][tid] = run;
-      run += v;
-    }
-    counts[tid] = run;
-    kept = C < 0 ? run : (int)min((long long)run, C);
-  }
-  sh[tid] = kept;
-  __syncthreads();
-  for (int o = 1; o < 512; o <<= 1) {
-    int v = tid >= o ? sh[tid - o] : 0;
-    __syncthreads();
-    sh[tid] += v;
-    __syncthreads();
-  }
-  off[tid] = sh[tid] - kept;
-  if (tid < N) offsets[tid] = sh[tid] - kept;
-  if (tid == 0) {
-    const int R = sh[511];
-    offsets[N] = R;
-    nkd[0] = R;
-    nkd[1] = A - R;
-  }
-  __syncthreads();
-  if (a < A) {
-    int sl = -1;
-    if (e >= 0) {
-      const int pos = cnt[wv][e] + r;
-      if (C < 0 || pos < C) {
-        sl = off[e] + pos;
-        perm[sl] = a;
-      }
-    }
-    slot[a] = sl;
-  }
+  dispatch_one_chunk(topk_idx, counts, offsets, slot, perm, nkd, A, N, C);
 }
 
 }  // namespace

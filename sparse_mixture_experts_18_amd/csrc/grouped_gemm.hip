@@ -28,6 +28,7 @@
 #include <type_traits>
 
 #include "moe_internal.h"
+#include "route_device.h"
 
 namespace moe {
 namespace {
@@ -39,254 +40,9 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 // ---------------------------------------------------------------------------
 // work-list construction
 // ---------------------------------------------------------------------------
-// exclusive prefix sums of two values over the block (blockDim.x a multiple
-// of 64, at most 1024): scans inside each wave with lane shuffles, then one
-// wave scans the wave totals; integer, so exact
-__device__ __forceinline__ void block_exclusive_scan2(int* sh0, int* sh1, int v0, int v1,
-                                                      int& ex0, int& ex1, int& tot0,
-                                                      int& tot1) {
-  const int i = threadIdx.x, lane = i & 63, w = i >> 6, nw = blockDim.x >> 6;
-  int a = v0, b = v1;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int ta = __shfl_up(a, o, 64), tb = __shfl_up(b, o, 64);
-    if (lane >= o) {
-      a += ta;
-      b += tb;
-    }
-  }
-  __syncthreads();  // the scratch may still be read by a previous call
-  if (lane == 63) {
-    sh0[w] = a;
-    sh1[w] = b;
-  }
-  __syncthreads();
-  if (w == 0) {
-    int ca = lane < nw ? sh0[lane] : 0, cb = lane < nw ? sh1[lane] : 0;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const int ta = __shfl_up(ca, o, 64), tb = __shfl_up(cb, o, 64);
-      if (lane >= o) {
-        ca += ta;
-        cb += tb;
-      }
-    }
-    if (lane < nw) {
-      sh0[32 + lane] = ca;  // inclusive wave prefixes
-      sh1[32 + lane] = cb;
-    }
-  }
-  __syncthreads();
-  const int pa = w ? sh0[32 + w - 1] : 0, pb = w ? sh1[32 + w - 1] : 0;
-  ex0 = pa + a - v0;
-  ex1 = pb + b - v1;
-  tot0 = sh0[32 + nw - 1];
-  tot1 = sh1[32 + nw - 1];
-}
-
-// Cost of an item for the XCD split: (live 32-row sub-tiles + a fixed part for
-// the weight slice every item streams) x k-slices.
-constexpr int kCostFixed = 2;
-
-// Work-list header (int32): [0] item count, [1..9] XCD range starts
-// (xcd x owns items [hdr[1+x], hdr[2+x])), [16..23] per-XCD item counters.
-constexpr int kHdrStart = 1, kHdrCtr = 16, kHdrDone = 24;  // header: 32 ints
-
-__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int N,
-                                                    int T, int has_shared, int bm1, int bm2,
-                                                    int nt1_r, int nt1_s, int nt2_r, int nt2_s,
-                                                    int k1_r, int k1_s, int k2_r, int k2_s,
-                                                    WorkItem* __restrict__ plan1,
-                                                    int32_t* __restrict__ hdr1,
-                                                    WorkItem* __restrict__ plan2,
-                                                    int32_t* __restrict__ hdr2, int deal) {
-  __shared__ int sh0[64], sh1[64];
-  __shared__ int st1s[1025], st2s[1025], mt1s[1024], mt2s[1024], rbases[1024], rowss[1024];
-  __shared__ long long ucost[1024];
-  __shared__ int uslot[1024];
-  const int s = threadIdx.x;
-  const int S = N + has_shared;
-  int rows = 0, rbase = 0, n1t = 0, n2t = 0;
-  if (s < N) {
-    rbase = offsets[s];
-    rows = offsets[s + 1] - rbase;
-    n1t = nt1_r;
-    n2t = nt2_r;
-  } else if (s < S) {
-    rows = T;
-    n1t = nt1_s;
-    n2t = nt2_s;
-  }
-  const int mt1 = (rows + bm1 - 1) / bm1, mt2 = (rows + bm2 - 1) / bm2;
-  int st1, st2, tot1, tot2;
-  block_exclusive_scan2(sh0, sh1, mt1 * n1t, mt2 * n2t, st1, st2, tot1, tot2);
-  st1s[s] = st1;
-  st2s[s] = st2;
-  mt1s[s] = mt1;
-  mt2s[s] = mt2;
-  rbases[s] = rbase;
-  rowss[s] = rows;
-  if (s == 0) {
-    st1s[1024] = tot1;
-    st2s[1024] = tot2;
-  }
-  __syncthreads();
-  {
-    const int pass = blockIdx.x;
-    const int* st = pass ? st2s : st1s;
-    const int* mts = pass ? mt2s : mt1s;
-    const int kr = (pass ? k2_r : k1_r) / 64, ks = (pass ? k2_s : k1_s) / 64;
-    WorkItem* plan = pass ? plan2 : plan1;
-    int32_t* hdr = pass ? hdr2 : hdr1;
-    const int tot = pass ? tot2 : tot1;
-    // Lists of routed experts on the wide tiles.  Units: each routed expert
-    // (all its column tiles) and each column tile of the shared expert.  A
-    // unit's cost is the sum of its items' costs (32-row sub-tiles plus a
-    // fixed part, times k-slices).  Units are ranked by cost (descending,
-    // ties by index) and dealt to the 8 XCDs in snake order (ranks 0..7 to
-    // XCDs 0..7, ranks 8..15 to XCDs 7..0, ...): every XCD gets the same
-    // total and a similar mix, and a unit never straddles two XCDs, so a
-    // list of about one item per CU leaves no CU with two.  Each XCD's range
-    // takes its units alternately from the large and the small end of its
-    // share (largest, smallest, second largest, ...), so compute-bound and
-    // weight-bound items run side by side; inside a unit, column tile then
-    // row block, so sibling row blocks of one weight slab are drawn in a
-    // row.  The small-row tiles stream the weights at a cost that hardly
-    // depends on the rows, so their lists keep the plain order and an
-    // equal-cost cut at item granularity.
-    const int nrt = pass ? nt2_r : nt1_r, nst = pass ? nt2_s : nt1_s;
-    const int U = N + (has_shared ? nst : 0);
-    if (deal && N > 0 && U <= 1016) {
-      long long c = -1;  // threads without a unit rank after every unit
-      int useg = 0, t0 = 0, t1 = 0;
-      if (s < U) {
-        useg = s < N ? s : N;
-        t0 = s < N ? 0 : s - N;
-        t1 = s < N ? nrt : t0 + 1;
-        const int R = rowss[useg], mt = mts[useg];
-        c = 0;
-        if (mt > 0) {
-          // row blocks as in the walk below: mt - 1 blocks of `part` rows
-          const int part = ((R + mt - 1) / mt + 31) / 32 * 32;
-          const long long sub = (long long)(mt - 1) * (part / 32) + (R - (mt - 1) * part + 31) / 32;
-          c = (long long)(t1 - t0) * (sub + (long long)kCostFixed * mt) * (useg < N ? kr : ks);
-        }
-      }
-      ucost[s] = c;
-      uslot[s] = -1;
-      __syncthreads();
-      const int R8 = (U + 7) >> 3;
-      if (s < U) {
-        int rank = 0;
-        for (int v = 0; v < U; ++v) {
-          const long long cv = ucost[v];
-          rank += (cv > c) || (cv == c && v < s);
-        }
-        const int rd = rank >> 3, p = rank & 7;
-        const int x = (rd & 1) ? 7 - p : p;
-        // position of round rd in the XCD's order 0, R8-1, 1, R8-2, ...
-        const int j = rd <= (R8 - 1) / 2 ? 2 * rd : 2 * (R8 - 1 - rd) + 1;
-        uslot[x * R8 + j] = s;
-      }
-      __syncthreads();
-      // thread q lays out slot q: XCD q / R8, position q % R8
-      const int u = uslot[s];
-      int useg2 = 0, u0 = 0, u1 = 0, mt = 0;
-      if (u >= 0) {
-        useg2 = u < N ? u : N;
-        u0 = u < N ? 0 : u - N;
-        u1 = u < N ? nrt : u0 + 1;
-        mt = mts[useg2];
-      }
-      int base, dummy_ex, total, dummy_tot;
-      block_exclusive_scan2(sh0, sh1, mt * (u1 - u0), 0, base, dummy_ex, total, dummy_tot);
-      if (s == 0) {
-        hdr[0] = total;
-        hdr[kHdrStart + 8] = total;
-        for (int x = 0; x < 8; ++x) hdr[kHdrCtr + x] = 0;
-        hdr[kHdrDone] = 0;
-      }
-      if (s < 8 * R8 && s % R8 == 0) hdr[kHdrStart + s / R8] = base;
-      if (u >= 0 && mt > 0) {
-        const int R = rowss[useg2];
-        const int part = ((R + mt - 1) / mt + 31) / 32 * 32;
-        int i = base;
-        for (int nt = u0; nt < u1; ++nt)
-          for (int m = 0; m < mt; ++m)
-            plan[i++] = WorkItem{useg2, rbases[useg2] + m * part, min(part, R - m * part), nt};
-      }
-      return;
-    }
-    // Otherwise (one-segment dense lists): items in segment-major, then column
-    // tile, then row block order.  Thread s fills a contiguous chunk of the
-    // list; the list is then cut into 8 ranges of equal cost, one per XCD.
-    const int chunk = (tot + 1023) / 1024;
-    const int i0 = min(tot, s * chunk), i1 = min(tot, i0 + chunk);
-    // segment of item i0: the last segment with st[seg] <= i0 (empty ones skipped)
-    int seg0 = 0;
-    {
-      int lo = 0, hi = 1023;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (st[mid] <= i0) lo = mid;
-        else hi = mid - 1;
-      }
-      seg0 = lo;
-    }
-    // walk the chunk: (segment, column tile, row block) advance incrementally
-    auto walk = [&](auto&& visit) {
-      int seg = seg0;
-      int loc = i0 - st[seg];
-      int mt = max(mts[seg], 1);
-      int m = loc % mt, nt = loc / mt;
-      for (int i = i0; i < i1; ++i) {
-        while (i >= st[seg + 1]) {  // next non-empty segment
-          ++seg;
-          mt = max(mts[seg], 1);
-          m = 0;
-          nt = 0;
-        }
-        // a segment's rows are cut into mt near-equal, 32-aligned row blocks,
-        // so the row blocks that share a weight slab run at the same pace
-        const int part = ((rowss[seg] + mt - 1) / mt + 31) / 32 * 32;
-        const int nr = min(part, rowss[seg] - m * part);
-        const int cost = (((nr + 31) >> 5) + kCostFixed) * (seg < N ? kr : ks);
-        visit(i, WorkItem{seg, rbases[seg] + m * part, nr, nt}, cost);
-        if (++m == mt) {
-          m = 0;
-          ++nt;
-        }
-      }
-    };
-    int local = 0;
-    walk([&](int i, const WorkItem& it, int c) {
-      plan[i] = it;
-      local += c;
-    });
-    int pre, dummy_ex, total, dummy_tot;
-    block_exclusive_scan2(sh0, sh1, local, 0, pre, dummy_ex, total, dummy_tot);
-    // boundary x = first item i with 8 * cost(items < i) >= x * total
-    if (s == 0) {
-      hdr[0] = tot;
-      hdr[kHdrStart] = 0;
-      hdr[kHdrStart + 8] = tot;
-      for (int x = 0; x < 8; ++x) hdr[kHdrCtr + x] = 0;
-      hdr[kHdrDone] = 0;
-      if (total == 0)
-        for (int x = 1; x < 8; ++x) hdr[kHdrStart + x] = 0;
-    }
-    if (total > 0) {
-      long long cum = pre;
-      walk([&](int i, const WorkItem&, int c) {
-        for (int x = 1; x < 8; ++x) {
-          const long long tgt = (long long)x * total;
-          if (8 * cum < tgt && tgt <= 8 * (cum + c)) hdr[kHdrStart + x] = i + 1;
-        }
-        cum += c;
-      });
-    }
-  }
-}
+// The two work lists of an expert projection pair (one block per list), or
+// the one or two lists of dense products.
+__global__ __launch_bounds__(1024) void plan_kernel(PlanArgs a) { plan_device(a, blockIdx.x); }
 
 // Non-persistent item index (fp32 path): block b runs on XCD b % 8; XCD x takes
 // the contiguous range [x*per, (x+1)*per).  -1 for blocks without work.
@@ -592,9 +348,13 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, const WorkItem& it,
   auto issue_b = [&](int kt) {
     unsigned char* st = Bbuf + (kt % SB) * C::B_BYTES;
     const uint32_t k0 = kt * C::ROWB;
+    // small-row tiles (one 32-row sub-tile per wave) read each weight byte
+    // about once: load the weights as streaming data so that they leave L2
+    // and the MALL before the activations and the work lists
+    constexpr int aux = C::MSW == 1 ? kNonTemporal : 0;
 #pragma unroll
     for (int j = 0; j < C::B_LOADS; ++j)
-      dma16(rb, b_off[j], k0, st + (w * C::B_LOADS + j) * 1024);
+      dma16<aux>(rb, b_off[j], k0, st + (w * C::B_LOADS + j) * 1024);
   };
 
 
@@ -910,7 +670,7 @@ __device__ __forceinline__ void gemm_item(const GemmArgs& g, int item, unsigned 
 
 template <bool GATED, bool MX, class C>
 __global__ __launch_bounds__(C::THREADS)
-__attribute__((amdgpu_waves_per_eu(C::WAVES * C::BLOCKS_PER_CU / 4))) void gemm_mfma_kernel(
+__attribute__((amdgpu_waves_per_eu(C::WAVES * C::BLOCKS_PER_CU / 4 > 0 ? C::WAVES * C::BLOCKS_PER_CU / 4 : 1))) void gemm_mfma_kernel(
     GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds[C::LDS_BYTES];
   int& s_item = *reinterpret_cast<int*>(lds);  // LDS is idle between items
@@ -1088,14 +848,17 @@ PlanGeom plan_geom(const moe_shape& s) {
 
 }  // namespace
 
+PlanArgs plan_args(const moe_shape& s, const int32_t* offsets, const Workspace& w) {
+  const int fs = s.d_ff_shared;
+  const PlanGeom pg = plan_geom(s);
+  return PlanArgs{offsets, s.n_experts, (int)s.T, fs > 0 ? 1 : 0, pg.bm1, pg.bm2, pg.nt1_r,
+                  pg.nt1_s, pg.nt2_r, pg.nt2_s, s.d_model, s.d_model, s.d_ff, fs > 0 ? fs : 64,
+                  w.plan1, w.plan1_hdr, w.plan2, w.plan2_hdr, narrow_tiles(s) ? 0 : 1};
+}
+
 hipError_t launch_plan(const moe_shape& s, const int32_t* offsets, const Workspace& w,
                        hipStream_t st) {
-  const int fs = s.d_ff_shared;
-  PlanGeom pg = plan_geom(s);
-  plan_kernel<<<2, 1024, 0, st>>>(offsets, s.n_experts, (int)s.T, fs > 0 ? 1 : 0, pg.bm1,
-                                  pg.bm2, pg.nt1_r, pg.nt1_s, pg.nt2_r, pg.nt2_s, s.d_model,
-                                  s.d_model, s.d_ff, fs > 0 ? fs : 64, w.plan1, w.plan1_hdr,
-                                  w.plan2, w.plan2_hdr, narrow_tiles(s) ? 0 : 1);
+  plan_kernel<<<2, 1024, 0, st>>>(plan_args(s, offsets, w));
   return hipGetLastError();
 }
 
@@ -1191,8 +954,9 @@ hipError_t launch_dense_plan(const moe_shape& s, bool gated1, int K1, int Nout1,
   const int bm = dense_bm(s);
   const int n1 = cdiv(Nout1, dense_bn(s, gated1));
   const int n2 = p2 ? cdiv(Nout2, dense_bn(s, false)) : 0;
-  plan_kernel<<<p2 ? 2 : 1, 1024, 0, st>>>(nullptr, 0, (int)s.T, 1, bm, bm, 0, n1, 0, n2, K1,
-                                           K1, p2 ? K2 : 64, p2 ? K2 : 64, p1, h1, p2, h2, 0);
+  plan_kernel<<<p2 ? 2 : 1, 1024, 0, st>>>(PlanArgs{nullptr, 0, (int)s.T, 1, bm, bm, 0, n1, 0,
+                                                    n2, K1, K1, p2 ? K2 : 64, p2 ? K2 : 64, p1,
+                                                    h1, p2, h2, 0});
   return hipGetLastError();
 }
 

@@ -195,10 +195,13 @@ __device__ __forceinline__ rsrc_t make_rsrc(const unsigned char* base,
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(base), (short)0,
                                            (int)bytes, 0x00020000);
 }
+// cache-policy bits of a buffer load (the aux operand): nt, streaming data
+constexpr int kNonTemporal = 2;
+template <int AUX = 0>
 __device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff,
                                       unsigned char* lds_wave_base) {
   typedef __attribute__((address_space(3))) void* lptr_t;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lptr_t)(lds_wave_base), 16, voff, soff, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lptr_t)(lds_wave_base), 16, voff, soff, 0, AUX);
 }
 
 // wait until at most n vector-memory ops of this wave are outstanding (they

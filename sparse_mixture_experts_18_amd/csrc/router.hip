@@ -11,6 +11,7 @@
 #include <type_traits>
 
 #include "moe_internal.h"
+#include "route_device.h"
 
 namespace moe {
 namespace {
@@ -197,6 +198,115 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const bf16_t* __restri
   }
 }
 
+// Small batches: one block per 32 x 32 tile of logits and 512-wide k-chunk
+// (the k split), reading the fp32 router weights directly.  The block loads
+// the chunk's x rows (32 KiB) and fp32 weights (64 KiB) in one round of
+// 16-byte loads, forms the three bf16 parts of each weight with the same
+// arithmetic as split3_kernel, and waves 0, 1, 2 each run the MFMA chain of
+// one part over the chunk's k-steps in order -- the three accumulators of
+// router_mfma_kernel, computed side by side -- so the partial planes are bit
+// for bit the ones of the other router kernels.
+constexpr int RS_T = 32;  // tile rows and columns
+__global__ __launch_bounds__(256) void router_small_kernel(const bf16_t* __restrict__ x,
+                                                           const float* __restrict__ w,
+                                                           float* __restrict__ out, int T,
+                                                           int N, int d) {
+  constexpr int SLW = RM_KC / 64;  // 64-wide slices per chunk
+  __shared__ __attribute__((aligned(16))) unsigned char As[SLW][RS_T * 128];
+  __shared__ __attribute__((aligned(16))) unsigned char Bs[3][SLW][RS_T * 128];
+  __shared__ __attribute__((aligned(16))) float red[2][RS_T * RS_T];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int m0 = blockIdx.x * RS_T, n0 = blockIdx.y * RS_T;
+  const int c = blockIdx.z;
+  const int k0 = c * RM_KC;
+  const int nsl = min(SLW, (d - k0) / 64);  // 64-wide slices in this chunk (d % 64 == 0)
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  // coalesced loads: load i of thread t takes 16-byte chunk i * 256 + t of the
+  // tile (x: 32 rows x 64 chunks of 8 bf16; weights: 32 rows x 128 chunks of
+  // 4 fp32), so a wave reads 1 KiB of one row per instruction
+  u32x4_t xa[8];
+  f32x4_t wb[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int g = i * 256 + tid, r = g >> 6, ch = g & 63;
+    const bf16_t* xp = x + (size_t)min(m0 + r, T - 1) * d + k0;
+    xa[i] = ch / 8 < nsl ? *reinterpret_cast<const u32x4_t*>(xp + ch * 8) : u32x4_t{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int g = i * 256 + tid, r = g >> 7, ch = g & 127;
+    const float* wp = w + (size_t)min(n0 + r, N - 1) * d + k0;
+    wb[i] = ch / 16 < nsl ? *reinterpret_cast<const f32x4_t*>(wp + ch * 4) : f32x4_t{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int g = i * 256 + tid, r = g >> 6, ch = g & 63, sl = ch / 8, c8 = ch % 8;
+    *reinterpret_cast<u32x4_t*>(&As[sl][r * 128 + ((c8 ^ rswz(r)) << 4)]) = xa[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int g = i * 256 + tid, r = g >> 7, ch = g & 127;
+    const int sl = ch / 16, c16 = ch % 16;  // half of a 16-byte bf16 chunk
+    const int pos = (((c16 >> 1) ^ rswz(r)) << 4) + (c16 & 1) * 8;
+    uint32_t h[3][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      uint32_t part[3][2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float v = wb[i][2 * u + e];
+        const bf16_t h1 = f32_to_bf16(v);
+        const float r1 = v - bf16_to_f32(h1);
+        const bf16_t h2 = f32_to_bf16(r1);
+        const float r2 = r1 - bf16_to_f32(h2);
+        part[0][e] = h1;
+        part[1][e] = h2;
+        part[2][e] = f32_to_bf16(r2);
+      }
+#pragma unroll
+      for (int t = 0; t < 3; ++t) h[t][u] = part[t][0] | (part[t][1] << 16);
+    }
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+      *reinterpret_cast<uint2*>(&Bs[t][sl][r * 128 + pos]) = make_uint2(h[t][0], h[t][1]);
+  }
+  __syncthreads();
+  const int fr = lane & 31, fh = lane >> 5;
+  f32x16_t acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  if (wv < 3) {
+    for (int sl = 0; sl < nsl; ++sl) {
+#pragma unroll
+      for (int ks = 0; ks < RM_BK / 16; ++ks) {
+        const int ch = 2 * ks + fh;
+        const bf16x8_t af =
+            *reinterpret_cast<const bf16x8_t*>(&As[sl][fr * 128 + ((ch ^ rswz(fr)) << 4)]);
+        const bf16x8_t bf =
+            *reinterpret_cast<const bf16x8_t*>(&Bs[wv][sl][fr * 128 + ((ch ^ rswz(fr)) << 4)]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc, 0, 0, 0);
+      }
+    }
+  }
+  // parts 1 and 2 to LDS, part 0's wave adds them smallest first
+  if (wv == 1 || wv == 2) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) red[wv - 1][i * 64 + lane] = acc[i];
+  }
+  __syncthreads();
+  if (wv == 0) {
+    float* o = out + (size_t)c * T * N;
+    const int col = n0 + fr;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = m0 + 8 * (i >> 2) + 4 * fh + (i & 3);
+      const float p = (red[1][i * 64 + lane] + red[0][i * 64 + lane]) + acc[i];
+      if (row < T && col < N) o[(size_t)row * N + col] = p;
+    }
+  }
+}
+
 // The same product for batches that take no k split: 128 tokens x 64
 // experts per block, eight waves of 32 x 32 (x the three planes), k-slices of
 // 64 through a four-stage LDS ring filled by direct DMA (two slices in
@@ -307,196 +417,19 @@ __global__ __launch_bounds__(512) void router_mfma2_kernel(const bf16_t* __restr
 // K2: one wavefront per token.  Lane l holds experts [l*P, l*P+P).
 // ---------------------------------------------------------------------------
 
-// total order used for selection: NaN lowest, -0 == +0; 0 is reserved for
-// "not a candidate"
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 1u;  // NaN
-  if (u == 0x80000000u) u = 0u;
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return u + 1u;
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-constexpr int TK_WAVES = 4;
-
 template <int P>
 __global__ __launch_bounds__(256) void topk_kernel(
     const float* __restrict__ logits, int nparts, float* __restrict__ logits_out,
-    const float* __restrict__ logit_add,
-    int logits_are_scores, const float* __restrict__ bias, float* __restrict__ scores_out,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int T, int N, int k,
-    int score_fn, int renorm, int n_groups, int topk_groups) {
+    const float* __restrict__ logit_add, int logits_are_scores, const float* __restrict__ bias,
+    float* __restrict__ scores_out, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    int T, int N, int k, int score_fn, int renorm, int n_groups, int topk_groups) {
   __shared__ float keys_lds[TK_WAVES][512];
   __shared__ float gsc[TK_WAVES][64];
   __shared__ int gsel[TK_WAVES][64];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int t_raw = blockIdx.x * TK_WAVES + wv;
-  const bool valid = t_raw < T;  // tail waves compute on token T-1, write nothing
-  const int t = valid ? t_raw : T - 1;
-  const float* lrow = logits + (size_t)t * N;
-  float s[P];
-  uint32_t ok[P];
-#pragma unroll
-  for (int p = 0; p < P; ++p) {
-    int e = lane * P + p;
-    float v = -INFINITY;
-    if (e < N) {
-      v = lrow[e];
-      // partial sums of a k-split router GEMM: added in chunk order, the
-      // order a single pass over the chunks uses
-      for (int c = 1; c < nparts; ++c) v += lrow[(size_t)c * T * N + e];
-      if (logits_out && valid) logits_out[(size_t)t * N + e] = v;
-      if (logit_add && !logits_are_scores) v += logit_add[(size_t)t * N + e];
-    }
-    s[p] = v;
-  }
-  if (!logits_are_scores) {
-    if (score_fn == MOE_SCORE_SOFTMAX) {
-      float m = s[0];
-#pragma unroll
-      for (int p = 1; p < P; ++p) m = fmaxf(m, s[p]);
-      m = wave_max(m);
-      float sum = 0.f;
-#pragma unroll
-      for (int p = 0; p < P; ++p) {
-        int e = lane * P + p;
-        s[p] = e < N ? expf(s[p] - m) : 0.f;
-        sum += s[p];
-      }
-      sum = wave_sum(sum);
-      const float inv = 1.0f / sum;
-#pragma unroll
-      for (int p = 0; p < P; ++p) s[p] = s[p] * inv;
-    } else {
-#pragma unroll
-      for (int p = 0; p < P; ++p) s[p] = 1.0f / (1.0f + expf(-s[p]));
-    }
-  }
-#pragma unroll
-  for (int p = 0; p < P; ++p) {
-    int e = lane * P + p;
-    if (e < N) {
-      if (scores_out && valid) scores_out[(size_t)t * N + e] = s[p];
-      float key = bias ? s[p] + bias[e] : s[p];
-      ok[p] = order_key(key);
-      keys_lds[wv][e] = key;
-    } else {
-      ok[p] = 0u;
-    }
-  }
-  if (n_groups > 1) {  // uniform across the block
-    // group score: fl32 sum of the best m keys of the group, best first
-    const int gsz = N / n_groups, m = k / topk_groups;
-    __syncthreads();
-    if (lane < n_groups) {
-      const float* gk = &keys_lds[wv][lane * gsz];
-      float acc = 0.f;
-      uint32_t prev_o = 0xffffffffu;
-      int prev_i = -1;
-      for (int r = 0; r < m; ++r) {
-        // next key after (prev_o, prev_i) in the order (key desc, index asc)
-        uint32_t bo = 0u;
-        int bi = -1;
-        float bv = 0.f;
-        for (int i = 0; i < gsz; ++i) {
-          uint32_t o = order_key(gk[i]);
-          bool after = (o < prev_o) || (o == prev_o && i > prev_i);
-          if (after && (bi < 0 || o > bo)) {
-            bo = o;
-            bi = i;
-            bv = gk[i];
-          }
-        }
-        acc = (r == 0) ? bv : acc + bv;
-        prev_o = bo;
-        prev_i = bi;
-      }
-      gsc[wv][lane] = acc;
-    }
-    __syncthreads();
-    if (lane < n_groups) {
-      uint32_t mine = order_key(gsc[wv][lane]);
-      int rank = 0;
-      for (int g = 0; g < n_groups; ++g) {
-        uint32_t o = order_key(gsc[wv][g]);
-        rank += (o > mine) || (o == mine && g < lane);
-      }
-      gsel[wv][lane] = rank < topk_groups;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-      int e = lane * P + p;
-      if (e < N && !gsel[wv][e / gsz]) ok[p] = 0u;
-    }
-  }
-  // Selection: the k largest (key, -index) pairs among the candidates
-  // (ok > 0; a valid shape has at least k).  tau, the k-th largest order key,
-  // is found bit by bit from wave ballots; every key above tau is taken, then
-  // the ties at tau in ascending expert order.  Lane j then receives the pick
-  // of rank j (key descending, index ascending): the order in which k rounds
-  // of arg-max would take them.
-  uint32_t tau = 0;
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t cand = tau | (1u << b);
-    int cnt = 0;
-#pragma unroll
-    for (int p = 0; p < P; ++p) cnt += __popcll(__ballot(ok[p] >= cand));
-    if (cnt >= k) tau = cand;
-  }
-  int need = k;  // ties at tau to take
-  int below = 0;  // ties at tau in the lanes below this one
-#pragma unroll
-  for (int p = 0; p < P; ++p) {
-    need -= __popcll(__ballot(ok[p] > tau));
-    const uint64_t tm = __ballot(ok[p] == tau);
-    below += __builtin_amdgcn_mbcnt_hi((uint32_t)(tm >> 32),
-                                       __builtin_amdgcn_mbcnt_lo((uint32_t)tm, 0u));
-  }
-  uint64_t selm[P];
-#pragma unroll
-  for (int p = 0; p < P; ++p) {
-    const bool tie = ok[p] == tau;
-    selm[p] = __ballot(ok[p] > tau || (tie && below < need));
-    below += tie;
-  }
-  int my_e = 0;
-  float my_s = 0.f;
-#pragma unroll
-  for (int p = 0; p < P; ++p) {
-    for (uint64_t m = selm[p]; m; m &= m - 1) {
-      const int l = __builtin_ctzll(m);
-      const uint32_t okm = __builtin_amdgcn_readlane(ok[p], l);
-      const float sm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s[p]), l));
-      const int em = l * P + p;
-      int rank = 0;
-#pragma unroll
-      for (int q = 0; q < P; ++q)
-        rank += __popcll(__ballot(ok[q] > okm || (ok[q] == okm && lane * P + q < em)));
-      if (lane == rank) {
-        my_e = em;
-        my_s = sm;
-      }
-    }
-  }
-  // renormalise: fp32 sum in ascending j
-  float sum = 0.f;
-  for (int j = 0; j < k; ++j)
-    sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), j));
-  if (valid && lane < k) {
-    topk_idx[(size_t)t * k + lane] = my_e;
-    topk_w[(size_t)t * k + lane] = renorm ? my_s / sum : my_s;
-  }
+  const int wv = threadIdx.x >> 6;
+  topk_token<P>(blockIdx.x * TK_WAVES + wv, keys_lds[wv], gsc[wv], gsel[wv], logits, nparts,
+                logits_out, logit_add, logits_are_scores, bias, scores_out, topk_idx, topk_w,
+                T, N, k, score_fn, renorm, n_groups, topk_groups);
 }
 
 }  // namespace
@@ -518,14 +451,16 @@ hipError_t launch_router_gemm(const moe_shape& s, const void* x, const float* w_
   *nparts = 1;
   if (act_bf16(s)) {
     const long long n = (long long)N * d;
-    split3_kernel<<<(int)min((n + 255) / 256, 2048LL), 256, 0, st>>>(w_router, w.wsplit, n);
     const int nkc = router_split_chunks(s);
     if (nkc) {
-      dim3 grid((T + RM_BM - 1) / RM_BM, (N + RM_BN - 1) / RM_BN, nkc);
-      router_mfma_kernel<<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(x), w.wsplit,
-                                               w.router_part, T, N, d, 1);
+      dim3 grid((T + RS_T - 1) / RS_T, (N + RS_T - 1) / RS_T, nkc);
+      router_small_kernel<<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(x), w_router,
+                                                w.router_part, T, N, d);
       *nparts = nkc;
-    } else if ((size_t)T * d * 2 < (1ull << 31) && (size_t)3 * N * d * 2 < (1ull << 31)) {
+      return hipGetLastError();
+    }
+    split3_kernel<<<(int)min((n + 255) / 256, 2048LL), 256, 0, st>>>(w_router, w.wsplit, n);
+    if ((size_t)T * d * 2 < (1ull << 31) && (size_t)3 * N * d * 2 < (1ull << 31)) {
       // (32-bit buffer offsets)
       const int Q = ((T + R2_BM - 1) / R2_BM) * ((N + R2_BN - 1) / R2_BN);
       router_mfma2_kernel<<<8 * ((Q + 7) / 8), 512, 0, st>>>(static_cast<const bf16_t*>(x),
