@@ -1,13 +1,15 @@
 """MoE FFN layer forward benchmark on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config dsv3]
+                    [--configs tiny,mixtral,decode,switch]
 
 One step = one full layer forward (router GEMM, scores + top-k, dispatch,
 grouped SwiGLU expert GEMMs incl. the shared expert, combine) over one batch
-of synthetic, seeded inputs already resident in HBM.  The steps are timed
-twice, launched eagerly and as replays of one HIP graph of the step; the
-faster of the two is the reported rate (both are in the line).  Prints ONE
-JSON line.
+of synthetic, seeded inputs already resident in HBM.  The steps of the
+headline workload (--config) are timed twice, launched eagerly and as replays
+of one HIP graph of the step; the faster of the two is the reported rate
+(both are in the line), and each replay is also timed on its own for the
+median and the 10th/90th percentiles.  Prints ONE JSON line.
 
 Extra fields beside the contract's:
   roofline      the dominant kernel, the gate/up grouped GEMM with the SwiGLU
@@ -25,6 +27,14 @@ Extra fields beside the contract's:
   latent        the LatentMoE variant of the layer at latent width d/4
   ep8_share     the expert FFNs at one GPU's share under 8-way expert
                 parallelism (N/8 experts, k*T rows spread evenly over them)
+  configs       the other workloads (--configs), each with the per-step
+                median / p10 / p90 of its graph-replayed forward, tokens/s,
+                TFLOP/s, the layer against its roofline, the same gate/up
+                roofline object and a cpu_baseline of its own.  Decode and
+                switch steps each follow a 512 MiB read that evicts the
+                last-level cache (their expert weights would otherwise stay
+                in it from one step to the next), and decode takes at least
+                500 timed steps.
 """
 from __future__ import annotations
 
@@ -50,8 +60,12 @@ def parse():
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", default="dsv3")
-    p.add_argument("--cpu-sample-tokens", type=int, default=64,
-                   help="tokens of the batch the oracle runs on (about 10 s on the host)")
+    p.add_argument("--configs", default="tiny,mixtral,decode,switch",
+                   help="comma list of further workloads measured after --config "
+                        "('' for none)")
+    p.add_argument("--cpu-sample-tokens", type=int, default=0,
+                   help="tokens of the batch the oracle runs on (0: the workload's default, "
+                        "about 10 s on the host)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--stage-iters", type=int, default=10)
     p.add_argument("--skip", default="",
@@ -93,11 +107,21 @@ def committed_traffic(workload: str):
         return None
 
 
-def cpu_baseline(cfg, inp, n_tokens: int) -> dict:
+# tokens of each workload's batch the oracle runs on (run again until 10 s of host
+# work have passed), the workloads whose steps follow a last-level-cache eviction,
+# and the fewest timed steps per workload
+CPU_SAMPLE = {"tiny": 64, "mixtral": 8, "decode": 64, "switch": 256, "dsv3": 64}
+STEP_FLUSH = {"decode", "switch"}
+MIN_STEPS = {"tiny": 500, "decode": 500, "switch": 200, "mixtral": 50}
+
+
+def cpu_baseline(cfg, inp, n_tokens: int, min_seconds: float = 10.0) -> dict:
     """The fp64 oracle, as it stands, on the first n_tokens tokens of the
     batch: router, scores, selection, dispatch, expert FFNs of every expert
-    those tokens touch, shared expert, combine.  Weights are copied to host
-    before the clock starts (exact fp32 copies of the bf16 values)."""
+    those tokens touch, shared expert, combine (a capacity, if any, follows
+    the sample's own token count).  Weights are copied to host before the
+    clock starts (exact fp32 copies of the bf16 values); the layer is run
+    again until min_seconds have passed."""
     import numpy as np
     import threadpoolctl
     import torch
@@ -127,19 +151,255 @@ def cpu_baseline(cfg, inp, n_tokens: int) -> dict:
     torch.cuda.synchronize()
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
+    runs = 0
     t0 = time.perf_counter()
-    oracle.moe_layer(x, wr, lambda e: (wcache[e][0].float().numpy(),
-                                       wcache[e][1].float().numpy()), None, top_k=cfg.top_k,
-                     score_fn=cfg.score_fn, renormalize=cfg.renormalize,
-                     n_groups=cfg.n_groups, topk_groups=cfg.topk_groups,
-                     capacity_factor=cfg.capacity_factor, capacity_rule=cfg.capacity_rule,
-                     bias=bias, logit_add=la, w1_shared=w1s, w2_shared=w2s)
-    dt = time.perf_counter() - t0
-    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": (f"first {n_tokens} tokens of the {cfg.name} batch: full fp64 layer "
-                       f"(router over all {cfg.n_experts} experts, {len(touched)} touched "
-                       f"experts, shared expert); {dt:.2f} s wall"),
+    while True:
+        oracle.moe_layer(x, wr, lambda e: (wcache[e][0].float().numpy(),
+                                           wcache[e][1].float().numpy()), None,
+                         top_k=cfg.top_k, score_fn=cfg.score_fn, renormalize=cfg.renormalize,
+                         n_groups=cfg.n_groups, topk_groups=cfg.topk_groups,
+                         capacity_factor=cfg.capacity_factor, capacity_rule=cfg.capacity_rule,
+                         bias=bias, logit_add=la, w1_shared=w1s, w2_shared=w2s)
+        runs += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    return {"value": round(n_tokens * runs / dt, 3), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"first {n_tokens} tokens of the {cfg.name} batch, {runs} run(s): full "
+                       f"fp64 layer (router over all {cfg.n_experts} experts, {len(touched)} "
+                       f"touched experts{', shared expert' if cfg.d_ff_shared else ''}); "
+                       f"{dt:.2f} s wall"),
             "blas": ",".join(sorted({i.get("internal_api", "?") for i in info}))}
+
+
+def quantiles(ts) -> dict:
+    t = sorted(ts)
+    q = lambda f: t[min(len(t) - 1, int(round(f * (len(t) - 1))))]
+    return {"median": round(q(0.5), 4), "p10": round(q(0.1), 4), "p90": round(q(0.9), 4)}
+
+
+class Timer:
+    """HIP-event timing on the stream the library launches on (torch's
+    current stream).  evict() reads 512 MiB, twice the 256 MiB last-level
+    cache (reads only: no dirty lines left to write back)."""
+
+    def __init__(self, torch, dev):
+        self.torch = torch
+        self.stream = torch.cuda.current_stream()
+        self.flush = torch.ones(64 << 20, dtype=torch.float64, device=dev)
+        self.sink = torch.empty((), dtype=torch.float64, device=dev)
+
+    def evict(self):
+        self.torch.sum(self.flush, dim=0, out=self.sink)
+
+    def each(self, fn, iters, evict=False, warm=2):
+        """ms of each of `iters` calls, one event pair per call; the eviction
+        (when asked) runs before each call, outside its events"""
+        torch = self.torch
+        evs = []
+        for _ in range(warm + iters):
+            if evict:
+                self.evict()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(self.stream)
+            fn()
+            b.record(self.stream)
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in evs[warm:]]
+
+    def back_to_back(self, fn, iters):
+        """mean ms of `iters` calls launched back to back"""
+        torch = self.torch
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(self.stream)
+        for _ in range(iters):
+            fn()
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+
+def layer_roofline(cfg, touched: int, n_kept: int, ms: float) -> dict:
+    """The whole layer against its roofline: the algorithmic bytes (router
+    weights, the touched experts' and the shared expert's weights, x read
+    and y written once) at the HBM peak, or the algorithmic FLOPs at the
+    MFMA peak of the layer's dtype, whichever takes longer; frac = that
+    time / the measured step."""
+    d = cfg.d_model
+    esz = 2 if cfg.dtype == "bf16" else 4
+    nbytes = (4 * cfg.n_experts * d
+              + esz * (3 * d * (touched * cfg.d_ff + cfg.d_ff_shared) + 2 * cfg.T * d))
+    fl = algorithmic_flops(cfg, n_kept)["total"]
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9) * 1e3
+    t_mfma = fl / (peak * 1e12) * 1e3
+    bound = "hbm" if t_hbm >= t_mfma else "mfma"
+    return {"bound": bound, "algorithmic_bytes": int(nbytes), "flops": fl,
+            "min_ms_at_peaks": round(max(t_hbm, t_mfma), 4),
+            "frac": round(max(t_hbm, t_mfma) / ms, 4),
+            "hbm_frac": round(t_hbm / ms, 4), "mfma_frac": round(t_mfma / ms, 4)}
+
+
+def expert_stages(moe, torch, tm, cfg, shape, inp, ws, n_kept, iters):
+    """Route and dispatch once, build the work lists, then time the gate/up
+    and the down grouped GEMMs alone (offsets=None launches the GEMM kernel
+    only, so each event pair brackets one kernel), each call after a
+    last-level-cache eviction.  Returns (roofline of gate/up, down-projection
+    figures, the routing buffers)."""
+    dev = inp.x.device
+    T, N, k, d = cfg.T, cfg.n_experts, cfg.top_k, cfg.d_model
+    b = dict(
+        sc=torch.empty((T, N), dtype=torch.float32, device=dev),
+        ti=torch.empty((T, k), dtype=torch.int32, device=dev),
+        tw=torch.empty((T, k), dtype=torch.float32, device=dev),
+        cn=torch.empty((N,), dtype=torch.int32, device=dev),
+        of=torch.empty((N + 1,), dtype=torch.int32, device=dev),
+        sl=torch.empty((T * k,), dtype=torch.int32, device=dev),
+        pm=torch.empty((T * k,), dtype=torch.int32, device=dev),
+        nkd=torch.empty((2,), dtype=torch.int32, device=dev),
+    )
+    dt = shape.torch_dtype
+    b["h"] = torch.empty((T * k, cfg.d_ff), dtype=dt, device=dev)
+    b["hs"] = (torch.empty((T, cfg.d_ff_shared), dtype=dt, device=dev)
+               if cfg.d_ff_shared else None)
+    b["yp"] = torch.empty((T * k, d), dtype=dt, device=dev)
+    b["ysh"] = torch.empty((T, d), dtype=dt, device=dev) if cfg.d_ff_shared else None
+    moe.moe_route(shape, inp.x, inp.w_router, inp.logit_add, None, inp.bias, None, b["sc"],
+                  b["ti"], b["tw"], ws)
+    moe.moe_dispatch(shape, b["ti"], b["cn"], b["of"], b["sl"], b["pm"], b["nkd"], ws)
+    moe.moe_expert_plan(shape, b["of"], ws)
+    t1 = tm.each(lambda: moe.moe_expert_gate_up(shape, inp.x, b["pm"], None, inp.w1,
+                                                inp.w1_shared, b["h"], b["hs"], ws),
+                 iters, evict=True)
+    t2 = tm.each(lambda: moe.moe_expert_down(shape, b["h"], b["hs"], None, inp.w2,
+                                             inp.w2_shared, b["yp"], b["ysh"], ws),
+                 iters, evict=True)
+    g1_ms, g2_ms = sum(t1) / len(t1), sum(t2) / len(t2)
+    counts = b["cn"].cpu().numpy()
+    g1_flops = 4.0 * d * cfg.d_ff * n_kept + 4.0 * T * d * cfg.d_ff_shared
+    g2_flops = 2.0 * d * cfg.d_ff * n_kept + 2.0 * T * d * cfg.d_ff_shared
+    touched = int((counts > 0).sum())
+    esz = 2 if cfg.dtype == "bf16" else 4
+    g1_bytes = esz * (touched * 2 * cfg.d_ff * d + 2 * cfg.d_ff_shared * d + T * d
+                      + n_kept * cfg.d_ff + T * cfg.d_ff_shared)
+    g2_bytes = esz * (touched * cfg.d_ff * d + cfg.d_ff_shared * d + n_kept * cfg.d_ff
+                      + T * cfg.d_ff_shared + n_kept * d + (T * d if cfg.d_ff_shared else 0))
+    traffic = committed_traffic(cfg.name)
+    # the bound is whichever peak the kernel's algorithmic work would hit
+    # first: its bytes at the HBM peak or its FLOPs at the MFMA peak
+    peak_fl = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    t_hbm = g1_bytes / (PEAK_HBM_GBS * 1e9)
+    t_mfma = g1_flops / (peak_fl * 1e12)
+    gbs = g1_bytes / (g1_ms * 1e-3) / 1e9
+    tfs = g1_flops / (g1_ms * 1e-3) / 1e12
+    if t_hbm >= t_mfma:
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
+                    "mfma_frac": round(tfs / peak_fl, 4)}
+    else:
+        roofline = {"bound": "mfma", "achieved": round(tfs, 2), "peak": peak_fl,
+                    "unit": "TFLOP/s", "frac": round(tfs / peak_fl, 4), "traffic": traffic,
+                    "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+    if cfg.dtype == "bf16":
+        kname = ("gemm_mfma_kernel<true, false, .> (bf16 gate/up projection + SwiGLU over "
+                 "every expert segment and the shared expert; one launch per call, work "
+                 "list prebuilt)")
+        k2name = "gemm_mfma_kernel<false, false, .> (bf16 down projection)"
+    else:
+        kname = ("gemm_f32_kernel<true> (fp32 gate/up projection + SwiGLU over every "
+                 "expert segment; one launch per call, work list prebuilt)")
+        k2name = "gemm_f32_kernel<false> (fp32 down projection)"
+    roofline.update({
+        "kernel": kname,
+        "avg_ms": round(g1_ms, 4),
+        "median_ms": quantiles(t1)["median"],
+        "flops_per_launch": g1_flops,
+        "algorithmic_bytes_per_launch": g1_bytes,
+        "touched_experts": touched,
+        "min_ms_at_peaks": round(max(t_hbm, t_mfma) * 1e3, 4),
+    })
+    g2_gbs = g2_bytes / (g2_ms * 1e-3) / 1e9
+    gemm2 = {"kernel": k2name, "avg_ms": round(g2_ms, 4),
+             "tflops": round(g2_flops / (g2_ms * 1e-3) / 1e12, 2),
+             "algorithmic_bytes_per_launch": g2_bytes, "GB/s": round(g2_gbs, 1),
+             "hbm_frac": round(g2_gbs / PEAK_HBM_GBS, 4)}
+    b["touched"] = touched
+    b["g1_flops"], b["g2_flops"] = g1_flops, g2_flops
+    return roofline, gemm2, b
+
+
+def workload_name(cfg) -> str:
+    return (f"{cfg.name}: T={cfg.T} d_model={cfg.d_model} N={cfg.n_experts} top_k={cfg.top_k}"
+            f" d_ff={cfg.d_ff} shared={cfg.d_ff_shared} score={cfg.score_fn}"
+            f" groups={cfg.topk_groups}/{cfg.n_groups}"
+            f" capacity_factor={cfg.capacity_factor}")
+
+
+def measure_config(moe, W, torch, dev, cfg, args) -> dict:
+    """One further workload: graph-replayed forwards timed one by one
+    (median, p10, p90), the layer roofline, the gate/up kernel roofline and
+    the oracle on a sample."""
+    print(f"[bench] {cfg.name}: generating inputs", file=sys.stderr, flush=True)
+    inp = W.make_inputs(cfg, seed=0, device=dev)
+    shape = moe.MoeShape.from_config(cfg)
+    ws = moe.workspace(shape, dev)
+    y = torch.empty((cfg.T, cfg.d_model), dtype=shape.torch_dtype, device=dev)
+    nkd = torch.empty(2, dtype=torch.int32, device=dev)
+    tm = Timer(torch, dev)
+
+    def step():
+        moe.moe_forward(shape, inp.x, inp.w_router, inp.logit_add, inp.bias, inp.w1, inp.w2,
+                        inp.w1_shared, inp.w2_shared, y, None, None, None, None, None, None,
+                        nkd, ws)
+    for _ in range(args.warmup):
+        step()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    iters = max(args.steps, MIN_STEPS.get(cfg.name, 0))
+    evict = cfg.name in STEP_FLUSH
+    print(f"[bench] {cfg.name}: {iters} timed steps", file=sys.stderr, flush=True)
+    ts = tm.each(graph.replay, iters, evict=evict, warm=max(2, args.warmup))
+    del graph
+    q = quantiles(ts)
+    ms = q["median"]
+    n_kept = int(nkd[0].item())
+    fl = algorithmic_flops(cfg, n_kept)
+    roofline, gemm2, b = expert_stages(moe, torch, tm, cfg, shape, inp, ws, n_kept,
+                                       args.stage_iters)
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    tfl = fl["total"] / (ms * 1e-3) / 1e12
+    ent = {
+        "workload": workload_name(cfg),
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "launch": "hip graph replay, one event pair per step",
+        "steps": iters,
+        "step_preceded_by": ("a 512 MiB read evicting the last-level cache" if evict
+                             else "the previous step"),
+        "ms_per_step": ms,
+        "ms_p10": q["p10"],
+        "ms_p90": q["p90"],
+        "tokens/s": round(cfg.T / (ms * 1e-3), 1),
+        "tflops": round(tfl, 3),
+        "peak_frac": round(tfl / peak, 4),
+        "n_kept": n_kept,
+        "layer_roofline": layer_roofline(cfg, b["touched"], n_kept, ms),
+        "roofline": roofline,
+        "gemm2": gemm2,
+    }
+    if not args.no_cpu_baseline:
+        print(f"[bench] {cfg.name}: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        ent["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens
+                                           or CPU_SAMPLE.get(cfg.name, 64))
+    del inp, ws, b
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return ent
 
 
 def main():
@@ -161,8 +421,26 @@ def main():
 
     moe.lib()  # fail loudly if the HIP library is missing
     cfg = W.CONFIGS[args.config]
+    others = [c.strip() for c in args.configs.split(",") if c.strip() and c.strip() != cfg.name]
+    unknown = [c for c in others if c not in W.CONFIGS]
+    if unknown:
+        raise SystemExit(f"--configs: unknown workloads {unknown}")
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    res = headline(moe, W, torch, dev, cfg, args)
+    # the headline workload's buffers are gone before the next inputs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    res["configs"] = {}
+    for name in others:
+        res["configs"][name] = measure_config(moe, W, torch, dev, W.CONFIGS[name], args)
+    print(json.dumps(res), flush=True)
+
+
+def headline(moe, W, torch, dev, cfg, args) -> dict:
+    """The headline workload: eager and graph-replayed forwards, the expert
+    GEMM stages, and the layer variants on the same inputs."""
+    skip = {t.strip() for t in args.skip.split(",") if t.strip()}
     print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
     inp = W.make_inputs(cfg, seed=0, device=dev)
     shape = moe.MoeShape.from_config(cfg)
@@ -172,7 +450,7 @@ def main():
         y=torch.empty((T, d), dtype=shape.torch_dtype, device=dev),
         n_kept_dropped=torch.empty(2, dtype=torch.int32, device=dev),
     )
-    stream = torch.cuda.current_stream()
+    tm = Timer(torch, dev)
 
     def step():
         moe.moe_forward(shape, inp.x, inp.w_router, inp.logit_add, inp.bias, inp.w1, inp.w2,
@@ -183,15 +461,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    eager_ms = e0.elapsed_time(e1) / args.steps
+    eager_ms = tm.back_to_back(step, args.steps)
 
     # the same step captured once in a HIP graph (the library does no host
     # syncs, allocations or memsets), then replayed: every kernel still runs
@@ -202,12 +472,9 @@ def main():
     for _ in range(args.warmup):
         graph.replay()
     torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
-        graph.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    graph_ms = e0.elapsed_time(e1) / args.steps
+    graph_ms = tm.back_to_back(graph.replay, args.steps)
+    q = quantiles(tm.each(graph.replay, args.steps))
+    del graph
     ms = min(eager_ms, graph_ms)
     n_kept = int(out["n_kept_dropped"][0].item())
     fl = algorithmic_flops(cfg, n_kept)
@@ -216,86 +483,16 @@ def main():
           file=sys.stderr, flush=True)
 
     # ---- per-kernel timing of the expert GEMMs, same stream, HIP events ----
-    sc = torch.empty((T, N), dtype=torch.float32, device=dev)
-    ti = torch.empty((T, k), dtype=torch.int32, device=dev)
-    tw = torch.empty((T, k), dtype=torch.float32, device=dev)
-    cn = torch.empty((N,), dtype=torch.int32, device=dev)
-    of = torch.empty((N + 1,), dtype=torch.int32, device=dev)
-    sl = torch.empty((T * k,), dtype=torch.int32, device=dev)
-    pm = torch.empty((T * k,), dtype=torch.int32, device=dev)
-    nkd = torch.empty((2,), dtype=torch.int32, device=dev)
-    dt = shape.torch_dtype
-    h = torch.empty((T * k, cfg.d_ff), dtype=dt, device=dev)
-    hs = torch.empty((T, cfg.d_ff_shared), dtype=dt, device=dev) if cfg.d_ff_shared else None
-    yp = torch.empty((T * k, d), dtype=dt, device=dev)
-    ysh = torch.empty((T, d), dtype=dt, device=dev) if cfg.d_ff_shared else None
-    moe.moe_route(shape, inp.x, inp.w_router, inp.logit_add, None, inp.bias, None, sc, ti, tw,
-                  ws)
-    moe.moe_dispatch(shape, ti, cn, of, sl, pm, nkd, ws)
-
-    # Before each timed call a read of 512 MiB evicts the 256 MiB last-level
-    # cache (reads only: no dirty lines left to write back), so the weights
-    # stream from HBM as they do inside a forward, where other kernels run
-    # between two launches of the same GEMM.
-    flush = torch.ones(64 << 20, dtype=torch.float64, device=dev)
-    sink = torch.empty((), dtype=torch.float64, device=dev)
+    roofline, gemm2, b = expert_stages(moe, torch, tm, cfg, shape, inp, ws, n_kept,
+                                       args.stage_iters)
+    sc, ti, tw, cn, of = b["sc"], b["ti"], b["tw"], b["cn"], b["of"]
+    sl, pm, nkd, yp, ysh = b["sl"], b["pm"], b["nkd"], b["yp"], b["ysh"]
+    touched, g1_flops, g2_flops = b["touched"], b["g1_flops"], b["g2_flops"]
+    esz = 2 if cfg.dtype == "bf16" else 4
 
     def timed(fn, iters):
-        evs = []
-        for _ in range(2 + iters):
-            torch.sum(flush, dim=0, out=sink)
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            fn()
-            b.record(stream)
-            evs.append((a, b))
-        torch.cuda.synchronize()
-        t = [a.elapsed_time(b) for a, b in evs[2:]]
+        t = tm.each(fn, iters, evict=True)
         return sum(t) / len(t)
-
-    # the work lists are built once; offsets=None then launches the GEMM
-    # kernel alone, so the events bracket exactly one kernel per call
-    moe.moe_expert_plan(shape, of, ws)
-    g1_ms = timed(lambda: moe.moe_expert_gate_up(shape, inp.x, pm, None, inp.w1, inp.w1_shared,
-                                                 h, hs, ws), args.stage_iters)
-    g2_ms = timed(lambda: moe.moe_expert_down(shape, h, hs, None, inp.w2, inp.w2_shared, yp,
-                                              ysh, ws), args.stage_iters)
-    counts = cn.cpu().numpy()
-    g1_flops = 4.0 * d * cfg.d_ff * n_kept + 4.0 * T * d * cfg.d_ff_shared
-    g2_flops = 2.0 * d * cfg.d_ff * n_kept + 2.0 * T * d * cfg.d_ff_shared
-    touched = int((counts > 0).sum())
-    esz = 2 if cfg.dtype == "bf16" else 4
-    g1_bytes = esz * (touched * 2 * cfg.d_ff * d + 2 * cfg.d_ff_shared * d + T * d
-                      + n_kept * cfg.d_ff + T * cfg.d_ff_shared)
-    traffic = committed_traffic(cfg.name)
-    # the bound is whichever peak the kernel's algorithmic work would hit
-    # first: its bytes at the HBM peak or its FLOPs at the MFMA peak
-    peak_fl = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
-    t_hbm = g1_bytes / (PEAK_HBM_GBS * 1e9)
-    t_mfma = g1_flops / (peak_fl * 1e12)
-    gbs = g1_bytes / (g1_ms * 1e-3) / 1e9
-    tfs = g1_flops / (g1_ms * 1e-3) / 1e12
-    if t_hbm >= t_mfma:
-        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                    "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
-                    "mfma_frac": round(tfs / peak_fl, 4)}
-    else:
-        roofline = {"bound": "mfma", "achieved": round(tfs, 2), "peak": peak_fl,
-                    "unit": "TFLOP/s", "frac": round(tfs / peak_fl, 4), "traffic": traffic,
-                    "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
-    roofline.update({
-        "kernel": "gemm_mfma_kernel<true, false, .> (bf16 gate/up projection + SwiGLU over every expert "
-                  "segment and the shared expert; one launch per call, work list prebuilt)",
-        "avg_ms": round(g1_ms, 4),
-        "flops_per_launch": g1_flops,
-        "algorithmic_bytes_per_launch": g1_bytes,
-        "touched_experts": touched,
-        "min_ms_at_peaks": round(max(t_hbm, t_mfma) * 1e3, 4),
-    })
-    gemm2 = {"kernel": "gemm_mfma_kernel<false, false, .> (bf16 down projection)", "avg_ms": round(g2_ms, 4),
-             "tflops": round(g2_flops / (g2_ms * 1e-3) / 1e12, 2)}
-
     # router telemetry over this forward's outputs (HBM-bound: it reads the
     # kept expert rows, the shared rows, the scores and the gates once)
     telemetry = None
@@ -322,13 +519,7 @@ def main():
                                inp.w1_shared, inp.w2_shared, y_ec, None, None, None, ws_ec)
         for _ in range(2):
             ec_step()
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(args.stage_iters):
-            ec_step()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ec_ms = e0.elapsed_time(e1) / args.stage_iters
+        ec_ms = tm.back_to_back(ec_step, args.stage_iters)
         expert_choice = {"ms_per_step": round(ec_ms, 4), "tokens/s": round(T / (ec_ms * 1e-3), 1),
                          "capacity_per_expert": moe.moe_ec_capacity(ec_shape)}
 
@@ -355,13 +546,7 @@ def main():
             mx_step()
         for _ in range(2):
             g_mx.replay()
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(args.steps):
-            g_mx.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        mx_ms = e0.elapsed_time(e1) / args.steps
+        mx_ms = tm.back_to_back(g_mx.replay, args.steps)
         del g_mx
         hq = torch.empty(moe.mx_bytes(T * k * cfg.d_ff), dtype=torch.uint8, device=dev)
         hsq = (torch.empty(moe.mx_bytes(T * cfg.d_ff_shared), dtype=torch.uint8, device=dev)
@@ -446,13 +631,7 @@ def main():
             lat_step()
         for _ in range(2):
             g_l.replay()
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(args.steps):
-            g_l.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        l_ms = e0.elapsed_time(e1) / args.steps
+        l_ms = tm.back_to_back(g_l.replay, args.steps)
         del g_l
         l_flops = (2.0 * T * d * N + 4.0 * T * d * l + 6.0 * l * cfg.d_ff * n_kept
                    + 6.0 * T * d * cfg.d_ff_shared)
@@ -478,14 +657,15 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) weights)",
-        "config": {"workload": f"{cfg.name}: T={T} d_model={d} N={N} top_k={k} d_ff={cfg.d_ff}"
-                               f" shared={cfg.d_ff_shared} score={cfg.score_fn}"
-                               f" groups={cfg.topk_groups}/{cfg.n_groups}"
-                               f" capacity_factor={cfg.capacity_factor}",
-                   "global_batch": T, "parallelism": "single GPU"},
+        "config": {"workload": workload_name(cfg), "global_batch": T,
+                   "parallelism": "single GPU"},
+        "ms_median": q["median"],
+        "ms_p10": q["p10"],
+        "ms_p90": q["p90"],
         "tflops": round(tflops, 2),
         "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "n_kept": n_kept,
+        "layer_roofline": layer_roofline(cfg, touched, n_kept, ms),
         "roofline": roofline,
         "gemm2": gemm2,
         "telemetry": telemetry,
@@ -496,8 +676,9 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens)
-    print(json.dumps(res), flush=True)
+        res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens
+                                           or CPU_SAMPLE.get(cfg.name, 64))
+    return res
 
 
 if __name__ == "__main__":
