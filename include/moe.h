@@ -86,6 +86,10 @@
  *     an error nothing is launched and the status says why.  No C++
  *     exception crosses this interface.  MOE_ERR_HIP reports a failed
  *     launch (the HIP error is then retrievable with hipGetLastError()).
+ *   - Threads: every entry point may be called from several host threads at
+ *     once (host state is read-only after its first initialisation, which
+ *     is race-free); calls that share a workspace or an output must still
+ *     not overlap on the GPU.
  *   - Determinism: every output is bitwise reproducible run to run, and the
  *     routing of a token does not depend on the other tokens of the batch
  *     (dropless) -- no atomics decide any value or order.
@@ -179,8 +183,16 @@ moe_status moe_quantize_mx(const void* in, int32_t in_dtype, int64_t rows,
  * only).  scores_in [T,N] fp32 or NULL: when given, the GEMM and score
  * function are skipped and these scores are selected on (x and w_router
  * may then be NULL).  Outputs: logits_out [T,N] = x W_r^T, the affinity
- * GEMM before logit_add (NULL: not written; ignored with scores_in), scores_out [T,N] (NULL: not written), topk_idx [T,k],
- * topk_w [T,k] (required). */
+ * GEMM before logit_add (NULL: not written; ignored with scores_in),
+ * scores_out [T,N] (NULL: not written), topk_idx [T,k], topk_w [T,k]
+ * (required).  Per-expert counts come from moe_dispatch, which needs the
+ * selection anyway.
+ * Source: "MoE architecture in practice", routing-math section (linear
+ * affinity without a bias, softmax, top-k, renormalised gates) and
+ * load-balancing section (selection on s + b, gates from s alone);
+ * llm-compass "MoE" page, gate equation and aux-loss-free selection;
+ * "MoE common taste of open models", section 7 (sigmoid scores, fp32
+ * router); "MoE industrial evolution", section 4 (group-limited routing). */
 moe_status moe_route(const moe_shape* shape, const void* x,
                      const float* w_router, const float* logit_add,
                      const float* scores_in, const float* bias,
@@ -190,7 +202,13 @@ moe_status moe_route(const moe_shape* shape, const void* x,
 /* Dispatch: per-expert counts, capacity drop and the stable permutation.
  * topk_idx [T,k] with values in [0,N).  Outputs (all required): counts [N]
  * (pre-drop), offsets [N+1] (exclusive scan of kept counts), slot [T*k],
- * perm [T*k], n_kept_dropped [2] = {R, T*k - R}. */
+ * perm [T*k], n_kept_dropped [2] = {R, T*k - R}.  No permuted copy of x is
+ * written: the gate/up projection gathers its rows through perm.
+ * Source: "MoE architecture in practice", capacity-factor section (the
+ * earliest assignments keep their slots, overflow is dropped) and
+ * expert-parallelism section (token-major flatten, stable grouping by
+ * expert into contiguous segments); llm-compass "MoE" page, capacity
+ * formula. */
 moe_status moe_dispatch(const moe_shape* shape, const int32_t* topk_idx,
                         int32_t* counts, int32_t* offsets, int32_t* slot,
                         int32_t* perm, int32_t* n_kept_dropped, void* ws,
@@ -243,7 +261,11 @@ moe_status moe_expert_down(const moe_shape* shape, const void* h,
 
 /* Combine: y_t = sum_j [slot_tj >= 0] g_tj y_perm[slot_tj] (+ y_shared_t),
  * fp32 accumulation in ascending j, then the shared term; dropped
- * assignments add nothing.  y_shared NULL when there is no shared expert. */
+ * assignments add nothing.  y_shared NULL when there is no shared expert.
+ * Source: llm-compass "MoE" page, output equation y = sum_i g_i E_i(x) and
+ * shared-expert equation; "MoE architecture in practice", expert-
+ * parallelism section (combine back to token order) and capacity-factor
+ * section (a dropped assignment contributes nothing). */
 moe_status moe_combine(const moe_shape* shape, const void* y_perm,
                        const void* y_shared, const int32_t* slot,
                        const float* topk_w, void* y, void* stream);
@@ -254,7 +276,11 @@ moe_status moe_combine(const moe_shape* shape, const void* y_perm,
  * aux_out are given, aux_out[0] = N * sum_i (counts_i / T) * mean_t s_ti
  * (computed before the bias changes; it does not depend on the bias).
  * counts, scores [T,N], bias [N], aux_out [1]: device pointers; counts and
- * bias required, step finite. */
+ * bias required, step finite.  ws holds the per-expert score means.
+ * Source: "MoE architecture in practice", load-balancing-loss section (the
+ * selection-only bias moved by a sign step against the mean load, and the
+ * N sum f_i P_i statistic); llm-compass "MoE" page, aux-loss and
+ * aux-loss-free equations. */
 moe_status moe_bias_update(const moe_shape* shape, const int32_t* counts,
                            const float* scores, float step, float clamp,
                            float* bias, float* aux_out, void* ws,
@@ -350,7 +376,12 @@ moe_status moe_forward_ec(const moe_shape* shape, const void* x,
  * Required: x, w_router, w1, w2, y (and the shared weights iff
  * d_ff_shared > 0).  Optional inputs logit_add, bias; optional outputs
  * (NULL: kept in the workspace only) scores_out [T,N], topk_idx, topk_w
- * [T,k], counts [N], offsets [N+1], slot [T*k], n_kept_dropped [2]. */
+ * [T,k], counts [N], offsets [N+1], slot [T*k], n_kept_dropped [2].  The
+ * SwiGLU intermediate h and the expert outputs y_perm, y_shared stay in the
+ * workspace.  Source: the layer of the header comment above -- llm-compass
+ * "MoE" page (gate and output equations, capacity formula, shared expert);
+ * "MoE architecture in practice", routing-math, capacity-factor,
+ * shared-expert and expert-parallelism sections. */
 moe_status moe_forward(const moe_shape* shape, const void* x,
                        const float* w_router, const float* logit_add,
                        const float* bias, const void* w1, const void* w2,

@@ -246,3 +246,59 @@ def test_mxfp8_and_latent_host_checks(m):
     ms = shape(dtype="mxfp8", d_model=128, d_ff=128)
     assert L.moe_forward_latent(ctypes.byref(ms), 128, *args, ws_ok, big, None) == \
         m.MOE_ERR_UNSUPPORTED
+
+
+def test_host_entry_points_from_many_threads(m):
+    """The host-side entry points (validation, capacity, workspace sizes, the
+    argument checks of the launching calls) give the same answers when called
+    from eight threads at once as from one (ctypes drops the GIL around each
+    call, so the calls really overlap)."""
+    import threading
+    L = m.lib()
+    P = ctypes.c_void_p
+    fake = P(4096)
+    big = 1 << 40
+    shapes = [shape(), shape(T=0), shape(top_k=9), shape(d_model=96),
+              shape(T=8192, d_model=7168, n_experts=256, top_k=8, d_ff=2048, d_ff_shared=2048,
+                    n_groups=8, topk_groups=4),
+              shape(capacity_factor=1.25), shape(capacity_factor=1.0,
+                                                 capacity_rule=m.MOE_CAP_ASSIGNMENTS),
+              shape(T=64, d_model=2048, n_experts=128, top_k=8, d_ff=768)]
+
+    def answers():
+        out = []
+        for s in shapes:
+            out.append((m.moe_check_shape(s), m.moe_capacity(s), m.moe_workspace_bytes(s),
+                        m.moe_router_stats_count(s), m.moe_ec_capacity(s),
+                        m.moe_latent_workspace_bytes(s, 64)))
+            # launching calls that must fail in validation, before any launch
+            out.append(L.moe_route(ctypes.byref(s), fake, fake, None, None, None, None, None,
+                                   None, None, P(256 * 1000), big, None))
+            out.append(L.moe_forward(ctypes.byref(s), fake, fake, None, None, fake, fake, None,
+                                     None, None, *([None] * 7), P(256 * 1000), big, None))
+            out.append(L.moe_dispatch(ctypes.byref(s), fake, fake, fake, None, fake, fake,
+                                      P(256 * 1000), big, None))
+        out.append(tuple(m.moe_status_string(i) for i in range(7)))
+        return out
+
+    expected = answers()
+    results, errors = [None] * 8, []
+
+    def worker(i):
+        try:
+            for _ in range(200):
+                r = answers()
+                if r != expected:
+                    results[i] = r
+                    return
+            results[i] = expected
+        except Exception as e:  # reported below, not swallowed
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    assert all(r == expected for r in results)
