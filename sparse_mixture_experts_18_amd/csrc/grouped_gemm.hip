@@ -26,12 +26,30 @@
 // list.  An fp32 VALU path serves fp32 layers.
 #include <atomic>
 #include <type_traits>
+#include <utility>
 
 #include "moe_internal.h"
 #include "route_device.h"
 
 namespace moe {
 namespace {
+// one group of the explicit instruction order of a scheduling region: N
+// instructions of the classes in MASK (0x008 MFMA, 0x020 vector-memory read,
+// 0x100 LDS read); nothing for N = 0
+template <int MASK, int N>
+__device__ __forceinline__ void sched() {
+  if constexpr (N > 0) __builtin_amdgcn_sched_group_barrier(MASK, N, 0);
+}
+constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedLdsRead = 0x100;
+// f(integral_constant<int, I>) for I = 0 .. N-1, in order
+template <int... I, class F>
+__device__ __forceinline__ void static_for_impl(std::integer_sequence<int, I...>, F&& f) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(std::make_integer_sequence<int, N>{}, f);
+}
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -348,10 +366,14 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, const WorkItem& it,
   auto issue_b = [&](int kt) {
     unsigned char* st = Bbuf + (kt % SB) * C::B_BYTES;
     const uint32_t k0 = kt * C::ROWB;
-    // small-row tiles (one 32-row sub-tile per wave) read each weight byte
-    // about once: load the weights as streaming data so that they leave L2
-    // and the MALL before the activations and the work lists
-    constexpr int aux = C::MSW == 1 ? kNonTemporal : 0;
+    // weights as streaming data, so that they leave L2 and the MALL before
+    // the rows they multiply: in the gate/up projection (the token rows
+    // are re-read by every column tile of their row block; mixtral -4 %,
+    // switch -16 %, dsv3 unchanged) and in the small-row tiles (one 32-row
+    // sub-tile per wave, each weight byte read about once).  The dsv3 down
+    // projection, whose sibling row blocks share their weight slabs in L2,
+    // loses 3.5 % with it.
+    constexpr int aux = (GATED || C::MSW == 1) ? kNonTemporal : 0;
 #pragma unroll
     for (int j = 0; j < C::B_LOADS; ++j)
       dma16<aux>(rb, b_off[j], k0, st + (w * C::B_LOADS + j) * 1024);
@@ -404,16 +426,122 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, const WorkItem& it,
     if (!BFIRST && j + SB - 1 >= 0 && j + SB - 1 < nk) issue_b(j + SB - 1);
   }
 
-  for (int kt = 0; kt < nk; ++kt) {
+  if constexpr (!MX) {
+    // bf16: the k-loop in two parts -- steady iterations that refill the
+    // ring, then the last SA-1 that do not -- and the live-row test of the
+    // wave's last sub-tile taken once per item, so the body of a slice is
+    // one straight-line block whose LDS reads and MFMAs are interleaved
+    // explicitly: each fragment is read at least one MFMA pair before it is
+    // used, instead of being read into the register its previous use has
+    // just released.
+    auto slice = [&](int kt, auto issue_tag, auto last_tag) {
+      constexpr bool ISSUE = decltype(issue_tag)::value;
+      constexpr bool LAST = decltype(last_tag)::value;
+      constexpr int MSL = LAST ? MS : MS - 1;  // live row sub-tiles
+      const unsigned char* As = Abuf + (kt % SA) * A_SL;
+      const unsigned char* Bs = Bbuf + (kt % SB) * C::B_BYTES;
+      if constexpr (MS * NT * 16 + 2 * (MS + NT) * 4 > 224) {
+        // tall tiles: weight fragments double-buffered across k-steps, row
+        // fragments in a two-register rotation one sub-tile ahead
+        FT bf[2][NT], ar[2];
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          bf[0][j] = Frag<MX>::read(Bs + b_row[j] * C::ROWB, 0, fh, C::swz(b_row[j]));
+        ar[0] = Frag<MX>::read(As + a_row[0] * C::ROWB, 0, fh, C::swz(a_row[0]));
+        sched<kSchedLdsRead, NT + 1>();
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+          const int cb = ks & 1;
+          const bool more = ks + 1 < KSTEPS;
+          if (ISSUE && ks == (BFIRST ? 1 : 0)) issue_a(kt + SA - 1);
+          if (ISSUE && ks == (BFIRST ? 0 : 1)) issue_b(kt + SB - 1);
+#pragma unroll
+          for (int i = 0; i < MSL; ++i) {
+            const int q = (ks * MSL + i) & 1;  // rotation slot of sub-tile i
+            if (i + 1 < MSL) {
+              ar[q ^ 1] = Frag<MX>::read(As + a_row[i + 1] * C::ROWB, ks, fh, C::swz(a_row[i + 1]));
+            } else if (more) {
+              ar[q ^ 1] = Frag<MX>::read(As + a_row[0] * C::ROWB, ks + 1, fh, C::swz(a_row[0]));
+#pragma unroll
+              for (int j = 0; j < NT; ++j)
+                bf[cb ^ 1][j] =
+                    Frag<MX>::read(Bs + b_row[j] * C::ROWB, ks + 1, fh, C::swz(b_row[j]));
+            }
+#pragma unroll
+            for (int j = 0; j < NT; ++j) acc[i][j] = mma(bf[cb][j], ar[q], acc[i][j], 0, 0);
+          }
+        }
+        // order: per sub-tile, the next fragment read(s), then its MFMAs
+        static_for<KSTEPS>([&](auto ks_c) {
+          constexpr int ks = decltype(ks_c)::value;
+          if constexpr (ISSUE && ks < 2)
+            sched<kSchedVmemRead, ks == (BFIRST ? 1 : 0) ? AL : C::B_LOADS>();
+          static_for<MSL>([&](auto i_c) {
+            constexpr int i = decltype(i_c)::value;
+            sched<kSchedLdsRead, (i + 1 < MSL ? 1 : (ks + 1 < KSTEPS ? NT + 1 : 0))>();
+            sched<kSchedMfma, NT>();
+          });
+        });
+      } else {
+        // fragments of k-step ks+1 are read while the MFMAs of k-step ks
+        // run (two register sets), one read after each MFMA
+        FT bf[2][NT], af[2][MS];
+        load_frags<MX, C, MS>(As, Bs, a_row, b_row, fh, 0, af[0], bf[0]);
+        sched<kSchedLdsRead, MS + NT>();
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+          const int cur = ks & 1;
+          if (ISSUE && ks == (BFIRST ? 1 : 0)) issue_a(kt + SA - 1);
+          if (ISSUE && ks == (BFIRST ? 0 : 1)) issue_b(kt + SB - 1);
+          if (ks + 1 < KSTEPS)
+            load_frags<MX, C, MS>(As, Bs, a_row, b_row, fh, ks + 1, af[cur ^ 1], bf[cur ^ 1]);
+#pragma unroll
+          for (int i = 0; i < MSL; ++i)
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+              acc[i][j] = mma(bf[cur][j], af[cur][i], acc[i][j], 0, 0);
+        }
+        static_for<KSTEPS>([&](auto ks_c) {
+          constexpr int ks = decltype(ks_c)::value;
+          if constexpr (ISSUE && ks < 2)
+            sched<kSchedVmemRead, ks == (BFIRST ? 1 : 0) ? AL : C::B_LOADS>();
+          constexpr int NM = MSL * NT;
+          constexpr int NR = ks + 1 < KSTEPS ? MS + NT : 0;
+          static_for<NM>([&](auto m_c) {
+            constexpr int m = decltype(m_c)::value;
+            sched<kSchedMfma, 1>();
+            sched<kSchedLdsRead, (m < NR ? 1 : 0)>();
+          });
+          sched<kSchedLdsRead, (NR > NM ? NR - NM : 0)>();
+        });
+      }
+    };
+    auto run = [&](auto last_tag) {
+      int kt = 0;
+      for (; kt < nk - (SA - 1); ++kt) {
+        wait_vm<YOUNGER>();
+        __builtin_amdgcn_s_barrier();
+        slice(kt, std::true_type{}, last_tag);
+      }
+      for (; kt < nk; ++kt) {
+        if (kt + SMAX - 2 < nk) wait_vm<YOUNGER>();
+        else wait_vm<0>();
+        __builtin_amdgcn_s_barrier();
+        if (BFIRST && kt + SB - 1 < nk) issue_b(kt + SB - 1);
+        slice(kt, std::false_type{}, last_tag);
+      }
+    };
+    if (last) run(std::true_type{});
+    else run(std::false_type{});
+  } else
+  for (int kt = 0; kt < nk; ++kt) {  // MXFP8
     // a scale group among the younger loads: one of iterations kt-SA+2 ..
     // kt-1 was a multiple of 4 that issued one
     bool grp = false;
-    if (MX) {
 #pragma unroll
-      for (int i = 1; i <= SA - 2; ++i) {
-        const int it2 = kt - i;
-        grp = grp || (it2 >= 0 && (it2 & 3) == 0 && (it2 >> 2) + 1 < ng);
-      }
+    for (int i = 1; i <= SA - 2; ++i) {
+      const int it2 = kt - i;
+      grp = grp || (it2 >= 0 && (it2 & 3) == 0 && (it2 >> 2) + 1 < ng);
     }
     if (kt + SMAX - 2 < nk) {  // every younger load was issued
       if (grp) wait_vm<YOUNGER + 1>();
@@ -430,75 +558,14 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, const WorkItem& it,
     // group buffer; byte b of the word is block b of the slice; the lane of
     // half h takes block 2ks + h into bits 0..7
     uint32_t sa_w[MS], sb_w[NT];
-    if (MX) {
-      if ((kt & 3) == 0 && (kt >> 2) + 1 < ng) issue_g((kt >> 2) + 1);
-      const uint32_t* sc =
-          reinterpret_cast<const uint32_t*>(Gbuf + ((kt >> 2) & 1) * C::SGB) + (kt & 3);
+    if ((kt & 3) == 0 && (kt >> 2) + 1 < ng) issue_g((kt >> 2) + 1);
+    const uint32_t* sc =
+        reinterpret_cast<const uint32_t*>(Gbuf + ((kt >> 2) & 1) * C::SGB) + (kt & 3);
 #pragma unroll
-      for (int i = 0; i < MS; ++i) sa_w[i] = sc[4 * a_row[i]] >> (8 * fh);
+    for (int i = 0; i < MS; ++i) sa_w[i] = sc[4 * a_row[i]] >> (8 * fh);
 #pragma unroll
-      for (int j = 0; j < NT; ++j) sb_w[j] = sc[4 * (C::BM + b_row[j])] >> (8 * fh);
-    }
-    if constexpr (!MX && MS * NT * 16 + 2 * (MS + NT) * 4 > 224) {
-      // tall tiles: the weight fragments of a k-step stay in registers, the
-      // row fragments rotate through two registers (each read one sub-tile
-      // ahead), so the fragments fit next to the accumulators
-      FT bf[NT], a_cur, a_nxt;
-#pragma unroll
-      for (int j = 0; j < NT; ++j)
-        bf[j] = Frag<MX>::read(Bs + b_row[j] * C::ROWB, 0, fh, C::swz(b_row[j]));
-      a_cur = Frag<MX>::read(As + a_row[0] * C::ROWB, 0, fh, C::swz(a_row[0]));
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        const bool more = ks + 1 < KSTEPS;
-        if (ks == (BFIRST ? 1 : 0) && kt + SA - 1 < nk) issue_a(kt + SA - 1);
-        if (ks == (BFIRST ? 0 : 1) && kt + SB - 1 < nk) issue_b(kt + SB - 1);
-#pragma unroll
-        for (int i = 0; i < MS; ++i) {
-          if (i + 1 < MS)
-            a_nxt = Frag<MX>::read(As + a_row[i + 1] * C::ROWB, ks, fh, C::swz(a_row[i + 1]));
-          else if (more)
-            a_nxt = Frag<MX>::read(As + a_row[0] * C::ROWB, ks + 1, fh, C::swz(a_row[0]));
-          if (i < MS - 1 || last) {
-#pragma unroll
-            for (int j = 0; j < NT; ++j) acc[i][j] = mma(bf[j], a_cur, acc[i][j], 0, 0);
-          }
-          if (i == MS - 1 && more) {
-#pragma unroll
-            for (int j = 0; j < NT; ++j)
-              bf[j] = Frag<MX>::read(Bs + b_row[j] * C::ROWB, ks + 1, fh, C::swz(b_row[j]));
-          }
-          a_cur = a_nxt;
-        }
-      }
-    } else if constexpr (!MX) {
-      // fragments of k-step ks+1 are read while the MFMAs of k-step ks run
-      // (two register sets)
-      FT bf[2][NT], af[2][MS];
-      load_frags<MX, C, MS>(As, Bs, a_row, b_row, fh, 0, af[0], bf[0]);
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        const int cur = ks & 1;
-        // refill the buffers of slice kt-1 (with a deeper A ring, B first):
-        // the first set behind the first fragment reads, the second one
-        // k-step later, so the reads of k-step 0 are not queued behind a
-        // burst of loads
-        if (ks == (BFIRST ? 1 : 0) && kt + SA - 1 < nk) issue_a(kt + SA - 1);
-        if (ks == (BFIRST ? 0 : 1) && kt + SB - 1 < nk) issue_b(kt + SB - 1);
-        if (ks + 1 < KSTEPS)
-          load_frags<MX, C, MS>(As, Bs, a_row, b_row, fh, ks + 1, af[cur ^ 1], bf[cur ^ 1]);
-#pragma unroll
-        for (int i = 0; i < MS - 1; ++i)
-#pragma unroll
-          for (int j = 0; j < NT; ++j)
-            acc[i][j] = mma(bf[cur][j], af[cur][i], acc[i][j], 0, 0);
-        if (last) {
-#pragma unroll
-          for (int j = 0; j < NT; ++j)
-            acc[MS - 1][j] = mma(bf[cur][j], af[cur][MS - 1], acc[MS - 1][j], 0, 0);
-        }
-      }
-    } else {
+    for (int j = 0; j < NT; ++j) sb_w[j] = sc[4 * (C::BM + b_row[j])] >> (8 * fh);
+    {
       // MXFP8 fragments are twice as wide and each MFMA four times as long:
       // one register set, each fragment re-read for the next k-step as soon
       // as its last MFMA of this step is issued
