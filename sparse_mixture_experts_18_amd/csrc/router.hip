@@ -207,6 +207,11 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const bf16_t* __restri
 // router_mfma_kernel, computed side by side -- so the partial planes are bit
 // for bit the ones of the other router kernels.
 constexpr int RS_T = 32;  // tile rows and columns
+// Each token tile of this kernel splits the weight chunk it uses again, so it
+// serves batches of at most two tiles; larger k-split batches split the
+// weights once (split3_kernel) and run router_mfma_kernel per chunk (the
+// same partial planes).
+constexpr int kRouterSmallMaxT = 2 * RS_T;
 __global__ __launch_bounds__(256) void router_small_kernel(const bf16_t* __restrict__ x,
                                                            const float* __restrict__ w,
                                                            float* __restrict__ out, int T,
@@ -452,7 +457,7 @@ hipError_t launch_router_gemm(const moe_shape& s, const void* x, const float* w_
   if (act_bf16(s)) {
     const long long n = (long long)N * d;
     const int nkc = router_split_chunks(s);
-    if (nkc) {
+    if (nkc && T <= kRouterSmallMaxT) {
       dim3 grid((T + RS_T - 1) / RS_T, (N + RS_T - 1) / RS_T, nkc);
       router_small_kernel<<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(x), w_router,
                                                 w.router_part, T, N, d);
@@ -460,7 +465,12 @@ hipError_t launch_router_gemm(const moe_shape& s, const void* x, const float* w_
       return hipGetLastError();
     }
     split3_kernel<<<(int)min((n + 255) / 256, 2048LL), 256, 0, st>>>(w_router, w.wsplit, n);
-    if ((size_t)T * d * 2 < (1ull << 31) && (size_t)3 * N * d * 2 < (1ull << 31)) {
+    if (nkc) {
+      dim3 grid((T + RM_BM - 1) / RM_BM, (N + RM_BN - 1) / RM_BN, nkc);
+      router_mfma_kernel<<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(x), w.wsplit,
+                                               w.router_part, T, N, d, 1);
+      *nparts = nkc;
+    } else if ((size_t)T * d * 2 < (1ull << 31) && (size_t)3 * N * d * 2 < (1ull << 31)) {
       // (32-bit buffer offsets)
       const int Q = ((T + R2_BM - 1) / R2_BM) * ((N + R2_BN - 1) / R2_BN);
       router_mfma2_kernel<<<8 * ((Q + 7) / 8), 512, 0, st>>>(static_cast<const bf16_t*>(x),

@@ -320,14 +320,16 @@ def test_router_kernels_agree_on_ragged_shapes():
     """A batch of 4133 tokens runs the router GEMM without the k split (the
     DMA-fed large-batch kernel: 128-token tiles, the last one 37 rows deep;
     96 experts, the second 64-expert tile half full; d = 576, so the last
-    512-wide k-chunk is one slice); batches of 64 tokens take the k split.
-    Rows 100..163 and the last 64 rows agree bit for bit, and every logit is
-    within the fp32 bound of the oracle's fp64 product."""
+    512-wide k-chunk is one slice); batches of 64 tokens take the k split in
+    the kernel that splits the fp32 weights itself, batches of 100 the k split
+    over the pre-split weights.  Rows 100..163, 200..299 and the last 64 rows
+    agree bit for bit, and every logit is within the fp32 bound of the
+    oracle's fp64 product."""
     cfg = W.CONFIGS["mixtral"].replace(name="ragged_router", T=4133, d_model=576,
                                        n_experts=96, top_k=4, d_ff=64)
     inp = W.make_inputs(cfg, seed=6, device="cuda")
     full = _route_logits(inp, moe.MoeShape.from_config(cfg))
-    for lo, hi in [(100, 164), (4069, 4133)]:
+    for lo, hi in [(100, 164), (200, 300), (4069, 4133)]:
         sub = W.LayerInputs(cfg, inp.x[lo:hi].contiguous(), inp.w_router, inp.w1, inp.w2,
                             inp.w1_shared, inp.w2_shared, inp.bias, None)
         part = _route_logits(sub, moe.MoeShape.from_config(cfg, T=hi - lo))
