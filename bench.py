@@ -83,13 +83,13 @@ def algorithmic_flops(cfg, n_kept: int) -> dict:
                 total=router + experts + shared)
 
 
-def committed_traffic(workload: str):
-    """HBM bytes per launch of the gate/up GEMM on this workload, from the
-    committed rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, each scaled
-    by the same counter on a plain 1 GiB copy); None when there is none or the
-    kernel source changed since the counters were taken."""
+def committed_traffic(workload: str, proj: str = "gate_up"):
+    """HBM bytes per launch of the gate/up (or down) GEMM on this workload,
+    from the committed rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE,
+    each scaled by the same counter on a plain 1 GiB copy); None when there is
+    none or the kernel source changed since the counters were taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"gemm_gate_up_{workload}_hbm_traffic.md")
+    path = os.path.join(ROOT, "profiles", f"gemm_{proj}_{workload}_hbm_traffic.md")
     src = os.path.join(ROOT, "sparse_mixture_experts_18_amd", "csrc", "grouped_gemm.hip")
     if not os.path.exists(path):
         return None
@@ -327,7 +327,8 @@ def expert_stages(moe, torch, tm, cfg, shape, inp, ws, n_kept, iters):
     gemm2 = {"kernel": k2name, "avg_ms": round(g2_ms, 4),
              "tflops": round(g2_flops / (g2_ms * 1e-3) / 1e12, 2),
              "algorithmic_bytes_per_launch": g2_bytes, "GB/s": round(g2_gbs, 1),
-             "hbm_frac": round(g2_gbs / PEAK_HBM_GBS, 4)}
+             "hbm_frac": round(g2_gbs / PEAK_HBM_GBS, 4),
+             "traffic": committed_traffic(cfg.name, "down")}
     b["touched"] = touched
     b["g1_flops"], b["g2_flops"] = g1_flops, g2_flops
     return roofline, gemm2, b
