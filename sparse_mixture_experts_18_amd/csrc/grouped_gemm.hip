@@ -434,6 +434,24 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, const WorkItem& it,
     // explicitly: each fragment is read at least one MFMA pair before it is
     // used, instead of being read into the register its previous use has
     // just released.
+    // Refill of the ring in a steady iteration, in the issue order the wait
+    // counts assume (with a deeper A ring, B first).  The gate/up projection
+    // issues both operands at k-step 0, as early as the barrier allows (its
+    // long reduction is bound by load latency: dsv3 -2.4 %, mixtral -5 %,
+    // switch -13 %); the down projection issues the second operand one
+    // k-step later, so the fragment reads of k-step 0 do not queue behind a
+    // burst of loads (issuing both at once costs it 2.5-11 %).
+    auto refill_second = [&](int kt) {
+      if (BFIRST) issue_a(kt + SA - 1);
+      else issue_b(kt + SB - 1);
+    };
+    constexpr int FIRST_LOADS = BFIRST ? C::B_LOADS : AL;
+    constexpr int REFILL0 = GATED ? AL + C::B_LOADS : FIRST_LOADS;
+    auto refill_first = [&](int kt) {
+      if (BFIRST) issue_b(kt + SB - 1);
+      else issue_a(kt + SA - 1);
+      if (GATED) refill_second(kt);
+    };
     auto slice = [&](int kt, auto issue_tag, auto last_tag) {
       constexpr bool ISSUE = decltype(issue_tag)::value;
       constexpr bool LAST = decltype(last_tag)::value;
@@ -453,8 +471,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, const WorkItem& it,
         for (int ks = 0; ks < KSTEPS; ++ks) {
           const int cb = ks & 1;
           const bool more = ks + 1 < KSTEPS;
-          if (ISSUE && ks == (BFIRST ? 1 : 0)) issue_a(kt + SA - 1);
-          if (ISSUE && ks == (BFIRST ? 0 : 1)) issue_b(kt + SB - 1);
+          if (ISSUE && ks == 0) refill_first(kt);
+          if (ISSUE && ks == 1 && !GATED) refill_second(kt);
 #pragma unroll
           for (int i = 0; i < MSL; ++i) {
             const int q = (ks * MSL + i) & 1;  // rotation slot of sub-tile i
@@ -474,8 +492,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, const WorkItem& it,
         // order: per sub-tile, the next fragment read(s), then its MFMAs
         static_for<KSTEPS>([&](auto ks_c) {
           constexpr int ks = decltype(ks_c)::value;
-          if constexpr (ISSUE && ks < 2)
-            sched<kSchedVmemRead, ks == (BFIRST ? 1 : 0) ? AL : C::B_LOADS>();
+          if constexpr (ISSUE && ks == 0) sched<kSchedVmemRead, REFILL0>();
+          if constexpr (ISSUE && ks == 1 && !GATED)
+            sched<kSchedVmemRead, (BFIRST ? AL : C::B_LOADS)>();
           static_for<MSL>([&](auto i_c) {
             constexpr int i = decltype(i_c)::value;
             sched<kSchedLdsRead, (i + 1 < MSL ? 1 : (ks + 1 < KSTEPS ? NT + 1 : 0))>();
@@ -491,8 +510,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, const WorkItem& it,
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
           const int cur = ks & 1;
-          if (ISSUE && ks == (BFIRST ? 1 : 0)) issue_a(kt + SA - 1);
-          if (ISSUE && ks == (BFIRST ? 0 : 1)) issue_b(kt + SB - 1);
+          if (ISSUE && ks == 0) refill_first(kt);
+          if (ISSUE && ks == 1 && !GATED) refill_second(kt);
           if (ks + 1 < KSTEPS)
             load_frags<MX, C, MS>(As, Bs, a_row, b_row, fh, ks + 1, af[cur ^ 1], bf[cur ^ 1]);
 #pragma unroll
@@ -503,8 +522,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, const WorkItem& it,
         }
         static_for<KSTEPS>([&](auto ks_c) {
           constexpr int ks = decltype(ks_c)::value;
-          if constexpr (ISSUE && ks < 2)
-            sched<kSchedVmemRead, ks == (BFIRST ? 1 : 0) ? AL : C::B_LOADS>();
+          if constexpr (ISSUE && ks == 0) sched<kSchedVmemRead, REFILL0>();
+          if constexpr (ISSUE && ks == 1 && !GATED)
+            sched<kSchedVmemRead, (BFIRST ? AL : C::B_LOADS)>();
           constexpr int NM = MSL * NT;
           constexpr int NR = ks + 1 < KSTEPS ? MS + NT : 0;
           static_for<NM>([&](auto m_c) {
