@@ -553,75 +553,106 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, const WorkItem& it,
     };
     if (last) run(std::true_type{});
     else run(std::false_type{});
-  } else
-  for (int kt = 0; kt < nk; ++kt) {  // MXFP8
-    // a scale group among the younger loads: one of iterations kt-SA+2 ..
-    // kt-1 was a multiple of 4 that issued one
-    bool grp = false;
+  } else {
+    // MXFP8: the same two-part k-loop and straight-line slices.  Fragments
+    // are twice as wide and each MFMA four times as long as in bf16: each
+    // row fragment is re-read for the next k-step right after its MFMAs,
+    // and the weight fragments of the next k-step are read into a second
+    // set at the start of this one.  The gate/up projection refills both
+    // operands at k-step 0, the down projection the weights at k-step 1.
+    auto slice = [&](int kt, auto issue_tag, auto last_tag) {
+      constexpr bool ISSUE = decltype(issue_tag)::value;
+      constexpr bool LAST = decltype(last_tag)::value;
+      constexpr int MSL = LAST ? MS : MS - 1;
+      const unsigned char* As = Abuf + (kt % SA) * A_SL;
+      const unsigned char* Bs = Bbuf + (kt % SB) * C::B_BYTES;
+      // scales of this slice: word kt % 4 of a row's 16 bytes in its group
+      // buffer; byte b of the word is block b of the slice; the lane of half
+      // h takes block 2ks + h into bits 0..7
+      const uint32_t* sc =
+          reinterpret_cast<const uint32_t*>(Gbuf + ((kt >> 2) & 1) * C::SGB) + (kt & 3);
+      uint32_t sa_w[MS], sb_w[NT];
 #pragma unroll
-    for (int i = 1; i <= SA - 2; ++i) {
-      const int it2 = kt - i;
-      grp = grp || (it2 >= 0 && (it2 & 3) == 0 && (it2 >> 2) + 1 < ng);
-    }
-    if (kt + SMAX - 2 < nk) {  // every younger load was issued
-      if (grp) wait_vm<YOUNGER + 1>();
-      else wait_vm<YOUNGER>();
-    } else {
-      wait_vm<0>();
-    }
-    // every wave's part of slice kt is now in LDS, and every wave is done
-    // with slice kt-1, whose buffers the next loads overwrite
-    __builtin_amdgcn_s_barrier();
-    const unsigned char* As = Abuf + (kt % SA) * A_SL;
-    const unsigned char* Bs = Bbuf + (kt % SB) * C::B_BYTES;
-    // MXFP8 scales of this slice: word kt % 4 of a row's 16 bytes in its
-    // group buffer; byte b of the word is block b of the slice; the lane of
-    // half h takes block 2ks + h into bits 0..7
-    uint32_t sa_w[MS], sb_w[NT];
-    if ((kt & 3) == 0 && (kt >> 2) + 1 < ng) issue_g((kt >> 2) + 1);
-    const uint32_t* sc =
-        reinterpret_cast<const uint32_t*>(Gbuf + ((kt >> 2) & 1) * C::SGB) + (kt & 3);
+      for (int i = 0; i < MS; ++i) sa_w[i] = sc[4 * a_row[i]] >> (8 * fh);
 #pragma unroll
-    for (int i = 0; i < MS; ++i) sa_w[i] = sc[4 * a_row[i]] >> (8 * fh);
-#pragma unroll
-    for (int j = 0; j < NT; ++j) sb_w[j] = sc[4 * (C::BM + b_row[j])] >> (8 * fh);
-    {
-      // MXFP8 fragments are twice as wide and each MFMA four times as long:
-      // one register set, each fragment re-read for the next k-step as soon
-      // as its last MFMA of this step is issued
-      FT bf[NT], af[MS];
-      load_frags<MX, C, MS>(As, Bs, a_row, b_row, fh, 0, af, bf);
+      for (int j = 0; j < NT; ++j) sb_w[j] = sc[4 * (C::BM + b_row[j])] >> (8 * fh);
+      FT bf[2][NT], af[MS];
+      load_frags<MX, C, MS>(As, Bs, a_row, b_row, fh, 0, af, bf[0]);
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
+        const int cb = ks & 1;
         const bool more = ks + 1 < KSTEPS;
-        if (ks == 0 && kt + SA - 1 < nk) issue_a(kt + SA - 1);
-        if (ks == 1 && kt + SB - 1 < nk) issue_b(kt + SB - 1);
+        if (ISSUE && ks == 0) {
+          issue_a(kt + SA - 1);
+          if (GATED) issue_b(kt + SB - 1);
+        }
+        if (ISSUE && ks == 1 && !GATED) issue_b(kt + SB - 1);
+        if (more) {
+#pragma unroll
+          for (int j = 0; j < NT; ++j)
+            bf[cb ^ 1][j] = Frag<MX>::read(Bs + b_row[j] * C::ROWB, ks + 1, fh, C::swz(b_row[j]));
+        }
         const int sh = 16 * ks;  // block 2ks + h sits 16 ks bits up
 #pragma unroll
-        for (int i = 0; i < MS - 1; ++i) {
+        for (int i = 0; i < MSL; ++i) {
 #pragma unroll
           for (int j = 0; j < NT; ++j)
-            acc[i][j] = mma(bf[j], af[i], acc[i][j], (int)(sb_w[j] >> sh), (int)(sa_w[i] >> sh));
-          if (more)
-            af[i] = Frag<MX>::read(As + a_row[i] * C::ROWB, ks + 1, fh, C::swz(a_row[i]));
-        }
-        if (last) {
-#pragma unroll
-          for (int j = 0; j < NT; ++j) {
-            acc[MS - 1][j] = mma(bf[j], af[MS - 1], acc[MS - 1][j], (int)(sb_w[j] >> sh),
-                                 (int)(sa_w[MS - 1] >> sh));
-            if (more) bf[j] = Frag<MX>::read(Bs + b_row[j] * C::ROWB, ks + 1, fh, C::swz(b_row[j]));
-          }
-          if (more)
-            af[MS - 1] = Frag<MX>::read(As + a_row[MS - 1] * C::ROWB, ks + 1, fh,
-                                        C::swz(a_row[MS - 1]));
-        } else if (more) {
-#pragma unroll
-          for (int j = 0; j < NT; ++j)
-            bf[j] = Frag<MX>::read(Bs + b_row[j] * C::ROWB, ks + 1, fh, C::swz(b_row[j]));
+            acc[i][j] = mma(bf[cb][j], af[i], acc[i][j], (int)(sb_w[j] >> sh), (int)(sa_w[i] >> sh));
+          if (more) af[i] = Frag<MX>::read(As + a_row[i] * C::ROWB, ks + 1, fh, C::swz(a_row[i]));
         }
       }
-    }
+      // order: the scale words and k-step 0's fragments, then per k-step
+      // the loads, the next weight fragments, and per sub-tile its MFMAs
+      // followed by the re-read of its row fragment
+      sched<kSchedLdsRead, 3 * (MS + NT)>();
+      static_for<KSTEPS>([&](auto ks_c) {
+        constexpr int ks = decltype(ks_c)::value;
+        constexpr bool more = ks + 1 < KSTEPS;
+        if constexpr (ISSUE && ks == 0) sched<kSchedVmemRead, GATED ? AL + C::B_LOADS : AL>();
+        if constexpr (ISSUE && ks == 1 && !GATED) sched<kSchedVmemRead, C::B_LOADS>();
+        sched<kSchedLdsRead, (more ? 2 * NT : 0)>();
+        static_for<MSL>([&](auto) {
+          sched<kSchedMfma, NT>();
+          sched<kSchedLdsRead, (more ? 2 : 0)>();
+        });
+      });
+    };
+    // a scale group among the younger loads at iteration kt: one of
+    // iterations kt-SA+2 .. kt-1 was a multiple of 4 that issued one
+    auto wait_for = [&](int kt) {
+      bool grp = false;
+#pragma unroll
+      for (int i = 1; i <= SA - 2; ++i) {
+        const int it2 = kt - i;
+        grp = grp || (it2 >= 0 && (it2 & 3) == 0 && (it2 >> 2) + 1 < ng);
+      }
+      if (kt + SMAX - 2 < nk) {  // every younger load was issued
+        if (grp) wait_vm<YOUNGER + 1>();
+        else wait_vm<YOUNGER>();
+      } else {
+        wait_vm<0>();
+      }
+    };
+    auto run = [&](auto last_tag) {
+      int kt = 0;
+      // every wave's part of slice kt is in LDS after the wait, and every
+      // wave is done with slice kt-1, whose buffers the refill overwrites,
+      // after the barrier
+      for (; kt < nk - (SA - 1); ++kt) {
+        wait_for(kt);
+        __builtin_amdgcn_s_barrier();
+        if ((kt & 3) == 0 && (kt >> 2) + 1 < ng) issue_g((kt >> 2) + 1);
+        slice(kt, std::true_type{}, last_tag);
+      }
+      for (; kt < nk; ++kt) {
+        wait_for(kt);
+        __builtin_amdgcn_s_barrier();
+        if ((kt & 3) == 0 && (kt >> 2) + 1 < ng) issue_g((kt >> 2) + 1);
+        slice(kt, std::false_type{}, last_tag);
+      }
+    };
+    if (last) run(std::true_type{});
+    else run(std::false_type{});
   }
 
   // epilogue.  32x32 accumulator layout of the transposed tile: lane l holds
