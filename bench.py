@@ -84,7 +84,8 @@ def algorithmic_flops(cfg, n_kept: int) -> dict:
 
 
 def committed_traffic(workload: str, proj: str = "gate_up"):
-    """HBM bytes per launch of the gate/up (or down) GEMM on this workload,
+    """HBM bytes per launch of the gate/up (proj "gate_up", "gate_up_mxfp8")
+    or down ("down") GEMM on this workload,
     from the committed rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE,
     each scaled by the same counter on a plain 1 GiB copy); None when there is
     none or the kernel source changed since the counters were taken."""
@@ -567,6 +568,8 @@ def headline(moe, W, torch, dev, cfg, args) -> dict:
             "ms_per_step": round(mx_ms, 4), "tokens/s": round(T / (mx_ms * 1e-3), 1),
             "tflops": round(fl["total"] / (mx_ms * 1e-3) / 1e12, 2),
             "gate_up_ms": round(m1_ms, 4), "gate_up_note": "x quantisation + grouped GEMM",
+            "gate_up_algorithmic_bytes": int(m1_bytes),
+            "gate_up_traffic": committed_traffic(cfg.name, "gate_up_mxfp8"),
             "gate_up_GB/s": round(m1_gbs, 1), "gate_up_hbm_frac": round(m1_gbs / PEAK_HBM_GBS, 4),
             "gate_up_TFLOP/s": round(m1_tfs, 2),
             "gate_up_fp8_frac": round(m1_tfs / PEAK_FP8_TFLOPS, 4),
