@@ -212,11 +212,13 @@ constexpr int RS_T = 32;  // tile rows and columns
 // weights once (split3_kernel) and run router_mfma_kernel per chunk (the
 // same partial planes).
 constexpr int kRouterSmallMaxT = 2 * RS_T;
-__global__ __launch_bounds__(256) void router_small_kernel(const bf16_t* __restrict__ x,
-                                                           const float* __restrict__ w,
-                                                           float* __restrict__ out, int T,
-                                                           int N, int d) {
+constexpr int RS_THREADS = 1024;  // sixteen waves: the weight split spread thin
+__global__ __launch_bounds__(RS_THREADS) void router_small_kernel(const bf16_t* __restrict__ x,
+                                                                  const float* __restrict__ w,
+                                                                  float* __restrict__ out, int T,
+                                                                  int N, int d) {
   constexpr int SLW = RM_KC / 64;  // 64-wide slices per chunk
+  constexpr int XL = RS_T * 64 / RS_THREADS, WL = RS_T * 128 / RS_THREADS;  // loads per thread
   __shared__ __attribute__((aligned(16))) unsigned char As[SLW][RS_T * 128];
   __shared__ __attribute__((aligned(16))) unsigned char Bs[3][SLW][RS_T * 128];
   __shared__ __attribute__((aligned(16))) float red[2][RS_T * RS_T];
@@ -227,31 +229,31 @@ __global__ __launch_bounds__(256) void router_small_kernel(const bf16_t* __restr
   const int nsl = min(SLW, (d - k0) / 64);  // 64-wide slices in this chunk (d % 64 == 0)
   typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
   typedef float f32x4_t __attribute__((ext_vector_type(4)));
-  // coalesced loads: load i of thread t takes 16-byte chunk i * 256 + t of the
-  // tile (x: 32 rows x 64 chunks of 8 bf16; weights: 32 rows x 128 chunks of
-  // 4 fp32), so a wave reads 1 KiB of one row per instruction
-  u32x4_t xa[8];
-  f32x4_t wb[16];
+  // coalesced loads: load i of thread t takes 16-byte chunk i * RS_THREADS + t
+  // of the tile (x: 32 rows x 64 chunks of 8 bf16; weights: 32 rows x 128
+  // chunks of 4 fp32), so a wave reads 1 KiB of one row per instruction
+  u32x4_t xa[XL];
+  f32x4_t wb[WL];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int g = i * 256 + tid, r = g >> 6, ch = g & 63;
+  for (int i = 0; i < XL; ++i) {
+    const int g = i * RS_THREADS + tid, r = g >> 6, ch = g & 63;
     const bf16_t* xp = x + (size_t)min(m0 + r, T - 1) * d + k0;
     xa[i] = ch / 8 < nsl ? *reinterpret_cast<const u32x4_t*>(xp + ch * 8) : u32x4_t{0, 0, 0, 0};
   }
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int g = i * 256 + tid, r = g >> 7, ch = g & 127;
+  for (int i = 0; i < WL; ++i) {
+    const int g = i * RS_THREADS + tid, r = g >> 7, ch = g & 127;
     const float* wp = w + (size_t)min(n0 + r, N - 1) * d + k0;
     wb[i] = ch / 16 < nsl ? *reinterpret_cast<const f32x4_t*>(wp + ch * 4) : f32x4_t{0, 0, 0, 0};
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int g = i * 256 + tid, r = g >> 6, ch = g & 63, sl = ch / 8, c8 = ch % 8;
+  for (int i = 0; i < XL; ++i) {
+    const int g = i * RS_THREADS + tid, r = g >> 6, ch = g & 63, sl = ch / 8, c8 = ch % 8;
     *reinterpret_cast<u32x4_t*>(&As[sl][r * 128 + ((c8 ^ rswz(r)) << 4)]) = xa[i];
   }
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int g = i * 256 + tid, r = g >> 7, ch = g & 127;
+  for (int i = 0; i < WL; ++i) {
+    const int g = i * RS_THREADS + tid, r = g >> 7, ch = g & 127;
     const int sl = ch / 16, c16 = ch % 16;  // half of a 16-byte bf16 chunk
     const int pos = (((c16 >> 1) ^ rswz(r)) << 4) + (c16 & 1) * 8;
     uint32_t h[3][2];
@@ -282,16 +284,23 @@ __global__ __launch_bounds__(256) void router_small_kernel(const bf16_t* __restr
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
   if (wv < 3) {
-    for (int sl = 0; sl < nsl; ++sl) {
-#pragma unroll
-      for (int ks = 0; ks < RM_BK / 16; ++ks) {
-        const int ch = 2 * ks + fh;
-        const bf16x8_t af =
-            *reinterpret_cast<const bf16x8_t*>(&As[sl][fr * 128 + ((ch ^ rswz(fr)) << 4)]);
-        const bf16x8_t bf =
-            *reinterpret_cast<const bf16x8_t*>(&Bs[wv][sl][fr * 128 + ((ch ^ rswz(fr)) << 4)]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc, 0, 0, 0);
-      }
+    // the chunk's k-steps in order; the fragments of step q+1 are read while
+    // the MFMA of step q runs
+    const int nq = nsl * (RM_BK / 16);
+    auto frag = [&](const unsigned char* base, int q) {
+      const int ch = 2 * (q & 3) + fh;
+      return *reinterpret_cast<const bf16x8_t*>(base + (q >> 2) * RS_T * 128 + fr * 128 +
+                                                ((ch ^ rswz(fr)) << 4));
+    };
+    const unsigned char* Ab = &As[0][0];
+    const unsigned char* Bb = &Bs[wv][0][0];
+    bf16x8_t af = frag(Ab, 0), bf = frag(Bb, 0);
+    for (int q = 0; q < nq; ++q) {
+      const int qn = q + 1 < nq ? q + 1 : q;
+      const bf16x8_t an = frag(Ab, qn), bn = frag(Bb, qn);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc, 0, 0, 0);
+      af = an;
+      bf = bn;
     }
   }
   // parts 1 and 2 to LDS, part 0's wave adds them smallest first
@@ -459,7 +468,7 @@ hipError_t launch_router_gemm(const moe_shape& s, const void* x, const float* w_
     const int nkc = router_split_chunks(s);
     if (nkc && T <= kRouterSmallMaxT) {
       dim3 grid((T + RS_T - 1) / RS_T, (N + RS_T - 1) / RS_T, nkc);
-      router_small_kernel<<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(x), w_router,
+      router_small_kernel<<<grid, RS_THREADS, 0, st>>>(static_cast<const bf16_t*>(x), w_router,
                                                 w.router_part, T, N, d);
       *nparts = nkc;
       return hipGetLastError();
