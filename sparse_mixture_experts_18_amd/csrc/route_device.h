@@ -192,13 +192,39 @@ __device__ __forceinline__ void plan_device(const PlanArgs& a, int pass) {
         hdr[kHdrDone] = 0;
       }
       if (s < 8 * R8 && s % R8 == 0) hdr[kHdrStart + s / R8] = base;
-      if (u >= 0 && mt > 0) {
-        const int R = rowss[useg2];
-        const int part = ((R + mt - 1) / mt + 31) / 32 * 32;
-        int i = base;
-        for (int nt = u0; nt < u1; ++nt)
-          for (int m = 0; m < mt; ++m)
-            plan[i++] = WorkItem{useg2, rbases[useg2] + m * part, min(part, R - m * part), nt};
+      if (total <= 64 * U) {  // a few items per unit: each slot's thread writes its own
+        if (u >= 0 && mt > 0) {
+          const int R = rowss[useg2];
+          const int part = ((R + mt - 1) / mt + 31) / 32 * 32;
+          int i = base;
+          for (int nt = u0; nt < u1; ++nt)
+            for (int m = 0; m < mt; ++m)
+              plan[i++] = WorkItem{useg2, rbases[useg2] + m * part, min(part, R - m * part), nt};
+        }
+        return;
+      }
+      // many items per unit (few experts with many column tiles: one thread
+      // writing an expert's hundreds of items took most of the 24 us of
+      // mixtral's plan): the block writes them together; item i belongs to
+      // the last slot whose base is <= i (slots without items have the next
+      // slot's base)
+      st1s[s] = base;  // (the segment starts are no longer needed)
+      if (s == 0) st1s[nthr] = total;
+      __syncthreads();
+      for (int i = s; i < total; i += nthr) {
+        int lo = 0, hi = nthr - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (st1s[mid] <= i) lo = mid;
+          else hi = mid - 1;
+        }
+        const int v = uslot[lo];
+        const int sg = v < N ? v : N;
+        const int t0v = v < N ? 0 : v - N;
+        const int mtv = mts[sg], R = rowss[sg];
+        const int part = ((R + mtv - 1) / mtv + 31) / 32 * 32;
+        const int loc = i - st1s[lo], m = loc % mtv, nt = t0v + loc / mtv;
+        plan[i] = WorkItem{sg, rbases[sg] + m * part, min(part, R - m * part), nt};
       }
       return;
     }
