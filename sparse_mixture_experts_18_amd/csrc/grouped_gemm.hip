@@ -116,10 +116,11 @@ struct GemmArgs {
 // i % RG == rg.  An item with few rows costs MFMA work in proportion to
 // ceil(rows/32), not to the full tile.
 //
-// Operands move global -> LDS with the direct DMA load (global_load_lds, 16
-// bytes per lane, one 1 KiB block of rows per wave instruction) into rings of
-// SA (rows) and SB (weights) buffers, so SA-1 / SB-1 k-slices are in flight
-// while the MFMAs consume one.  Each wave waits only on its own loads (vmcnt); one s_barrier per slice
+// Operands move global -> LDS with the direct buffer-to-LDS load
+// (buffer_load_dwordx4 ... lds, 16 bytes per lane, one 1 KiB block of rows per
+// wave instruction) into rings of SA (rows) and SB (weights) buffers, so
+// SA-1 / SB-1 k-slices are in flight while the MFMAs consume one.  Each wave
+// waits only on its own loads (vmcnt); one s_barrier per slice
 // publishes the slice to all waves and retires the buffer that the next DMA
 // overwrites.  Inside an LDS row the 16-byte chunk c of row r sits at position
 // c ^ swz(r), swz(r) = (r / rows-per-256-bytes) % chunks-per-row: the 32 rows
