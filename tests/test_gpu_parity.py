@@ -180,6 +180,13 @@ SMALL = [
     # five and six 32-row sub-tiles per wave (the tall tiles), partial column tiles
     _small_cfg("s_tall_rows", T=1600, n_experts=5, top_k=1, d_model=192, d_ff=320,
                d_ff_shared=192),
+    # extreme skew: nearly every token picks experts 0 and 1 (three row blocks
+    # each, sharing their weight slabs), the other experts (nearly) empty
+    _small_cfg("s_skew", T=1100, n_experts=16, top_k=2, zipf_s=10.0, d_model=256, d_ff=256,
+               d_ff_shared=128),
+    # few experts with many column tiles (128 gate/up items per expert): the
+    # work list is written by the whole block
+    _small_cfg("s_wide_units", T=1200, n_experts=3, top_k=1, d_model=128, d_ff=8192),
 ]
 
 
