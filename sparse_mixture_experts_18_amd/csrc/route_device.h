@@ -394,8 +394,44 @@ __device__ __forceinline__ void topk_token(
   if (n_groups > 1) {  // uniform across the block
     // group score: fl32 sum of the best m keys of the group, best first
     const int gsz = N / n_groups, m = k / topk_groups;
+    // groups of whole lanes (gsz = lpg * P, lpg a power of two) with m <= 2:
+    // the group's best two (key, index) pairs by a shuffle reduction over its
+    // lpg lanes.  A pair is the 64-bit (order key, ~index), so the larger one
+    // is the larger key, then the lower index -- the order of the serial scan
+    // below, which serves every other shape.
+    const int lpg = gsz / P;
+    const bool whole = m <= 2 && gsz == lpg * P && lpg <= 64 && (lpg & (lpg - 1)) == 0;
+    if (whole) {
+      uint64_t b1 = 0, b2 = 0;  // this lane's best two (0: none)
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const int e = lane * P + p;
+        const uint64_t c = e < N ? ((uint64_t)ok[p] << 32) | (uint32_t)~(uint32_t)e : 0ull;
+        if (c > b1) {
+          b2 = b1;
+          b1 = c;
+        } else if (c > b2) {
+          b2 = c;
+        }
+      }
+      for (int off = 1; off < lpg; off <<= 1) {
+        const uint64_t o1 = ((uint64_t)(uint32_t)__shfl_xor((int)(b1 >> 32), off, 64) << 32) |
+                            (uint32_t)__shfl_xor((int)(uint32_t)b1, off, 64);
+        const uint64_t o2 = ((uint64_t)(uint32_t)__shfl_xor((int)(b2 >> 32), off, 64) << 32) |
+                            (uint32_t)__shfl_xor((int)(uint32_t)b2, off, 64);
+        const uint64_t n1 = b1 > o1 ? b1 : o1;
+        const uint64_t lo = b1 > o1 ? o1 : b1, hi2 = b2 > o2 ? b2 : o2;
+        b2 = lo > hi2 ? lo : hi2;
+        b1 = n1;
+      }
+      const int g = lane / lpg;
+      if (lane % lpg == 0 && g < n_groups) {
+        const float v1 = keys_w[~(uint32_t)b1];
+        gsc_w[g] = m == 1 ? v1 : v1 + keys_w[~(uint32_t)b2];
+      }
+    }
     __syncthreads();
-    if (lane < n_groups) {
+    if (!whole && lane < n_groups) {
       const float* gk = &keys_w[lane * gsz];
       float acc = 0.f;
       uint32_t prev_o = 0xffffffffu;

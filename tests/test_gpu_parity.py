@@ -236,12 +236,15 @@ def test_injected_tie_scores_bit_exact():
 
 @pytest.mark.parametrize("N,k,groups", [(24, 5, (1, 1)), (100, 7, (1, 1)), (130, 1, (1, 1)),
                                          (256, 8, (8, 4)), (512, 16, (1, 1)),
-                                         (512, 16, (16, 8))])
+                                         (512, 16, (16, 8)), (96, 12, (4, 2))])
 def test_topk_selection_specials_every_lane_width(N, k, groups):
     """Selection over 1, 2, 4 and 8 experts per lane: keys from a few values
     (ties at the k-th key), all-equal rows, exactly k-1 keys above a run of
     ties, NaN, +-0 and +-inf, with a selection bias; indices against the
-    oracle's (key desc, index asc) rule, weights against its renormalisation."""
+    oracle's (key desc, index asc) rule, weights against its renormalisation.
+    The group-limited cases score groups of whole lanes by the shuffle
+    reduction (best 2 keys of 8 or 4 lanes) and, with 4 groups of 24 experts
+    and the best 6 keys each, by the serial scan."""
     T = 300
     cfg = _small_cfg("sel", T=T, n_experts=N, top_k=k, n_groups=groups[0],
                      topk_groups=groups[1], bias_zero=True)
